@@ -1,0 +1,257 @@
+"""Benchmark of the fused LayerNorm-MLP forward on one MI355X.
+
+A step is one call of the fused forward (norm -> GEMM1 + bias + GELU ->
+GEMM2 + bias) on the 8192 x 4096 -> 16384 -> 4096 bf16 workload, with all
+inputs resident in HBM. The value is the GEMM work of the step (2*M*N*K per
+GEMM) divided by the step's wall time, in TFLOP/s. The other workloads
+(LayerNorm+Dense, RMSNorm-SwiGLU, the fp8 forward and the activation
+backward) are measured the same way and reported under "parts".
+
+Per-kernel durations come from HIP events the library records around each
+of its launches on the launch stream (te_timing_enable) during the timed
+region; the dominant kernel's figure is the "roofline" entry. The
+"cpu_baseline" entry times the fp64 oracle on a bounded row sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-parts]
+                       [--no-cpu-baseline] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused LN-MLP fwd TFLOP/s + % of MI355X bf16/fp8 MFMA peak; dact+dbias GB/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Case:
+    """Inputs on the device plus a closure running one step."""
+
+    def __init__(self, w: W.Workload, te, dev):
+        self.w = w
+        t = W.make_inputs(w)
+        self.g = {k: v.to(dev) for k, v in t.items()}
+        g = self.g
+        self.qset = te.QuantizerSet(dev) if w.quant != "none" else None
+        if w.kind == "dense":
+            ws_n = te.te_layernorm_dense_fwd_workspace_size(w.rows, w.hidden, w.ffn, 1,
+                                                            1 if self.qset else 0)
+            self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+            self.y = torch.empty(w.rows, w.ffn, dtype=g["x"].dtype, device=dev)
+            self.fn = lambda: te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g.get("bias"),
+                                                 epsilon=w.epsilon, quantizer_set=self.qset,
+                                                 workspace=self.ws, out=self.y)
+        else:
+            act = te.act_type_of(w.activation_type)
+            ws_n = te.te_layernorm_mlp_fwd_workspace_size(w.rows, w.hidden, w.ffn,
+                                                          0 if w.dtype == "fp32" else 1, act,
+                                                          1 if self.qset else 0)
+            self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+            self.y = torch.empty(w.rows, w.hidden, dtype=g["x"].dtype, device=dev)
+            self.fn = lambda: te.layernorm_mlp(
+                g["x"], g["gamma"], g.get("beta"), [g["kernel1"], g["kernel2"]], [g.get("bias1"), g.get("bias2")],
+                w.norm_type, zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
+                activation_type=w.activation_type, quantizer_set=self.qset, workspace=self.ws, out=self.y)
+
+    def flops(self):
+        return self.w.gemm_flops()
+
+
+class DactCase:
+    """dact + dbias on grad [M, F] and the saved pre-activation h1 [M, F]."""
+
+    def __init__(self, w: W.Workload, te, dev):
+        self.w = w
+        t = W.make_inputs(w)
+        self.grad = t["grad"].to(dev)
+        gen = torch.Generator().manual_seed(1)
+        # h1 of the same shape and a GEMM1-like spread
+        self.h1 = (torch.randn(w.rows, w.ffn, generator=gen) * 1.5).to(torch.bfloat16).to(dev)
+        self.dx = torch.empty_like(self.h1)
+        self.dbias = torch.empty(w.ffn, dtype=torch.float32, device=dev)
+        act = te.act_type_of(w.activation_type)
+        n = te.te_dact_dbias_workspace_size(w.rows, w.ffn, act)
+        self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        B = te._binding
+
+        def fn():
+            B.te_dact_dbias(self.grad, self.h1, w.rows, w.ffn, B.TE_BF16, act, self.dx, self.dbias, B.TE_F32,
+                            self.ws, self.ws.numel())
+        self.fn = fn
+
+    def bytes(self):
+        # grad + h1 read, dx written (bf16), dbias written (fp32)
+        return 3 * self.w.rows * self.w.ffn * 2 + self.w.ffn * 4
+
+
+def time_steps(fn, steps, warmup, te=None):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if te is not None:
+        te.te_timing_reset()
+        te.te_timing_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    kernels = {}
+    if te is not None:
+        kernels = te.te_timing_collect()
+        te.te_timing_enable(False)
+    return ms, kernels
+
+
+def kernel_work(w: W.Workload, name: str):
+    """Algorithmic work of one launch of a kernel of the given workload:
+    (amount, unit, bound)."""
+    g = 2 if w.gated else 1
+    M, H, F = w.rows, w.hidden, w.ffn
+    if name.startswith("gemm"):
+        if w.kind == "dense":
+            return 2 * M * H * F, "flop", "mfma"
+        if name in ("gemm_bf16_act", "gemm_bf16_gated", "gemm_fp8_h_amax"):
+            return 2 * M * H * g * F, "flop", "mfma"
+        return 2 * M * F * H, "flop", "mfma"
+    if name == "dact_dbias":
+        return 3 * M * F * 2, "byte", "hbm"
+    if name == "norm_fwd":
+        return 2 * M * H * 2 + 2 * H * 2, "byte", "hbm"
+    return None
+
+
+def roofline(w, kernels, dtype_key):
+    if not kernels:
+        return None
+    name, (cnt, total) = max(kernels.items(), key=lambda kv: kv[1][1])
+    work = kernel_work(w, name)
+    if work is None:
+        return None
+    amount, unit, bound = work
+    avg_s = total / cnt / 1e3
+    if unit == "flop":
+        achieved = amount / avg_s / 1e12
+        peak = PEAK[dtype_key]
+        u = "TFLOP/s"
+    else:
+        achieved = amount / avg_s / 1e9
+        peak = HBM_PEAK_GBS
+        u = "GB/s"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
+            "frac": round(achieved / peak, 4), "traffic": None, "avg_ms": round(total / cnt, 4),
+            "launches": cnt}
+
+
+def cpu_baseline(w: W.Workload, budget_s: float = 12.0):
+    """Times the fp64 oracle forward on a bounded row sample of workload w."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    t = W.make_inputs(w)
+    f = {k: W.to_f64(v) for k, v in t.items()}
+    rows = 16
+    done_rows, elapsed = 0, 0.0
+    while elapsed < budget_s and done_rows < w.rows:
+        sel = slice(done_rows % w.rows, done_rows % w.rows + rows)
+        t0 = time.perf_counter()
+        O.layernorm_mlp_fwd(f["x"][sel], f["gamma"], f.get("beta"), f["kernel1"], f["kernel2"], f.get("bias1"),
+                            f.get("bias2"), norm_type=w.norm_type, zero_centered_gamma=w.zero_centered_gamma,
+                            epsilon=w.epsilon, activation_type=w.activation_type)
+        elapsed += time.perf_counter() - t0
+        done_rows += rows
+        rows = min(rows * 2, 1024)
+    flops = w.scaled(rows=done_rows).gemm_flops()
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle forward of {done_rows} of {w.rows} rows ({elapsed:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ln_mlp_gelu_bf16")
+    ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this library has no "
+              "multi-GPU path; the value is the single-GPU throughput", file=sys.stderr)
+        sys.exit(2)
+    import rmsnorm_mlp_transformer_amd as te
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    dkey = "fp8" if w.quant != "none" else w.dtype
+    log(f"bench: {w.name} rows={w.rows} hidden={w.hidden} ffn={w.ffn} dtype={dkey}")
+    case = Case(w, te, dev)
+    ms, kernels = time_steps(case.fn, args.steps, args.warmup, te)
+    value = case.flops() / (ms / 1e3) / 1e12
+    log(f"bench: {ms:.4f} ms/step, {value:.1f} TFLOP/s, kernels {kernels}")
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if dkey == "bf16" else dkey, "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "hidden": w.hidden, "ffn": w.ffn,
+                   "norm": w.norm_type, "activation": list(w.activation_type), "quant": w.quant,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK[dkey], 4),
+        "roofline": roofline(w, kernels, dkey),
+        "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in kernels.items()},
+    }
+    if not args.no_parts:
+        parts = {}
+        for name in ("ln_dense_bf16", "rms_swiglu_bf16", "ln_mlp_gelu_fp8"):
+            if name == w.name:
+                continue
+            pw = W.WORKLOADS[name]
+            c = Case(pw, te, dev)
+            pms, pk = time_steps(c.fn, max(5, args.steps // 2), 3, te)
+            pv = c.flops() / (pms / 1e3) / 1e12
+            pkey = "fp8" if pw.quant != "none" else pw.dtype
+            parts[name] = {"ms_per_step": round(pms, 4), "TFLOP/s": round(pv, 2),
+                           "frac_of_peak": round(pv / PEAK[pkey], 4),
+                           "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in pk.items()},
+                           "roofline": roofline(pw, pk, pkey)}
+            log(f"bench part {name}: {pms:.4f} ms, {pv:.1f} TFLOP/s")
+            del c
+            torch.cuda.empty_cache()
+        dw = W.WORKLOADS["ln_mlp_gelu_fp8"]
+        d = DactCase(dw, te, dev)
+        dms, dk = time_steps(d.fn, max(10, args.steps), 3, te)
+        gbs = d.bytes() / (dms / 1e3) / 1e9
+        parts["dact_dbias_gelu_bf16"] = {"ms_per_step": round(dms, 4), "GB/s": round(gbs, 1),
+                                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                         "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
+                                         "roofline": roofline(dw, {k: v for k, v in dk.items()
+                                                                   if k == "dact_dbias"}, "bf16")}
+        log(f"bench part dact_dbias: {dms:.4f} ms, {gbs:.0f} GB/s")
+        result["parts"] = parts
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"bench cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

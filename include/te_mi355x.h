@@ -1,0 +1,244 @@
+/*
+ * te_mi355x.h - C ABI of the fused norm / MLP library for AMD MI355X (gfx950).
+ *
+ * The operations follow the I/O contracts of three pages of the
+ * TransformerEngine JAX documentation:
+ *   [ACT]   "NVIDIA TransformerEngine JAX Activation"
+ *   [MLP]   "NVIDIA TransformerEngine JAX LayerNorm MLP"
+ *   [DENSE] "NVIDIA TransformerEngine JAX LayerNorm Dense"
+ *
+ * Conventions for every entry point:
+ *  - Tensors are dense, row-major and contiguous in device memory. Leading
+ *    axes are flattened into `rows`; the last axis is the feature axis.
+ *    Weight matrices are [in_features, out_features] (the pages' x @ kernel).
+ *  - All buffers, including the workspace and fp8 metadata, are owned by the
+ *    caller. The library never allocates or frees device memory and keeps no
+ *    pointer after a call returns. Device pointers must be 16-byte aligned.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
+ *    null stream) and never synchronises the host.
+ *  - Arguments are fully validated before the first launch: a non-zero status
+ *    means nothing was written. The message for the last failure on the
+ *    calling thread is available from te_last_error(). Launch failures map to
+ *    TE_ERR_HIP; faults inside kernels surface at the caller's synchronise.
+ *  - Feature sizes (hidden, ffn, cols, out_features) must be positive
+ *    multiples of 16; rows may be 0: then no tensor element is written,
+ *    except that te_dact_dbias sets dbias to zero and the single-tensor
+ *    calls with E4M3 output (te_layernorm_fwd, te_act_lu) set their meta to
+ *    amax 0, scale 1, scale_inv 1.
+ *  - Supported dtype/quantisation combinations: TE_F32 with TE_QUANT_NONE;
+ *    TE_BF16 with TE_QUANT_NONE or TE_QUANT_FP8_E4M3_CURRENT. Anything else
+ *    returns TE_ERR_UNSUPPORTED.
+ *  - fp8 is OCP E4M3 (largest finite value 448), encoded with
+ *    round-to-nearest-even after saturating to +-448, with per-tensor current
+ *    scaling: amax = max |t| over the whole tensor, scale = 448 / amax
+ *    (1 if amax is 0), scale_inv = 1 / scale, code = E4M3(t * scale), all in
+ *    fp32. Quantised values are decoded as E4M3(code) * scale_inv.
+ *  - Output buffers must not overlap inputs.
+ */
+#ifndef TE_MI355X_H
+#define TE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum te_status {
+  TE_SUCCESS = 0,
+  TE_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, bad size, bad enum */
+  TE_ERR_UNSUPPORTED = 2,      /* valid but unsupported combination        */
+  TE_ERR_WORKSPACE_TOO_SMALL = 3,
+  TE_ERR_HIP = 4               /* a HIP launch or runtime call failed       */
+} te_status;
+
+typedef enum te_dtype { TE_F32 = 0, TE_BF16 = 1, TE_E4M3 = 2 } te_dtype;
+
+/* [MLP] Inputs: norm_type "layernorm" or "rmsnorm". */
+typedef enum te_norm_type { TE_LAYERNORM = 0, TE_RMSNORM = 1 } te_norm_type;
+
+/* [ACT] Inputs: activation_type, a single name or a gated pair. A gated pair
+ * (f, linear) reads a [rows, 2*cols] input whose first `cols` columns a go
+ * through f and whose second `cols` columns b are the linear gate:
+ * out = f(a) * b. GELU is the tanh approximation
+ * 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); GELU_ERF is x * Phi(x). */
+typedef enum te_act_type {
+  TE_ACT_RELU = 0,
+  TE_ACT_GELU = 1,
+  TE_ACT_GELU_ERF = 2,
+  TE_ACT_SILU = 3,
+  TE_ACT_LINEAR = 4,
+  TE_ACT_REGLU = 5,  /* ("relu", "linear") */
+  TE_ACT_GEGLU = 6,  /* ("gelu", "linear") */
+  TE_ACT_SWIGLU = 7  /* ("silu", "linear") */
+} te_act_type;
+
+/* [MLP]/[DENSE] Inputs: quantizer_set. NONE is the no-op quantizer set. */
+typedef enum te_quant { TE_QUANT_NONE = 0, TE_QUANT_FP8_E4M3_CURRENT = 1 } te_quant;
+
+/* Per-tensor fp8 metadata: three device pointers to one float each, written
+ * by the call that quantises the tensor (amax, then scale and scale_inv). */
+typedef struct te_fp8_meta {
+  float* amax;
+  float* scale;
+  float* scale_inv;
+} te_fp8_meta;
+
+/* Forward context saved for the backward ([DENSE] Description: the backward
+ * reuses the saved forward context). Every field is optional (NULL skips it).
+ *   h1     [rows, G*ffn] GEMM1 output plus bias1, before the activation
+ *          (bf16 for a TE_BF16 call, fp32 for TE_F32); this is the `x`
+ *          input of te_dact_dbias.
+ *   mu     [rows] fp32 per-row mean (LayerNorm only).
+ *   rsigma [rows] fp32 per-row 1/sqrt(var + eps) (or 1/rms for RMSNorm).
+ *   *_meta fp8 metadata of the normalised input, kernel1, the activation
+ *          output and kernel2 (fp8 calls only; a meta with any NULL field is
+ *          kept in the workspace instead).
+ *   xq     [rows, hidden] E4M3 codes of the normalised input (fp8 only).
+ *   w1q_t  [G*ffn, hidden] E4M3 codes of kernel1, transposed (fp8 only).
+ *   w2q_t  [hidden, ffn] E4M3 codes of kernel2, transposed (fp8 only).
+ *   actq   [rows, ffn] E4M3 codes of the activation output (fp8 only).
+ *   The code buffers replace the matching workspace buffers when given. */
+typedef struct te_mlp_saved {
+  void* h1;
+  float* mu;
+  float* rsigma;
+  te_fp8_meta x_meta;
+  te_fp8_meta w1_meta;
+  te_fp8_meta act_meta;
+  te_fp8_meta w2_meta;
+  uint8_t* xq;
+  uint8_t* w1q_t;
+  uint8_t* w2q_t;
+  uint8_t* actq;
+} te_mlp_saved;
+
+/* te_layernorm_fwd - the normalisation step ([MLP] Description step (1);
+ * [DENSE] Description and Inputs: gamma, beta, norm_type,
+ * zero_centered_gamma, epsilon).
+ *   LayerNorm: y = (x - mean) / sqrt(var + epsilon) * g + beta (biased var).
+ *   RMSNorm:   y = x / sqrt(mean(x^2) + epsilon) * g; beta is ignored and may
+ *              be NULL.
+ *   g = 1 + gamma when zero_centered_gamma != 0, else gamma.
+ * x: [rows, hidden] of x_dtype (F32 or BF16); gamma, beta: [hidden] of
+ * x_dtype. y: [rows, hidden] of y_dtype: F32, BF16 or E4M3. For E4M3 the
+ * whole tensor is quantised with current scaling and y_meta (required) gets
+ * amax/scale/scale_inv. mu, rsigma: optional [rows] fp32 outputs (mu is not
+ * written for RMSNorm). Workspace: te_layernorm_fwd_workspace_size(). */
+te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta,
+                           int64_t rows, int64_t hidden, te_dtype x_dtype,
+                           te_norm_type norm_type, int zero_centered_gamma, float epsilon,
+                           void* y, te_dtype y_dtype, const te_fp8_meta* y_meta,
+                           float* mu, float* rsigma,
+                           void* workspace, size_t workspace_bytes, void* stream);
+size_t te_layernorm_fwd_workspace_size(int64_t rows, int64_t hidden, te_dtype x_dtype,
+                                       te_dtype y_dtype);
+
+/* te_act_lu - activation forward with optional fp8 output ([ACT]
+ * Description: the forward applies the activation with optional
+ * quantisation; Outputs: the activated tensor).
+ * x: [rows, G*cols] of x_dtype (F32 or BF16), G = 2 for gated types.
+ * y: [rows, cols] of y_dtype (F32, BF16 or E4M3). For E4M3, y holds the codes
+ * and y_meta (required) the amax/scale/scale_inv of the whole output; the
+ * page's dequantised result is te_dequantize() of it. No workspace. */
+te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype,
+                    te_act_type act_type, void* y, te_dtype y_dtype,
+                    const te_fp8_meta* y_meta, void* stream);
+
+/* te_dact_dbias - activation backward with the bias-gradient reduction
+ * ([ACT] Description: the backward rule computes the activation gradient;
+ * [MLP] Description: the fused backward gives the activation gradient and the
+ * bias reduction).
+ *   dx = grad * act'(x); gated (f, linear) with x = [a | b]:
+ *   dx = [grad * b * f'(a) | grad * f(a)].
+ *   dbias[j] = sum over rows of dx[:, j], accumulated in fp32 from the fp32
+ *   values of dx before they are rounded to `dtype`.
+ * grad: [rows, cols]; x: [rows, G*cols] (the saved pre-activation h1);
+ * dx: [rows, G*cols]; all of `dtype` (F32 or BF16). dbias: optional
+ * [G*cols] of dbias_dtype (F32 or BF16). The reduction order is fixed, so
+ * results are bitwise reproducible. Workspace:
+ * te_dact_dbias_workspace_size(). */
+te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,
+                        te_dtype dtype, te_act_type act_type, void* dx,
+                        void* dbias, te_dtype dbias_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+size_t te_dact_dbias_workspace_size(int64_t rows, int64_t cols, te_act_type act_type);
+
+/* te_layernorm_dense_fwd - normalisation followed by a dense layer ([DENSE]
+ * Description; Outputs: LayerNorm(x) @ kernel + bias). With
+ * TE_QUANT_FP8_E4M3_CURRENT the normalised input and the kernel are both
+ * quantised to E4M3 before the GEMM (fp32 accumulate, bf16 output).
+ * x: [rows, hidden]; kernel: [hidden, out_features]; gamma, beta: [hidden];
+ * bias: optional [out_features]; y: [rows, out_features]; all of `dtype`.
+ * Workspace: te_layernorm_dense_fwd_workspace_size(). */
+te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* gamma,
+                                 const void* beta, const void* bias,
+                                 int64_t rows, int64_t hidden, int64_t out_features,
+                                 te_dtype dtype, te_norm_type norm_type,
+                                 int zero_centered_gamma, float epsilon, te_quant quant,
+                                 void* y, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+size_t te_layernorm_dense_fwd_workspace_size(int64_t rows, int64_t hidden,
+                                             int64_t out_features, te_dtype dtype,
+                                             te_quant quant);
+
+/* te_layernorm_mlp_fwd - the fused feed-forward sublayer ([MLP] Description:
+ * (1) normalisation, (2) GEMM1 with bias1, (3) activation, (4) GEMM2 with
+ * bias2; Outputs: LayerNorm(x) -> GEMM1 -> Activation -> GEMM2).
+ * x: [rows, hidden]; gamma, beta: [hidden] (beta ignored for RMSNorm);
+ * kernel1: [hidden, G*ffn]; bias1: optional [G*ffn]; kernel2: [ffn, hidden];
+ * bias2: optional [hidden]; y: [rows, hidden]; all of `dtype`.
+ * With TE_QUANT_FP8_E4M3_CURRENT (dtype BF16): the normalised input, both
+ * kernels and the activation output are quantised per tensor; GEMM1 plus
+ * bias1 is rounded to bf16 (h1) and the activation is evaluated from that h1.
+ * saved: optional forward context (see te_mlp_saved).
+ * Workspace: te_layernorm_mlp_fwd_workspace_size(). */
+te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* beta,
+                               const void* kernel1, const void* bias1,
+                               const void* kernel2, const void* bias2,
+                               int64_t rows, int64_t hidden, int64_t ffn,
+                               te_dtype dtype, te_norm_type norm_type,
+                               int zero_centered_gamma, float epsilon,
+                               te_act_type act_type, te_quant quant,
+                               void* y, const te_mlp_saved* saved,
+                               void* workspace, size_t workspace_bytes, void* stream);
+size_t te_layernorm_mlp_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t ffn,
+                                           te_dtype dtype, te_act_type act_type,
+                                           te_quant quant);
+
+/* te_quantize - the per-tensor fp8 quantiser on its own ([ACT] Inputs:
+ * quantizer; [DENSE] Description: the normalised output and the kernel are
+ * quantised before the GEMM). x: [n] of x_dtype (F32 or BF16); codes: [n]
+ * bytes; meta: required, gets amax/scale/scale_inv. */
+te_status te_quantize(const void* x, int64_t n, te_dtype x_dtype, uint8_t* codes,
+                      const te_fp8_meta* meta, void* stream);
+
+/* te_dequantize - E4M3(code) * scale_inv back to F32 or BF16 ([ACT]
+ * Outputs: the activated tensor is dequantised back to the original
+ * precision). scale_inv is read from meta on the device. */
+te_status te_dequantize(const uint8_t* codes, int64_t n, const te_fp8_meta* meta,
+                        void* y, te_dtype y_dtype, void* stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* te_last_error(void);
+
+/* Library version string. */
+const char* te_version(void);
+
+/* Per-kernel timing, for benchmarks and profiling. When enabled, every
+ * kernel the library launches is bracketed by a pair of HIP events recorded
+ * on the launch stream. te_timing_collect() waits for the recorded events,
+ * adds their durations to per-kernel totals, and returns the number of
+ * distinct kernels seen; te_timing_get() reads entry i (name, launch count,
+ * total milliseconds). te_timing_reset() clears the totals. Not thread-safe. */
+te_status te_timing_enable(int enable);
+int te_timing_collect(void);
+te_status te_timing_get(int i, const char** name, int64_t* launches, double* total_ms);
+void te_timing_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TE_MI355X_H */

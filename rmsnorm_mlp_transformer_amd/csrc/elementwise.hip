@@ -1,0 +1,459 @@
+// HBM-bound kernels for gfx950: per-tensor amax and E4M3 quantisation
+// (current scaling), dequantisation, the activation forward (act_lu) and the
+// activation backward with the fused bias-gradient reduction (dact + dbias).
+//
+// Every kernel moves 16 bytes per lane per access so that one wave touches
+// 1 KiB of contiguous memory per load instruction.
+//
+// Sources: "NVIDIA TransformerEngine JAX Activation" (Description: forward
+// activation with optional quantisation, backward activation gradient;
+// Outputs: dequantised result); "... LayerNorm MLP" (Description: the fused
+// backward gives the activation gradient with the bias reduction);
+// "... LayerNorm Dense" (Description: the normalised input and the kernel
+// are quantised before the GEMM).
+#include "te_common.hpp"
+#include "te_kernels.hpp"
+
+namespace te {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void unpack8_bf16(const uint4& c, float* f) {
+  f[0] = bf16_lo(c.x); f[1] = bf16_hi(c.x); f[2] = bf16_lo(c.y); f[3] = bf16_hi(c.y);
+  f[4] = bf16_lo(c.z); f[5] = bf16_hi(c.z); f[6] = bf16_lo(c.w); f[7] = bf16_hi(c.w);
+}
+__device__ __forceinline__ uint4 pack8_bf16(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// Load 8 consecutive elements (bf16: one 16-byte load; fp32: two).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t e, float* f) {
+  if constexpr (BF16) {
+    unpack8_bf16(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + e), f);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + e);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + e + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void store8(void* base, int64_t e, const float* f) {
+  if constexpr (BF16) {
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + e) = pack8_bf16(f);
+  } else {
+    float* p = reinterpret_cast<float*>(base) + e;
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+}
+__device__ __forceinline__ uint2 encode8(const float* f, float scale) {
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w0 |= e4m3_encode(f[i] * scale) << (8 * i);
+    w1 |= e4m3_encode(f[i + 4] * scale) << (8 * i);
+  }
+  return make_uint2(w0, w1);
+}
+
+unsigned grid_for(int64_t work_items, int per_thread) {
+  int64_t blocks = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
+  if (blocks < 1) blocks = 1;
+  if (blocks > 65535LL * 16) blocks = 65535LL * 16;
+  return (unsigned)blocks;
+}
+
+// ------------------------------------------------------------------ fill / meta
+__global__ void fill_zero_kernel(float* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+__global__ void fill_zero_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Metadata of an empty tensor: amax 0, scale 1, scale_inv 1.
+__global__ void empty_meta_kernel(float* amax, float* scale, float* scale_inv) {
+  if (threadIdx.x == 0) {
+    *amax = 0.0f;
+    *scale = 1.0f;
+    *scale_inv = 1.0f;
+  }
+}
+
+// ------------------------------------------------------------------ amax
+// n is a multiple of 8 (every tensor size here is a multiple of 16).
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) amax_kernel(const void* x, int64_t n8, float* amax) {
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n8; c += stride) {
+    float f[8];
+    load8<BF16>(x, c * 8, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64_t n8, uint8_t* codes,
+                                                            const float* amax, float* scale_out,
+                                                            float* scale_inv_out) {
+  const float scale = fp8_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out != nullptr) {
+    *scale_out = scale;
+    *scale_inv_out = 1.0f / scale;
+  }
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n8; c += stride) {
+    float f[8];
+    load8<BF16>(x, c * 8, f);
+    *reinterpret_cast<uint2*>(codes + c * 8) = encode8(f, scale);
+  }
+}
+
+// Quantise x [rows, cols] into codes_t [cols, rows]. A 64 x 64 tile goes
+// through LDS: each lane reads 8 consecutive columns of one row (16 bytes for
+// bf16) and writes 16 consecutive rows of one column as 16 code bytes.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
+    const void* x, int64_t rows, int64_t cols, uint8_t* codes_t, const float* amax,
+    float* scale_out, float* scale_inv_out) {
+  __shared__ uint8_t tile[64][64 + 4];
+  const float scale = fp8_scale_from_amax(*amax);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && scale_out != nullptr) {
+    *scale_out = scale;
+    *scale_inv_out = 1.0f / scale;
+  }
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+  // read: 64 rows x 8 column-chunks = 512 chunks, 2 per thread
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int idx = t + p * kThreads;
+    const int r = idx >> 3, cc = (idx & 7) * 8;
+    float f[8];
+    if (r0 + r < rows && c0 + cc < cols) {
+      load8<BF16>(x, (r0 + r) * cols + c0 + cc, f);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[cc + i][r] = (uint8_t)e4m3_encode(f[i] * scale);
+  }
+  __syncthreads();
+  // write: 64 output rows (= input columns) x 4 chunks of 16 codes
+  const int oc = t >> 2, orr = (t & 3) * 16;
+  if (c0 + oc < cols && r0 + orr < rows) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = (uint32_t)tile[oc][orr + 4 * q] | ((uint32_t)tile[oc][orr + 4 * q + 1] << 8) |
+             ((uint32_t)tile[oc][orr + 4 * q + 2] << 16) | ((uint32_t)tile[oc][orr + 4 * q + 3] << 24);
+    }
+    *reinterpret_cast<uint4*>(codes_t + (c0 + oc) * rows + r0 + orr) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* codes, int64_t n8,
+                                                              const float* scale_inv, void* y) {
+  const float si = *scale_inv;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n8; c += stride) {
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + c * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = e4m3_decode((w.x >> (8 * i)) & 0xFF) * si;
+      f[i + 4] = e4m3_decode((w.y >> (8 * i)) & 0xFF) * si;
+    }
+    store8<BF16>(y, c * 8, f);
+  }
+}
+
+// ------------------------------------------------------------------ act_lu
+// Thread (x) = 8 output columns; blocks in y walk the rows with a stride.
+// MODE 0: store; 1: amax only; 2: E4M3 codes.
+template <bool BF16, int ACT, bool GATED, int MODE, int OUT>
+__global__ void __launch_bounds__(kThreads) act_kernel(const void* x, int64_t rows, int64_t cols,
+                                                       void* y, float* amax, float* scale_out,
+                                                       float* scale_inv_out) {
+  const int64_t in_cols = GATED ? 2 * cols : cols;
+  const int64_t cc = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
+  float scale = 1.0f;
+  if constexpr (MODE == 2) {
+    scale = fp8_scale_from_amax(*amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      *scale_out = scale;
+      *scale_inv_out = 1.0f / scale;
+    }
+  }
+  float m = 0.0f;
+  if (cc < cols) {
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+      float a[8], o[8];
+      load8<BF16>(x, r * in_cols + cc, a);
+      if constexpr (GATED) {
+        float b[8];
+        load8<BF16>(x, r * in_cols + cols + cc, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]) * b[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]);
+      }
+      if constexpr (MODE == 0) {
+        store8<OUT == kBF16>(y, r * cols + cc, o);
+      } else if constexpr (MODE == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(o[i]));
+      } else {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(y) + r * cols + cc) = encode8(o, scale);
+      }
+    }
+  }
+  if constexpr (MODE == 1) {
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  }
+}
+
+dim3 act_grid(int64_t rows, int64_t cols) {
+  const int64_t gx = (cols / 8 + kThreads - 1) / kThreads;
+  int64_t gy = (8192 + gx - 1) / gx;          // ~8192 blocks, each row handled by one block
+  if (gy > rows) gy = rows;
+  if (gy < 1) gy = 1;
+  if (gy > 65535) gy = 65535;
+  return dim3((unsigned)gx, (unsigned)gy);
+}
+
+// ------------------------------------------------------------------ dact + dbias
+// Block = 4 waves over one strip of 512 output columns (8 per lane) and one
+// chunk of rows; wave w takes rows w, w+4, ... of the chunk. Each lane keeps
+// fp32 column sums in registers; the 4 waves are combined in LDS and every
+// block writes one row of fp32 partials, which dbias_finalize sums in a fixed
+// order (bitwise reproducible).
+constexpr int kDactStrip = 512;
+
+template <bool BF16, int ACT, bool GATED>
+__global__ void __launch_bounds__(kThreads) dact_kernel(const void* grad, const void* x, int64_t rows,
+                                                        int64_t cols, int64_t rows_per_chunk,
+                                                        void* dx, float* partials) {
+  constexpr int G = GATED ? 2 : 1;
+  __shared__ float red[4][G][kDactStrip];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * kDactStrip + lane * 8;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
+  int64_t r_end = r_begin + rows_per_chunk;
+  if (r_end > rows) r_end = rows;
+  const int64_t xcols = G * cols;
+  float sa[8], sb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
+  if (col < cols) {
+    int64_t r = r_begin + w;
+#pragma unroll 2
+    for (; r < r_end; r += 4) {
+      float g[8], a[8], d[8];
+      load8<BF16>(grad, r * cols + col, g);
+      load8<BF16>(x, r * xcols + col, a);
+      if constexpr (GATED) {
+        float b[8], db[8];
+        load8<BF16>(x, r * xcols + cols + col, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d[i] = g[i] * b[i] * act_bwd<ACT>(a[i]);
+          db[i] = g[i] * act_fwd<ACT>(a[i]);
+          sa[i] += d[i];
+          sb[i] += db[i];
+        }
+        store8<BF16>(dx, r * xcols + col, d);
+        store8<BF16>(dx, r * xcols + cols + col, db);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d[i] = g[i] * act_bwd<ACT>(a[i]);
+          sa[i] += d[i];
+        }
+        store8<BF16>(dx, r * xcols + col, d);
+      }
+    }
+  }
+  if (partials == nullptr) return;   // no dbias requested (uniform across the block)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    red[w][0][lane * 8 + i] = sa[i];
+    if constexpr (GATED) red[w][G - 1][lane * 8 + i] = sb[i];
+  }
+  __syncthreads();
+  // 256 threads finalise G*512 columns: fixed order w = 0..3
+  for (int idx = threadIdx.x; idx < G * kDactStrip; idx += kThreads) {
+    const int h = idx / kDactStrip, cl = idx % kDactStrip;
+    const int64_t c = (int64_t)blockIdx.x * kDactStrip + cl;
+    if (c < cols) {
+      const float s = ((red[0][h][cl] + red[1][h][cl]) + red[2][h][cl]) + red[3][h][cl];
+      partials[(int64_t)blockIdx.y * xcols + h * cols + c] = s;
+    }
+  }
+}
+
+template <int OUT>
+__global__ void __launch_bounds__(kThreads) dbias_finalize_kernel(const float* partials, int64_t chunks,
+                                                                  int64_t n, void* dbias) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= n) return;
+  float s = 0.0f;
+  for (int64_t k = 0; k < chunks; ++k) s += partials[k * n + c];
+  if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(dbias)[c] = f32_to_bf16(s);
+  else reinterpret_cast<float*>(dbias)[c] = s;
+}
+
+template <bool BF16>
+hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool gated, int mode,
+                        void* y, int y_dtype, float* amax, float* so, float* sio, hipStream_t s) {
+  const dim3 grid = act_grid(rows, cols);
+#define TE_ACT_CASE(A, G)                                                                         \
+  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
+  else if (mode == 2) act_kernel<BF16, A, G, 2, kE4M3><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
+  else if (y_dtype == kBF16) act_kernel<BF16, A, G, 0, kBF16><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
+  else act_kernel<BF16, A, G, 0, kF32><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio);
+#define TE_ACT_G(A) if (gated) { TE_ACT_CASE(A, true) } else { TE_ACT_CASE(A, false) }
+  switch (act) {
+    case kRelu: TE_ACT_G(kRelu) break;
+    case kGelu: TE_ACT_G(kGelu) break;
+    case kGeluErf: TE_ACT_G(kGeluErf) break;
+    case kSilu: TE_ACT_G(kSilu) break;
+    default: TE_ACT_G(kLinear) break;
+  }
+#undef TE_ACT_G
+#undef TE_ACT_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(float* p, int n, hipStream_t s) {
+  LaunchScope scope("fill_zero", s);
+  fill_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_bytes(void* p, int64_t nbytes, hipStream_t s) {
+  LaunchScope scope("fill_zero", s);
+  const int64_t words = nbytes / 4;
+  fill_zero_words_kernel<<<(unsigned)((words + 255) / 256), 256, 0, s>>>(reinterpret_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStream_t s) {
+  LaunchScope scope("empty_meta", s);
+  empty_meta_kernel<<<1, 64, 0, s>>>(amax, scale, scale_inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s) {
+  LaunchScope scope("amax", s);
+  const unsigned grid = grid_for(n / 8, 8);
+  if (x_dtype == kBF16) amax_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
+  else amax_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes, const float* amax,
+                           float* scale_out, float* scale_inv_out, hipStream_t s) {
+  LaunchScope scope("quantize", s);
+  const unsigned grid = grid_for(n / 8, 4);
+  if (x_dtype == kBF16)
+    quantize_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, codes, amax, scale_out, scale_inv_out);
+  else
+    quantize_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, codes, amax, scale_out, scale_inv_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
+                                     uint8_t* codes_t, const float* amax, float* scale_out,
+                                     float* scale_inv_out, hipStream_t s) {
+  LaunchScope scope("quantize_transpose", s);
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (x_dtype == kBF16)
+    quantize_transpose_kernel<true><<<grid, kThreads, 0, s>>>(x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
+  else
+    quantize_transpose_kernel<false><<<grid, kThreads, 0, s>>>(x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale_inv, void* y,
+                             int y_dtype, hipStream_t s) {
+  LaunchScope scope("dequantize", s);
+  const unsigned grid = grid_for(n / 8, 4);
+  if (y_dtype == kBF16) dequantize_kernel<true><<<grid, kThreads, 0, s>>>(codes, n / 8, scale_inv, y);
+  else dequantize_kernel<false><<<grid, kThreads, 0, s>>>(codes, n / 8, scale_inv, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, int act, bool gated,
+                      int mode, void* y, int y_dtype, float* amax, float* scale_out,
+                      float* scale_inv_out, hipStream_t s) {
+  static const char* names[3] = {"act_lu", "act_amax", "act_quant"};
+  LaunchScope scope(names[mode], s);
+  if (x_dtype == kBF16)
+    return act_dispatch<true>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
+  return act_dispatch<false>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
+}
+
+int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated) {
+  (void)gated;
+  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
+  int64_t chunks = (2048 + strips - 1) / strips;     // aim for ~2048 blocks (8 per CU)
+  const int64_t max_chunks = (rows + 15) / 16;         // at least 16 rows per block
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  return chunks;
+}
+
+hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                             int act, bool gated, void* dx, void* dbias, int dbias_dtype,
+                             float* partials, hipStream_t s) {
+  const int64_t chunks = dact_row_chunks(rows, cols, gated);
+  const int64_t rpc = (rows + chunks - 1) / chunks;
+  const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
+  {
+    LaunchScope scope("dact_dbias", s);
+#define TE_DACT(B, A, G) dact_kernel<B, A, G><<<grid, kThreads, 0, s>>>(grad, x, rows, cols, rpc, dx, partials)
+#define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);
+#define TE_DACT_A(B)                                   \
+  switch (act) {                                       \
+    case kRelu: TE_DACT_G(B, kRelu) break;             \
+    case kGelu: TE_DACT_G(B, kGelu) break;             \
+    case kGeluErf: TE_DACT_G(B, kGeluErf) break;       \
+    case kSilu: TE_DACT_G(B, kSilu) break;             \
+    default: TE_DACT_G(B, kLinear) break;              \
+  }
+    if (dtype == kBF16) { TE_DACT_A(true) } else { TE_DACT_A(false) }
+#undef TE_DACT_A
+#undef TE_DACT_G
+#undef TE_DACT
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dbias != nullptr) {
+    LaunchScope scope("dbias_finalize", s);
+    const int64_t n = (gated ? 2 : 1) * cols;
+    const unsigned g2 = (unsigned)((n + kThreads - 1) / kThreads);
+    if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
+    else dbias_finalize_kernel<kF32><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace te

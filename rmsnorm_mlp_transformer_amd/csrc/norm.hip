@@ -1,0 +1,244 @@
+// Row-wise LayerNorm / RMSNorm forward for gfx950.
+//
+// One 64-lane wavefront owns one row: the row is read once into registers
+// with 16-byte loads (each load instruction of the wave covers 1 KiB of the
+// row), the mean and the centred sum of squares are reduced across the wave
+// in fp32, and the normalised row is written straight out in the layout and
+// precision the following GEMM reads as its A operand (fp32, bf16 or E4M3),
+// so no separate normalised tensor is produced. Rows wider than the register
+// budget fall back to a loop that re-reads the row from cache.
+//
+// Definitions ("NVIDIA TransformerEngine JAX LayerNorm MLP", Description step
+// (1); "... LayerNorm Dense", Inputs: gamma, beta, norm_type,
+// zero_centered_gamma, epsilon): LayerNorm y = (x - mean) / sqrt(var + eps)
+// * g + beta with the biased variance; RMSNorm y = x / sqrt(mean(x^2) + eps)
+// * g; g = 1 + gamma for a zero-centred gamma.
+#include "te_common.hpp"
+#include "te_kernels.hpp"
+
+namespace te {
+namespace {
+
+template <bool BF16>
+struct Io {
+  static constexpr int VEC = BF16 ? 8 : 4;   // elements per 16-byte chunk
+  static __device__ __forceinline__ void unpack(const uint4& c, float* f) {
+    if constexpr (BF16) {
+      f[0] = bf16_lo(c.x); f[1] = bf16_hi(c.x); f[2] = bf16_lo(c.y); f[3] = bf16_hi(c.y);
+      f[4] = bf16_lo(c.z); f[5] = bf16_hi(c.z); f[6] = bf16_lo(c.w); f[7] = bf16_hi(c.w);
+    } else {
+      f[0] = __uint_as_float(c.x); f[1] = __uint_as_float(c.y);
+      f[2] = __uint_as_float(c.z); f[3] = __uint_as_float(c.w);
+    }
+  }
+};
+
+// The normalised value; the same operation sequence in every mode, so the
+// amax pass and the quantise pass see bit-identical values.
+__device__ __forceinline__ float norm_value(float v, float mean, float rs, float g, float b) {
+#pragma clang fp contract(off)
+  return __builtin_fmaf((v - mean) * rs, g, b);
+}
+
+// Store VEC output values of chunk `c` of row `row`.
+template <int OUT, int VEC>
+__device__ __forceinline__ void store_chunk(void* y, int64_t row, int64_t hidden, int64_t c,
+                                            const float* v, float qscale) {
+  const int64_t e = row * hidden + c * VEC;
+  if constexpr (OUT == kF32) {
+    float* p = reinterpret_cast<float*>(y) + e;
+#pragma unroll
+    for (int i = 0; i < VEC; i += 4)
+      *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+  } else if constexpr (OUT == kBF16) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(y) + e;
+    if constexpr (VEC == 8) {
+      *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    } else {
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  } else {
+    uint8_t* p = reinterpret_cast<uint8_t*>(y) + e;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) w[i / 4] |= e4m3_encode(v[i] * qscale) << (8 * (i % 4));
+    if constexpr (VEC == 8) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint32_t*>(p) = w[0];
+  }
+}
+
+struct NormArgs {
+  const void* x; const void* gamma; const void* beta;
+  int64_t rows, hidden; float eps; int zcg;
+  void* y; float* mu; float* rsigma; float* amax; float* scale_out; float* scale_inv_out;
+};
+
+// NCH > 0: NCH 16-byte chunks per lane kept in registers. NCH == 0: loop.
+template <bool BF16, int NCH, bool RMS, int MODE, int OUT>
+__global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
+  using I = Io<BF16>;
+  constexpr int VEC = I::VEC;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int64_t nch = a.hidden / VEC;
+  const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
+  const uint4* gr = reinterpret_cast<const uint4*>(a.gamma);
+  const uint4* br = reinterpret_cast<const uint4*>(a.beta);
+  const float inv_h = 1.0f / (float)a.hidden;
+
+  float qscale = 1.0f;
+  if constexpr (MODE == kNormQuant) {
+    qscale = fp8_scale_from_amax(*a.amax);
+    if (row == 0 && lane == 0) {
+      *a.scale_out = qscale;
+      *a.scale_inv_out = 1.0f / qscale;
+    }
+  }
+
+  float mean = 0.0f, rs;
+  float lmax = 0.0f;
+  if constexpr (NCH > 0) {
+    float v[NCH][VEC];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int64_t c = lane + 64 * j;
+      if (c < nch) {
+        I::unpack(xr[c], v[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) v[j][i] = 0.0f;
+      }
+      if constexpr (!RMS) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += v[j][i];
+      }
+    }
+    if constexpr (!RMS) mean = wave_sum(s) * inv_h;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (lane + 64 * j < nch) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float d = v[j][i] - mean;
+          ss += d * d;
+        }
+      }
+    }
+    rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
+    if constexpr (MODE != kNormQuant) {
+      if (lane == 0) {
+        if (a.mu != nullptr && !RMS) a.mu[row] = mean;
+        if (a.rsigma != nullptr) a.rsigma[row] = rs;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int64_t c = lane + 64 * j;
+      if (c < nch) {
+        float g[VEC], b[VEC], y[VEC];
+        I::unpack(gr[c], g);
+        if constexpr (!RMS) I::unpack(br[c], b);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float gi = a.zcg ? 1.0f + g[i] : g[i];
+          y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
+          lmax = fmaxf(lmax, fabsf(y[i]));
+        }
+        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+      }
+    }
+  } else {
+    float s = 0.0f, v[VEC];
+    if constexpr (!RMS) {
+      for (int64_t c = lane; c < nch; c += 64) {
+        I::unpack(xr[c], v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += v[i];
+      }
+      mean = wave_sum(s) * inv_h;
+    }
+    float ss = 0.0f;
+    for (int64_t c = lane; c < nch; c += 64) {
+      I::unpack(xr[c], v);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float d = v[i] - mean;
+        ss += d * d;
+      }
+    }
+    rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
+    if constexpr (MODE != kNormQuant) {
+      if (lane == 0) {
+        if (a.mu != nullptr && !RMS) a.mu[row] = mean;
+        if (a.rsigma != nullptr) a.rsigma[row] = rs;
+      }
+    }
+    for (int64_t c = lane; c < nch; c += 64) {
+      float g[VEC], b[VEC], y[VEC];
+      I::unpack(xr[c], v);
+      I::unpack(gr[c], g);
+      if constexpr (!RMS) I::unpack(br[c], b);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        const float gi = a.zcg ? 1.0f + g[i] : g[i];
+        y[i] = norm_value(v[i], mean, rs, gi, RMS ? 0.0f : b[i]);
+        lmax = fmaxf(lmax, fabsf(y[i]));
+      }
+      if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+    }
+  }
+  if constexpr (MODE == kNormAmax) {
+    lmax = wave_max(lmax);
+    if (lane == 0) atomic_max_nonneg(a.amax, lmax);
+  }
+}
+
+template <bool BF16, int NCH, bool RMS>
+hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  if (mode == kNormAmax) {
+    norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32><<<grid, block, 0, s>>>(a);
+  } else if (mode == kNormQuant) {
+    norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3><<<grid, block, 0, s>>>(a);
+  } else if (y_dtype == kF32) {
+    norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kF32><<<grid, block, 0, s>>>(a);
+  } else {
+    norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kBF16><<<grid, block, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16, bool RMS>
+hipError_t dispatch_nch(const NormArgs& a, int mode, int y_dtype, hipStream_t s) {
+  const int64_t nch = a.hidden / Io<BF16>::VEC;
+  const int64_t per_lane = (nch + 63) / 64;
+  if (per_lane <= 1) return dispatch_mode<BF16, 1, RMS>(a, mode, y_dtype, s);
+  if (per_lane <= 2) return dispatch_mode<BF16, 2, RMS>(a, mode, y_dtype, s);
+  if (per_lane <= 4) return dispatch_mode<BF16, 4, RMS>(a, mode, y_dtype, s);
+  if (per_lane <= 8) return dispatch_mode<BF16, 8, RMS>(a, mode, y_dtype, s);
+  return dispatch_mode<BF16, 0, RMS>(a, mode, y_dtype, s);
+}
+
+}  // namespace
+
+hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
+                       int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
+                       int y_dtype, void* y, float* mu, float* rsigma, float* amax,
+                       float* scale_out, float* scale_inv_out, hipStream_t s) {
+  static const char* names[3] = {"norm_fwd", "norm_amax", "norm_quant"};
+  LaunchScope scope(names[mode], s);
+  NormArgs a{x, gamma, beta, rows, hidden, eps, zcg ? 1 : 0, y, mu, rsigma, amax, scale_out,
+             scale_inv_out};
+  if (x_dtype == kBF16) {
+    return rms ? dispatch_nch<true, true>(a, mode, y_dtype, s)
+               : dispatch_nch<true, false>(a, mode, y_dtype, s);
+  }
+  return rms ? dispatch_nch<false, true>(a, mode, y_dtype, s)
+             : dispatch_nch<false, false>(a, mode, y_dtype, s);
+}
+
+}  // namespace te

@@ -1,0 +1,537 @@
+// C ABI of the library: argument validation, workspace layout and the launch
+// sequence of every entry point declared in include/te_mi355x.h.
+//
+// Every entry point validates all of its arguments before the first HIP call,
+// so a failed call writes nothing and the validation paths run without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "te_kernels.hpp"
+#include "../../include/te_mi355x.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+te_status fail(te_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+te_status ok() {
+  g_error.clear();
+  return TE_SUCCESS;
+}
+
+te_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TE_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+#define TE_ARG(cond, ...) TE_REQUIRE(cond, TE_ERR_INVALID_ARGUMENT, __VA_ARGS__)
+#define TE_HIP(expr, what)                                   \
+  do {                                                       \
+    const hipError_t e_ = (expr);                            \
+    if (e_ != hipSuccess) return hip_status(e_, what);       \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool feature_ok(int64_t n) { return n > 0 && n % 16 == 0 && n <= (int64_t)1 << 30; }
+bool valid_act(int a) { return a >= TE_ACT_RELU && a <= TE_ACT_SWIGLU; }
+bool is_gated(int a) { return a >= TE_ACT_REGLU; }
+int act_kind(int a) {
+  switch (a) {
+    case TE_ACT_RELU: case TE_ACT_REGLU: return te::kRelu;
+    case TE_ACT_GELU: case TE_ACT_GEGLU: return te::kGelu;
+    case TE_ACT_GELU_ERF: return te::kGeluErf;
+    case TE_ACT_SILU: case TE_ACT_SWIGLU: return te::kSilu;
+    default: return te::kLinear;
+  }
+}
+size_t esize(int dt) { return dt == TE_F32 ? 4 : dt == TE_BF16 ? 2 : 1; }
+bool meta_ok(const te_fp8_meta* m) {
+  return m != nullptr && m->amax != nullptr && m->scale != nullptr && m->scale_inv != nullptr;
+}
+bool meta_complete(const te_fp8_meta& m) {
+  return m.amax != nullptr && m.scale != nullptr && m.scale_inv != nullptr;
+}
+
+// Carves 256-byte aligned sub-buffers from the caller's workspace. With a
+// NULL base it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~size_t(255);
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+  float* floats(size_t n) { return static_cast<float*>(take(n * sizeof(float))); }
+};
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// fp8 metadata slots: caller's meta when complete, else workspace floats.
+struct Meta {
+  float* amax;
+  float* scale;
+  float* scale_inv;
+};
+Meta pick_meta(const te_fp8_meta* user, float* ws3) {
+  if (user != nullptr && meta_complete(*user)) return {user->amax, user->scale, user->scale_inv};
+  return {ws3, ws3 ? ws3 + 1 : nullptr, ws3 ? ws3 + 2 : nullptr};
+}
+
+// ---------------------------------------------------------------- per-kernel timing
+struct TimingRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct TimingTotal {
+  std::string name;
+  int64_t launches;
+  double ms;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+std::vector<TimingTotal> g_totals;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// ---------------------------------------------------------------- layouts
+struct DenseWs {
+  void* xn;        // normalised input (F32/BF16) or codes
+  uint8_t* wt;     // fp8: kernel codes, transposed
+  float* metas;    // fp8: 6 floats
+};
+DenseWs dense_ws(Carver& c, int64_t rows, int64_t hidden, int64_t out, int dtype, int quant) {
+  DenseWs w{};
+  if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
+    w.metas = c.floats(6);
+    w.xn = c.take((size_t)rows * hidden);
+    w.wt = static_cast<uint8_t*>(c.take((size_t)out * hidden));
+  } else {
+    w.xn = c.take((size_t)rows * hidden * esize(dtype));
+  }
+  return w;
+}
+
+struct MlpWs {
+  void* xn;        // normalised input (F32/BF16) or its codes
+  void* act;       // activation output (F32/BF16) or its codes
+  uint8_t* w1t;    // fp8: kernel1 codes transposed [G*ffn, hidden]
+  uint8_t* w2t;    // fp8: kernel2 codes transposed [hidden, ffn]
+  void* h1;        // fp8: GEMM1 output + bias1, bf16 [rows, G*ffn] (when not saved)
+  float* metas;    // fp8: 12 floats
+};
+MlpWs mlp_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int dtype, int act, int quant,
+             bool need_h1) {
+  MlpWs w{};
+  const int64_t g = is_gated(act) ? 2 : 1;
+  if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
+    w.metas = c.floats(12);
+    w.xn = c.take((size_t)rows * hidden);
+    w.w1t = static_cast<uint8_t*>(c.take((size_t)g * ffn * hidden));
+    w.w2t = static_cast<uint8_t*>(c.take((size_t)hidden * ffn));
+    if (need_h1) w.h1 = c.take((size_t)rows * g * ffn * 2);
+    w.act = c.take((size_t)rows * ffn);
+  } else {
+    w.xn = c.take((size_t)rows * hidden * esize(dtype));
+    w.act = c.take((size_t)rows * ffn * esize(dtype));
+  }
+  return w;
+}
+
+te_status check_dtype_quant(te_dtype dtype, te_quant quant) {
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16 || dtype == TE_E4M3, "invalid dtype %d", (int)dtype);
+  TE_ARG(quant == TE_QUANT_NONE || quant == TE_QUANT_FP8_E4M3_CURRENT, "invalid quant %d", (int)quant);
+  TE_REQUIRE(dtype != TE_E4M3, TE_ERR_UNSUPPORTED, "E4M3 is not an input dtype");
+  TE_REQUIRE(!(dtype == TE_F32 && quant != TE_QUANT_NONE), TE_ERR_UNSUPPORTED,
+             "fp8 quantisation requires dtype TE_BF16");
+  return TE_SUCCESS;
+}
+
+te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
+                     int64_t hidden, te_norm_type nt, float eps) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows must be in [0, 2^31], got %lld", (long long)rows);
+  TE_ARG(feature_ok(hidden), "hidden must be a positive multiple of 16, got %lld", (long long)hidden);
+  TE_ARG(nt == TE_LAYERNORM || nt == TE_RMSNORM, "invalid norm_type %d", (int)nt);
+  TE_ARG(eps >= 0.0f && eps < 1e30f, "epsilon must be finite and >= 0");
+  TE_ARG(x != nullptr && gamma != nullptr, "x and gamma are required");
+  TE_ARG(nt == TE_RMSNORM || beta != nullptr, "beta is required for layernorm");
+  TE_ARG(aligned16(x) && aligned16(gamma) && (beta == nullptr || aligned16(beta)),
+         "x, gamma and beta must be 16-byte aligned");
+  return TE_SUCCESS;
+}
+
+}  // namespace
+
+namespace te {
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_timing) return;
+  hipEvent_t a = pooled_event(), b = pooled_event();
+  if (a == nullptr || b == nullptr) return;
+  if (hipEventRecord(a, s) != hipSuccess) return;
+  g_pending.push_back({name, a, b});
+  slot = (int)g_pending.size() - 1;
+}
+LaunchScope::~LaunchScope() {
+  if (slot >= 0) (void)hipEventRecord(g_pending[slot].stop, stream);
+}
+}  // namespace te
+
+extern "C" {
+
+const char* te_last_error(void) { return g_error.c_str(); }
+const char* te_version(void) { return "temi355x 0.1.0 (gfx950)"; }
+
+// ---------------------------------------------------------------- timing
+te_status te_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return ok();
+}
+int te_timing_collect(void) {
+  for (auto& r : g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+      TimingTotal* t = nullptr;
+      for (auto& e : g_totals)
+        if (e.name == r.name) t = &e;
+      if (t == nullptr) {
+        g_totals.push_back({r.name, 0, 0.0});
+        t = &g_totals.back();
+      }
+      t->launches += 1;
+      t->ms += ms;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_pending.clear();
+  return (int)g_totals.size();
+}
+te_status te_timing_get(int i, const char** name, int64_t* launches, double* total_ms) {
+  TE_ARG(i >= 0 && i < (int)g_totals.size(), "timing index %d out of range", i);
+  if (name) *name = g_totals[i].name.c_str();
+  if (launches) *launches = g_totals[i].launches;
+  if (total_ms) *total_ms = g_totals[i].ms;
+  return ok();
+}
+void te_timing_reset(void) {
+  te_timing_collect();
+  g_totals.clear();
+}
+
+// ---------------------------------------------------------------- norm
+size_t te_layernorm_fwd_workspace_size(int64_t, int64_t, te_dtype, te_dtype) { return 0; }
+
+te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta, int64_t rows,
+                           int64_t hidden, te_dtype x_dtype, te_norm_type norm_type,
+                           int zero_centered_gamma, float epsilon, void* y, te_dtype y_dtype,
+                           const te_fp8_meta* y_meta, float* mu, float* rsigma, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  te_status st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
+  if (st != TE_SUCCESS) return st;
+  TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype");
+  TE_ARG(y != nullptr && aligned16(y), "y is required and must be 16-byte aligned");
+  TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
+  hipStream_t s = as_stream(stream);
+  if (rows == 0) {
+    if (y_dtype == TE_E4M3) TE_HIP(te::launch_empty_meta(y_meta->amax, y_meta->scale, y_meta->scale_inv, s), "meta");
+    return ok();
+  }
+  const bool rms = norm_type == TE_RMSNORM;
+  if (y_dtype != TE_E4M3) {
+    TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
+                           te::kNormStore, y_dtype, y, mu, rsigma, nullptr, nullptr, nullptr, s),
+           "norm");
+    return ok();
+  }
+  TE_HIP(te::launch_fill_zero(y_meta->amax, 1, s), "fill");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
+                         te::kNormAmax, y_dtype, nullptr, mu, rsigma, y_meta->amax, nullptr, nullptr, s),
+         "norm amax");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
+                         te::kNormQuant, y_dtype, y, nullptr, nullptr, y_meta->amax, y_meta->scale,
+                         y_meta->scale_inv, s),
+         "norm quantise");
+  return ok();
+}
+
+// ---------------------------------------------------------------- activation
+te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype, te_act_type act_type,
+                    void* y, te_dtype y_dtype, const te_fp8_meta* y_meta, void* stream) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype");
+  TE_ARG(x != nullptr && y != nullptr && aligned16(x) && aligned16(y), "x and y are required, 16-byte aligned");
+  TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
+  hipStream_t s = as_stream(stream);
+  if (rows == 0) {
+    if (y_dtype == TE_E4M3) TE_HIP(te::launch_empty_meta(y_meta->amax, y_meta->scale, y_meta->scale_inv, s), "meta");
+    return ok();
+  }
+  const bool g = is_gated(act_type);
+  const int k = act_kind(act_type);
+  if (y_dtype != TE_E4M3) {
+    TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 0, y, y_dtype, nullptr, nullptr, nullptr, s), "act");
+    return ok();
+  }
+  TE_HIP(te::launch_fill_zero(y_meta->amax, 1, s), "fill");
+  TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 1, nullptr, y_dtype, y_meta->amax, nullptr, nullptr, s),
+         "act amax");
+  TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 2, y, y_dtype, y_meta->amax, y_meta->scale,
+                        y_meta->scale_inv, s),
+         "act quantise");
+  return ok();
+}
+
+size_t te_dact_dbias_workspace_size(int64_t rows, int64_t cols, te_act_type act_type) {
+  if (rows <= 0 || cols <= 0) return 0;
+  const bool g = is_gated(act_type);
+  Carver c(nullptr);
+  c.floats((size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols);
+  return c.off;
+}
+
+te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
+                        te_act_type act_type, void* dx, void* dbias, te_dtype dbias_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
+  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(grad != nullptr && x != nullptr && dx != nullptr, "grad, x and dx are required");
+  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
+         "pointers must be 16-byte aligned");
+  const size_t need = te_dact_dbias_workspace_size(rows, cols, act_type);
+  if (dbias != nullptr) {
+    TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL,
+               "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    TE_ARG(workspace != nullptr && aligned16(workspace), "workspace is required (16-byte aligned)");
+  }
+  hipStream_t s = as_stream(stream);
+  const bool g = is_gated(act_type);
+  if (rows == 0) {   // the bias gradient of an empty batch is zero
+    if (dbias != nullptr) TE_HIP(te::launch_fill_zero_bytes(dbias, (g ? 2 : 1) * cols * (int64_t)esize(dbias_dtype), s), "fill");
+    return ok();
+  }
+  Carver c(workspace);
+  float* partials = dbias != nullptr ? c.floats((size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols) : nullptr;
+  TE_HIP(te::launch_dact_dbias(grad, x, rows, cols, dtype, act_kind(act_type), g, dx, dbias, dbias_dtype,
+                               partials, s),
+         "dact_dbias");
+  return ok();
+}
+
+// ---------------------------------------------------------------- quantiser
+te_status te_quantize(const void* x, int64_t n, te_dtype x_dtype, uint8_t* codes, const te_fp8_meta* meta,
+                      void* stream) {
+  TE_ARG(n >= 0 && n % 16 == 0, "n must be a non-negative multiple of 16");
+  TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(x != nullptr && codes != nullptr && aligned16(x) && aligned16(codes), "x and codes are required, 16-byte aligned");
+  TE_ARG(meta_ok(meta), "meta with amax, scale and scale_inv is required");
+  hipStream_t s = as_stream(stream);
+  TE_HIP(te::launch_fill_zero(meta->amax, 1, s), "fill");
+  if (n > 0) TE_HIP(te::launch_amax(x, n, x_dtype, meta->amax, s), "amax");
+  TE_HIP(te::launch_quantize(x, n, x_dtype, codes, meta->amax, meta->scale, meta->scale_inv, s), "quantise");
+  return ok();
+}
+
+te_status te_dequantize(const uint8_t* codes, int64_t n, const te_fp8_meta* meta, void* y, te_dtype y_dtype,
+                        void* stream) {
+  TE_ARG(n >= 0 && n % 16 == 0, "n must be a non-negative multiple of 16");
+  TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16, "y_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(codes != nullptr && y != nullptr && aligned16(codes) && aligned16(y), "codes and y are required, 16-byte aligned");
+  TE_ARG(meta != nullptr && meta->scale_inv != nullptr, "meta->scale_inv is required");
+  if (n == 0) return ok();
+  TE_HIP(te::launch_dequantize(codes, n, meta->scale_inv, y, y_dtype, as_stream(stream)), "dequantise");
+  return ok();
+}
+
+// ---------------------------------------------------------------- layernorm + dense
+size_t te_layernorm_dense_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t out_features, te_dtype dtype,
+                                             te_quant quant) {
+  if (rows < 0 || hidden <= 0 || out_features <= 0) return 0;
+  Carver c(nullptr);
+  dense_ws(c, rows, hidden, out_features, dtype, quant);
+  return c.off;
+}
+
+te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* gamma, const void* beta,
+                                 const void* bias, int64_t rows, int64_t hidden, int64_t out_features,
+                                 te_dtype dtype, te_norm_type norm_type, int zero_centered_gamma, float epsilon,
+                                 te_quant quant, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  te_status st = check_dtype_quant(dtype, quant);
+  if (st != TE_SUCCESS) return st;
+  st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
+  if (st != TE_SUCCESS) return st;
+  TE_ARG(feature_ok(out_features), "out_features must be a positive multiple of 16");
+  TE_ARG(kernel != nullptr && y != nullptr && aligned16(kernel) && aligned16(y), "kernel and y are required, 16-byte aligned");
+  TE_ARG(bias == nullptr || aligned16(bias), "bias must be 16-byte aligned");
+  const size_t need = te_layernorm_dense_fwd_workspace_size(rows, hidden, out_features, dtype, quant);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
+  if (rows == 0) return ok();
+  hipStream_t s = as_stream(stream);
+  Carver c(workspace);
+  DenseWs w = dense_ws(c, rows, hidden, out_features, dtype, quant);
+  const bool rms = norm_type == TE_RMSNORM, zcg = zero_centered_gamma != 0;
+  te::Epilogue ep{bias, y, nullptr, nullptr, te::kLinear, false};
+  if (quant == TE_QUANT_NONE) {
+    TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn,
+                           nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
+    if (dtype == TE_F32)
+      TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.xn), static_cast<const float*>(kernel), rows,
+                                 out_features, hidden, ep, s), "gemm");
+    else
+      TE_HIP(te::launch_gemm_bf16(w.xn, kernel, rows, out_features, hidden, ep, s), "gemm");
+    return ok();
+  }
+  float* mx = w.metas;      // amax, scale, scale_inv of the normalised input
+  float* mw = w.metas + 3;  // ... of the kernel
+  TE_HIP(te::launch_fill_zero(w.metas, 6, s), "fill");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr,
+                         nullptr, nullptr, mx, nullptr, nullptr, s), "norm amax");
+  TE_HIP(te::launch_amax(kernel, hidden * out_features, dtype, mw, s), "kernel amax");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
+                         nullptr, nullptr, mx, mx + 1, mx + 2, s), "norm quantise");
+  TE_HIP(te::launch_quantize_transpose(kernel, hidden, out_features, dtype, w.wt, mw, mw + 1, mw + 2, s),
+         "kernel quantise");
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.wt, rows, out_features, hidden, mx, mw, ep, s),
+         "fp8 gemm");
+  return ok();
+}
+
+// ---------------------------------------------------------------- layernorm MLP
+size_t te_layernorm_mlp_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t ffn, te_dtype dtype,
+                                           te_act_type act_type, te_quant quant) {
+  if (rows < 0 || hidden <= 0 || ffn <= 0) return 0;
+  Carver c(nullptr);
+  mlp_ws(c, rows, hidden, ffn, dtype, act_type, quant, true);
+  return c.off;
+}
+
+te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* beta, const void* kernel1,
+                               const void* bias1, const void* kernel2, const void* bias2, int64_t rows,
+                               int64_t hidden, int64_t ffn, te_dtype dtype, te_norm_type norm_type,
+                               int zero_centered_gamma, float epsilon, te_act_type act_type, te_quant quant,
+                               void* y, const te_mlp_saved* saved, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  te_status st = check_dtype_quant(dtype, quant);
+  if (st != TE_SUCCESS) return st;
+  st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
+  if (st != TE_SUCCESS) return st;
+  TE_ARG(feature_ok(ffn), "ffn must be a positive multiple of 16, got %lld", (long long)ffn);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(kernel1 != nullptr && kernel2 != nullptr && y != nullptr, "kernel1, kernel2 and y are required");
+  TE_ARG(aligned16(kernel1) && aligned16(kernel2) && aligned16(y) && (bias1 == nullptr || aligned16(bias1)) &&
+             (bias2 == nullptr || aligned16(bias2)),
+         "tensors must be 16-byte aligned");
+  void* h1_user = saved ? saved->h1 : nullptr;
+  float* mu = saved ? saved->mu : nullptr;
+  float* rsigma = saved ? saved->rsigma : nullptr;
+  TE_ARG(h1_user == nullptr || aligned16(h1_user), "saved->h1 must be 16-byte aligned");
+  if (saved != nullptr)
+    TE_ARG(aligned16(saved->xq) && aligned16(saved->w1q_t) && aligned16(saved->w2q_t) && aligned16(saved->actq),
+           "saved code buffers must be 16-byte aligned");
+  const size_t need = te_layernorm_mlp_fwd_workspace_size(rows, hidden, ffn, dtype, act_type, quant);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(workspace != nullptr && aligned16(workspace), "workspace is required (16-byte aligned)");
+  if (rows == 0) return ok();
+
+  hipStream_t s = as_stream(stream);
+  Carver c(workspace);
+  MlpWs w = mlp_ws(c, rows, hidden, ffn, dtype, act_type, quant, true);
+  const bool rms = norm_type == TE_RMSNORM, zcg = zero_centered_gamma != 0;
+  const bool gated = is_gated(act_type);
+  const int k = act_kind(act_type);
+  const int64_t nb1 = (gated ? 2 : 1) * ffn;
+
+  if (quant == TE_QUANT_NONE) {
+    TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn, mu,
+                           rsigma, nullptr, nullptr, nullptr, s), "norm");
+    te::Epilogue e1{bias1, w.act, h1_user, nullptr, k, gated};
+    te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
+    if (dtype == TE_F32) {
+      TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.xn), static_cast<const float*>(kernel1), rows, nb1,
+                                 hidden, e1, s), "gemm1");
+      TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.act), static_cast<const float*>(kernel2), rows,
+                                 hidden, ffn, e2, s), "gemm2");
+    } else {
+      TE_HIP(te::launch_gemm_bf16(w.xn, kernel1, rows, nb1, hidden, e1, s), "gemm1");
+      TE_HIP(te::launch_gemm_bf16(w.act, kernel2, rows, hidden, ffn, e2, s), "gemm2");
+    }
+    return ok();
+  }
+
+  Meta mx = pick_meta(saved ? &saved->x_meta : nullptr, w.metas);
+  Meta m1 = pick_meta(saved ? &saved->w1_meta : nullptr, w.metas + 3);
+  Meta ma = pick_meta(saved ? &saved->act_meta : nullptr, w.metas + 6);
+  Meta m2 = pick_meta(saved ? &saved->w2_meta : nullptr, w.metas + 9);
+  void* h1 = h1_user != nullptr ? h1_user : w.h1;
+  if (saved != nullptr) {
+    if (saved->xq != nullptr) w.xn = saved->xq;
+    if (saved->w1q_t != nullptr) w.w1t = saved->w1q_t;
+    if (saved->w2q_t != nullptr) w.w2t = saved->w2q_t;
+    if (saved->actq != nullptr) w.act = saved->actq;
+  }
+  TE_HIP(te::launch_fill_zero(w.metas, 12, s), "fill");
+  for (const Meta* m : {&mx, &m1, &ma, &m2})
+    if (m->amax < w.metas || m->amax >= w.metas + 12) TE_HIP(te::launch_fill_zero(m->amax, 1, s), "fill");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr, mu,
+                         rsigma, mx.amax, nullptr, nullptr, s), "norm amax");
+  TE_HIP(te::launch_amax(kernel1, hidden * nb1, dtype, m1.amax, s), "kernel1 amax");
+  TE_HIP(te::launch_amax(kernel2, ffn * hidden, dtype, m2.amax, s), "kernel2 amax");
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
+                         nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, s), "norm quantise");
+  TE_HIP(te::launch_quantize_transpose(kernel1, hidden, nb1, dtype, w.w1t, m1.amax, m1.scale, m1.scale_inv, s),
+         "kernel1 quantise");
+  TE_HIP(te::launch_quantize_transpose(kernel2, ffn, hidden, dtype, w.w2t, m2.amax, m2.scale, m2.scale_inv, s),
+         "kernel2 quantise");
+  te::Epilogue e1{bias1, nullptr, h1, ma.amax, k, gated};
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.w1t, rows, nb1, hidden, mx.amax, m1.amax, e1, s),
+         "fp8 gemm1");
+  TE_HIP(te::launch_act(h1, rows, ffn, TE_BF16, k, gated, 2, w.act, TE_E4M3, ma.amax, ma.scale, ma.scale_inv, s),
+         "act quantise");
+  te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.act), w.w2t, rows, hidden, ffn, ma.amax, m2.amax, e2, s),
+         "fp8 gemm2");
+  return ok();
+}
+
+}  // extern "C"

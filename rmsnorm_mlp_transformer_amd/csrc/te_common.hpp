@@ -1,0 +1,130 @@
+// Device helpers shared by the gfx950 kernels: element conversions, the
+// E4M3 encoder, the activation functions and wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "te_kernels.hpp"
+
+namespace te {
+
+// ---------------------------------------------------------------- vector types
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 has a hardware convert for this).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// OCP E4M3 encoder: saturate to +-448, then round to nearest even on the
+// E4M3 grid. Subnormals (|v| < 2^-6) sit on the grid k * 2^-9; normals keep 3
+// mantissa bits. Written with integer operations so that the rounding is
+// exactly the format's definition.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fminf(__uint_as_float(u & 0x7FFFFFFFu), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // a * 512 is exact; rint rounds half to even -> 0..8 (8 is the first normal, code 0x08)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);          // round the 23-bit mantissa to 3 bits, ties to even
+    code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);   // exponent bias 127 -> 7
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+  float mag = e == 0 ? (float)m * 0.001953125f
+                     : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Current scaling from a (non-negative) amax: scale = 448 / amax, or 1.
+__device__ __forceinline__ float fp8_scale_from_amax(float amax) {
+  return amax > 0.0f ? 448.0f / amax : 1.0f;
+}
+
+// ---------------------------------------------------------------- activations
+constexpr float kGeluK0 = 0.7978845608028654f;   // sqrt(2/pi)
+constexpr float kGeluK1 = 0.044715f;
+constexpr float kInvSqrt2 = 0.70710678118654752f;
+constexpr float kInvSqrt2Pi = 0.39894228040143268f;
+
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// tanh(u) = 1 - 2 / (1 + e^(2u)); saturates cleanly to +-1 for large |u|.
+__device__ __forceinline__ float tanh_fast(float u) {
+  return 1.0f - 2.0f * fast_rcp(1.0f + __expf(2.0f * u));
+}
+
+template <int A>
+__device__ __forceinline__ float act_fwd(float x) {
+  if constexpr (A == kRelu) {
+    return x > 0.0f ? x : 0.0f;
+  } else if constexpr (A == kGelu) {
+    const float u = kGeluK0 * (x + kGeluK1 * x * x * x);
+    return 0.5f * x * (1.0f + tanh_fast(u));
+  } else if constexpr (A == kGeluErf) {
+    return 0.5f * x * (1.0f + erff(x * kInvSqrt2));
+  } else if constexpr (A == kSilu) {
+    return x * fast_rcp(1.0f + __expf(-x));
+  } else {
+    return x;
+  }
+}
+
+template <int A>
+__device__ __forceinline__ float act_bwd(float x) {
+  if constexpr (A == kRelu) {
+    return x > 0.0f ? 1.0f : 0.0f;
+  } else if constexpr (A == kGelu) {
+    const float x2 = x * x;
+    const float t = tanh_fast(kGeluK0 * (x + kGeluK1 * x2 * x));
+    return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * kGeluK0 * (1.0f + 3.0f * kGeluK1 * x2);
+  } else if constexpr (A == kGeluErf) {
+    return 0.5f * (1.0f + erff(x * kInvSqrt2)) + x * __expf(-0.5f * x * x) * kInvSqrt2Pi;
+  } else if constexpr (A == kSilu) {
+    const float s = fast_rcp(1.0f + __expf(-x));
+    return s * (1.0f + x * (1.0f - s));
+  } else {
+    return 1.0f;
+  }
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// amax accumulator: non-negative floats order like their bit patterns.
+__device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace te

@@ -1,0 +1,100 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Every launcher assumes its arguments were validated by the C ABI layer and
+// returns the HIP error of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace te {
+
+// Element types as in te_dtype.
+enum { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+
+// Activation kinds (kernel template parameters).
+enum ActKind { kRelu = 0, kGelu = 1, kGeluErf = 2, kSilu = 3, kLinear = 4 };
+
+// Brackets one kernel launch with HIP events when per-kernel timing is on.
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  int slot;
+  hipStream_t stream;
+};
+
+// ---------------------------------------------------------------- norm
+enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
+// kNormStore: y (F32/BF16) and optional mu/rsigma.
+// kNormAmax : no y; amax of the normalised tensor into *amax (must start at 0),
+//             optional mu/rsigma.
+// kNormQuant: y = E4M3 codes with scale from *amax; writes scale/scale_inv.
+hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
+                       int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
+                       int y_dtype, void* y, float* mu, float* rsigma, float* amax,
+                       float* scale_out, float* scale_inv_out, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+hipError_t launch_fill_zero(float* p, int n, hipStream_t s);
+// Zero nbytes (a multiple of 4) at p.
+hipError_t launch_fill_zero_bytes(void* p, int64_t nbytes, hipStream_t s);
+// amax = 0, scale = 1, scale_inv = 1 (metadata of an empty tensor).
+hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStream_t s);
+
+// amax of |x| over n elements into *amax (atomic max, *amax must start at 0).
+hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s);
+
+// codes[i] = E4M3(x[i] * scale), scale from *amax; writes scale/scale_inv.
+hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes,
+                           const float* amax, float* scale_out, float* scale_inv_out,
+                           hipStream_t s);
+
+// Quantise a [rows, cols] matrix and store it transposed as [cols, rows]
+// codes (K-contiguous operand layout for the fp8 GEMM).
+hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
+                                     uint8_t* codes_t, const float* amax, float* scale_out,
+                                     float* scale_inv_out, hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale_inv, void* y,
+                             int y_dtype, hipStream_t s);
+
+// Activation forward: x [rows, G*cols] -> y [rows, cols].
+// mode 0: store y (F32/BF16); 1: amax only; 2: E4M3 codes using *amax.
+hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, int act,
+                      bool gated, int mode, void* y, int y_dtype, float* amax,
+                      float* scale_out, float* scale_inv_out, hipStream_t s);
+
+// dact + dbias. partials: fp32 workspace of dact_partials_floats() floats.
+int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated);
+hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,
+                             int dtype, int act, bool gated, void* dx, void* dbias,
+                             int dbias_dtype, float* partials, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMMs
+// Epilogue applied to h = acc * scale + bias (scale = 1 unless fp8):
+//   out   : act(h) (or act(h_a) * h_b when gated), NULL to skip
+//   h_out : h rounded to the element type, NULL to skip
+//   amax  : atomic max of |act(h_rounded)|, NULL to skip (fp8 forward)
+struct Epilogue {
+  const void* bias;       // [n_b] of the GEMM's element type, or NULL
+  void* out;              // [M, n_out]
+  void* h_out;            // [M, n_b]
+  float* amax;
+  int act;                // ActKind
+  bool gated;
+};
+
+// bf16: C[M, n_out] from A [M, K] (row-major) and B [K, n_b] (row-major).
+hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
+                            const Epilogue& ep, hipStream_t s);
+
+// fp8: A codes [M, K] and B^T codes [n_b, K] (both K-contiguous); the
+// accumulator is multiplied by scale_inv(amax_a) * scale_inv(amax_b).
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b,
+                           int64_t K, const float* amax_a, const float* amax_b,
+                           const Epilogue& ep, hipStream_t s);
+
+// fp32: all operands fp32.
+hipError_t launch_gemm_f32(const float* A, const float* B, int64_t M, int64_t n_b, int64_t K,
+                           const Epilogue& ep, hipStream_t s);
+
+}  // namespace te

@@ -1,0 +1,185 @@
+"""GPU parity of the HBM-bound kernels against the fp64 oracle: the row norm
+(fp32 / bf16 / E4M3 output), the quantiser, act_lu and dact + dbias."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rmsnorm_mlp_transformer_amd as te
+import workloads as W
+from gpu_util import TOL, assert_rel, check_codes, codes_np, dev, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _norm_inputs(rows, hidden, dtype, zcg, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    dt = W.TORCH_DTYPE[dtype]
+    x = (torch.randn(rows, hidden, generator=g) * 1.7 + 0.3).to(dt)
+    gamma = (torch.randn(hidden, generator=g) * 0.1 + (0.0 if zcg else 1.0)).to(dt)
+    beta = (torch.randn(hidden, generator=g) * 0.1).to(dt)
+    return x, gamma, beta
+
+
+NORM_SHAPES = [(1, 16), (37, 128), (64, 4096), (5, 4112), (130, 768), (3, 8192 + 512)]
+
+
+@pytest.mark.parametrize("rows,hidden", NORM_SHAPES)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("zcg", [False, True])
+def test_norm_matches_oracle(rows, hidden, dtype, norm, zcg):
+    print(f"norm {norm} {dtype} zcg={zcg} {rows}x{hidden}", flush=True)
+    x, gamma, beta = _norm_inputs(rows, hidden, dtype, zcg)
+    xd, gd, bd = x.to(dev()), gamma.to(dev()), beta.to(dev())
+    y, mu, rs = te.layernorm(xd, gd, bd if norm == "layernorm" else None, norm, zcg, 1e-5,
+                             out_dtype=torch.float32, return_stats=True)
+    yb = te.layernorm(xd, gd, bd, norm, zcg, 1e-5)
+    torch.cuda.synchronize()
+    ry, rmu, rrs = O.normalize(f64(x), f64(gamma), f64(beta), norm, 1e-5, zcg)
+    assert_rel(f64(y), ry, TOL["fp32"], "y fp32")
+    assert_rel(f64(yb), ry, TOL["bf16"] if dtype == "bf16" else TOL["fp32"], "y")
+    assert_rel(f64(rs), rrs, 1e-5, "rsigma")
+    if norm == "layernorm":
+        scale = np.abs(f64(x)).mean()
+        assert np.max(np.abs(f64(mu) - rmu)) <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("rows,hidden", [(37, 128), (64, 4096), (5, 4112)])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_norm_e4m3_output(rows, hidden, norm):
+    print(f"norm e4m3 {norm} {rows}x{hidden}", flush=True)
+    x, gamma, beta = _norm_inputs(rows, hidden, "bf16", False, seed=3)
+    q = te.Fp8Meta()
+    codes = te.layernorm(x.to(dev()), gamma.to(dev()), beta.to(dev()), norm, False, 1e-6, quantizer=q)
+    codes2 = te.layernorm(x.to(dev()), gamma.to(dev()), beta.to(dev()), norm, False, 1e-6, quantizer=q)
+    torch.cuda.synchronize()
+    ry, _, _ = O.normalize(f64(x), f64(gamma), f64(beta), norm, 1e-6, False)
+    rq, rm = O.quantize(ry)
+    m = q.values()
+    assert abs(m["amax"] - rm["amax"]) <= 1e-5 * rm["amax"]
+    # scale / scale_inv follow from the GPU's own amax exactly
+    assert m["scale"] == float(np.float32(448.0) / np.float32(m["amax"]))
+    assert m["scale_inv"] == float(np.float32(1.0) / np.float32(m["scale"]))
+    check_codes(codes_np(codes), rq, "xq")
+    assert torch.equal(codes, codes2)
+
+
+def test_quantize_codec_exhaustive():
+    """Every E4M3 value, every midpoint between neighbours (ties), one fp32
+    ulp either side of each midpoint, saturation beyond 448, subnormals and
+    signed zeros; amax is 448 so the scale is exactly 1 and the GPU codes must
+    equal the oracle's codec bit for bit."""
+    pos = O.e4m3_decode(np.arange(0, 0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    m32 = mids.astype(np.float32)
+    vals = np.concatenate([pos, mids, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9)),
+                           [448.0, 460.0, 464.0, 500.0, 1e-9, 2.0 ** -10, 3 * 2.0 ** -11, 0.0]])
+    vals = np.concatenate([vals, -vals])
+    vals = np.concatenate([vals, np.zeros((-len(vals)) % 16)])
+    # keep amax at exactly 448
+    vals = np.clip(vals, -448.0, 448.0)
+    vals[-1] = 448.0
+    x = torch.from_numpy(vals.astype(np.float32))
+    q = te.Fp8Meta()
+    codes = te.quantize(x.to(dev()), q)
+    deq = te.dequantize(codes, q, torch.float32)
+    torch.cuda.synchronize()
+    assert q.values()["scale"] == 1.0
+    ref = O.e4m3_encode(O.fl32(vals))
+    got = codes_np(codes)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(vals[i], hex(got[i]), hex(ref[i])) for i in bad[:10]]
+    assert np.array_equal(f64(deq), O.e4m3_decode(ref))
+
+
+@pytest.mark.parametrize("n,dtype,std", [(16, "fp32", 1.0), (4096, "bf16", 0.02), (1 << 20, "bf16", 3.0),
+                                         (123456 * 16, "fp32", 1e-3)])
+def test_quantize_current_scaling_bit_exact(n, dtype, std):
+    print(f"quantize {dtype} n={n}", flush=True)
+    g = torch.Generator().manual_seed(n)
+    x = (torch.randn(n, generator=g) * std).to(W.TORCH_DTYPE[dtype])
+    q = te.Fp8Meta()
+    codes = te.quantize(x.to(dev()), q)
+    deq = te.dequantize(codes, q, torch.float32)
+    torch.cuda.synchronize()
+    rq, rm = O.quantize(f64(x))
+    m = q.values()
+    assert m == {k: float(v) for k, v in rm.items()}
+    assert np.array_equal(codes_np(codes), rq)
+    assert np.array_equal(f64(deq), O.fl32(O.dequantize(rq, rm)))
+
+
+def test_quantize_all_zero_tensor():
+    q = te.Fp8Meta()
+    codes = te.quantize(torch.zeros(64, device=dev()), q)
+    torch.cuda.synchronize()
+    assert q.values() == {"amax": 0.0, "scale": 1.0, "scale_inv": 1.0}
+    assert int(codes.sum()) == 0
+
+
+ACTS = [("relu",), ("gelu",), ("gelu_erf",), ("silu",), ("linear",),
+        ("relu", "linear"), ("gelu", "linear"), ("silu", "linear")]
+
+
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (33, 272), (256, 1024)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_act_lu_matches_oracle(act, rows, cols, dtype):
+    print(f"act_lu {act} {dtype} {rows}x{cols}", flush=True)
+    a = W.make_act_inputs(rows, cols, len(act) == 2, dtype, seed=rows)
+    y = te.activation(a["x"].to(dev()), act)
+    torch.cuda.synchronize()
+    ref = O.activation(f64(a["x"]), act)
+    assert_rel(f64(y), ref, TOL[dtype], f"act {act}")
+
+
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("rows,cols", [(33, 272), (512, 1024)])
+def test_act_lu_e4m3(act, rows, cols):
+    print(f"act_lu e4m3 {act} {rows}x{cols}", flush=True)
+    a = W.make_act_inputs(rows, cols, len(act) == 2, "bf16", seed=7)
+    q = te.Fp8Meta()
+    codes = te.activation_codes(a["x"].to(dev()), act, q)
+    deq = te.activation(a["x"].to(dev()), act, quantizer=q)
+    torch.cuda.synchronize()
+    ref_act = O.activation(f64(a["x"]), act)
+    rq, rm = O.quantize(ref_act)
+    m = q.values()
+    assert abs(m["amax"] - rm["amax"]) <= 1e-5 * rm["amax"]
+    check_codes(codes_np(codes), rq, "act codes")
+    assert_rel(f64(deq), ref_act, TOL["fp8"], "dequantised act")
+
+
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (37, 272), (1000, 1536)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dact_dbias_matches_oracle(act, rows, cols, dtype):
+    print(f"dact_dbias {act} {dtype} {rows}x{cols}", flush=True)
+    a = W.make_act_inputs(rows, cols, len(act) == 2, dtype, seed=cols)
+    g, x = a["grad"].to(dev()), a["x"].to(dev())
+    dx, db = te.dact_dbias(g, x, act)
+    dx2, db2 = te.dact_dbias(g, x, act)
+    dxn, none = te.dact_dbias(g, x, act, with_dbias=False)
+    dbb = te.dact_dbias(g, x, act, dbias_dtype=torch.bfloat16)[1]
+    torch.cuda.synchronize()
+    rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), act)
+    assert_rel(f64(dx), rdx, TOL[dtype], "dx")
+    assert_rel(f64(db), rdb, 1e-5, "dbias fp32")
+    assert_rel(f64(dbb), rdb, TOL["bf16"], "dbias bf16")
+    assert none is None and torch.equal(dxn, dx)
+    assert torch.equal(dx, dx2) and torch.equal(db, db2), "not bitwise reproducible"
+
+
+def test_empty_rows_is_a_no_op():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev())
+    y = te.activation(x, ("gelu",))
+    dx, db = te.dact_dbias(torch.empty(0, 32, dtype=torch.bfloat16, device=dev()), x, ("silu", "linear"))
+    q = te.Fp8Meta()
+    q.buf.fill_(7.0)
+    codes = te.activation_codes(x, ("gelu",), q)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64) and dx.shape == (0, 64) and codes.shape == (0, 64)
+    assert db.shape == (64,) and not db.any()
+    assert q.values() == {"amax": 0.0, "scale": 1.0, "scale_inv": 1.0}
