@@ -1,0 +1,51 @@
+// gfx950 memory primitives shared by the MFMA GEMMs: buffer resources with
+// hardware range checking, direct global->LDS loads and the transposing LDS
+// read.
+//
+// buffer_load ... lds: each lane of the wave fetches 16 bytes at
+// base + voffset + soffset and the wave writes them to LDS at
+// M0 + 16 * lane, i.e. one instruction fills 1 KiB of LDS in lane order.
+// Offsets at or beyond the resource's num_records read as zero, which the
+// GEMMs use for ragged tiles instead of branches.
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, the four 8-byte chunks
+// addressed by lanes 4i .. 4i+3 form row i (16 consecutive 16-bit values)
+// and lane j of the group receives element j of rows 0..3. With row i = B[k+i]
+// [n .. n+15] this hands lane j the four consecutive k values of column n+j,
+// the layout the MFMA wants for its B operand.
+#pragma once
+
+#include "te_common.hpp"
+
+namespace te {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on the gfx9 family.
+constexpr int kBufferWord3 = 0x00020000;
+// A byte offset that is always beyond num_records: the load returns zeros.
+constexpr uint32_t kOffNone = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// 16 bytes per lane from the buffer into LDS at lds (wave-uniform) + 16 * lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ i16x4_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+}
+
+// Wait until every outstanding global/buffer load (including LDS-DMA) of the
+// wave has landed, then synchronise the workgroup.
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+}  // namespace te

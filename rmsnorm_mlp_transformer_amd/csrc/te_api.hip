@@ -183,7 +183,7 @@ te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t
   TE_ARG(feature_ok(hidden), "hidden must be a positive multiple of 16, got %lld", (long long)hidden);
   TE_ARG(nt == TE_LAYERNORM || nt == TE_RMSNORM, "invalid norm_type %d", (int)nt);
   TE_ARG(eps >= 0.0f && eps < 1e30f, "epsilon must be finite and >= 0");
-  TE_ARG(x != nullptr && gamma != nullptr, "x and gamma are required");
+  TE_ARG(gamma != nullptr && (x != nullptr || rows == 0), "x and gamma are required");
   TE_ARG(nt == TE_RMSNORM || beta != nullptr, "beta is required for layernorm");
   TE_ARG(aligned16(x) && aligned16(gamma) && (beta == nullptr || aligned16(beta)),
          "x, gamma and beta must be 16-byte aligned");
@@ -262,7 +262,7 @@ te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta, i
   if (st != TE_SUCCESS) return st;
   TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
   TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype");
-  TE_ARG(y != nullptr && aligned16(y), "y is required and must be 16-byte aligned");
+  TE_ARG((y != nullptr || rows == 0) && aligned16(y), "y is required and must be 16-byte aligned");
   TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
   hipStream_t s = as_stream(stream);
   if (rows == 0) {
@@ -295,7 +295,8 @@ te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype,
   TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
   TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
   TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype");
-  TE_ARG(x != nullptr && y != nullptr && aligned16(x) && aligned16(y), "x and y are required, 16-byte aligned");
+  TE_ARG(((x != nullptr && y != nullptr) || rows == 0) && aligned16(x) && aligned16(y),
+         "x and y are required, 16-byte aligned");
   TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
   hipStream_t s = as_stream(stream);
   if (rows == 0) {
@@ -333,7 +334,7 @@ te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t c
   TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
   TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
   TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
-  TE_ARG(grad != nullptr && x != nullptr && dx != nullptr, "grad, x and dx are required");
+  TE_ARG((grad != nullptr && x != nullptr && dx != nullptr) || rows == 0, "grad, x and dx are required");
   TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
          "pointers must be 16-byte aligned");
   const size_t need = te_dact_dbias_workspace_size(rows, cols, act_type);
@@ -399,7 +400,8 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
   TE_ARG(feature_ok(out_features), "out_features must be a positive multiple of 16");
-  TE_ARG(kernel != nullptr && y != nullptr && aligned16(kernel) && aligned16(y), "kernel and y are required, 16-byte aligned");
+  TE_ARG(kernel != nullptr && (y != nullptr || rows == 0) && aligned16(kernel) && aligned16(y),
+         "kernel and y are required, 16-byte aligned");
   TE_ARG(bias == nullptr || aligned16(bias), "bias must be 16-byte aligned");
   const size_t need = te_layernorm_dense_fwd_workspace_size(rows, hidden, out_features, dtype, quant);
   TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
@@ -457,7 +459,8 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
   if (st != TE_SUCCESS) return st;
   TE_ARG(feature_ok(ffn), "ffn must be a positive multiple of 16, got %lld", (long long)ffn);
   TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
-  TE_ARG(kernel1 != nullptr && kernel2 != nullptr && y != nullptr, "kernel1, kernel2 and y are required");
+  TE_ARG(kernel1 != nullptr && kernel2 != nullptr && (y != nullptr || rows == 0),
+         "kernel1, kernel2 and y are required");
   TE_ARG(aligned16(kernel1) && aligned16(kernel2) && aligned16(y) && (bias1 == nullptr || aligned16(bias1)) &&
              (bias2 == nullptr || aligned16(bias2)),
          "tensors must be 16-byte aligned");

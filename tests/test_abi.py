@@ -93,7 +93,10 @@ def test_mlp_rmsnorm_accepts_null_beta_and_zero_rows_is_a_no_op():
     # rows = 0 succeeds without any HIP call (so it succeeds without a GPU)
     assert _mlp(rows=0) == B.TE_SUCCESS
     assert _mlp(rows=0, beta=None, norm=B.TE_RMSNORM) == B.TE_SUCCESS
+    # an empty batch may come with NULL x / y (an empty tensor's data pointer)
+    assert _mlp(rows=0, x=None, y=None) == B.TE_SUCCESS
     assert te.te_last_error() == ""
+    assert _mlp(rows=1, x=None) == B.TE_ERR_INVALID_ARGUMENT
 
 
 @no_gpu
