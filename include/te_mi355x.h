@@ -21,7 +21,9 @@
  *    calling thread is available from te_last_error(). Launch failures map to
  *    TE_ERR_HIP; faults inside kernels surface at the caller's synchronise.
  *  - Feature sizes (hidden, ffn, cols, out_features) must be positive
- *    multiples of 16; rows may be 0: then no tensor element is written,
+ *    multiples of 16 and at most 2^22, and each weight matrix must be
+ *    smaller than 2 GiB (TE_ERR_UNSUPPORTED otherwise); rows may be 0: then
+ *    no tensor element is written,
  *    except that te_dact_dbias sets dbias to zero and the single-tensor
  *    calls with E4M3 output (te_layernorm_fwd, te_act_lu) set their meta to
  *    amax 0, scale 1, scale_inv 1.

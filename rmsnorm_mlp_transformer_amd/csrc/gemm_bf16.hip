@@ -4,27 +4,22 @@
 // and the dense layer of "... LayerNorm Dense" (Outputs: x @ kernel + bias).
 //
 // A is [M, K] row-major (K contiguous); B is the page's kernel layout
-// [K, N] row-major (N contiguous). Both tiles of a 64-deep k stage move from
+// [K, N] row-major (N contiguous). Both tiles of a BK-deep k stage move from
 // memory to LDS with buffer_load ... lds (no register staging): the A tile
-// as 256 rows of 128 bytes, the B tile as 64 k-rows of 512 bytes, each with
+// as 256 rows of 2 BK bytes, the B tile as BK k-rows of 512 bytes, each with
 // its 16-byte chunks XOR-swizzled per row so that the reads below hit
 // distinct banks. The MFMA (v_mfma_f32_32x32x16_bf16) wants 8 consecutive k
 // per lane for both operands: A fragments are plain ds_read_b128 of a row,
 // B fragments are two ds_read_b64_tr_b16 (4 k each) that transpose the
-// N-contiguous tile on the way out of LDS. Two LDS stages (128 KiB): the
-// loads of stage k+1 are in flight while the MFMAs of stage k run; one
-// barrier per stage.
+// N-contiguous tile on the way out of LDS. STAGES LDS stages (128 KiB in
+// all): the loads of the next STAGES - 1 stages are in flight while the
+// MFMAs of the current one run; one barrier per stage.
 #include "gemm_common.hpp"
 #include "gemm_lds.hpp"
 #include "te_kernels.hpp"
 
 namespace te {
 namespace {
-
-constexpr int BK = 64;                          // k per stage
-constexpr int A_BYTES = kTileM * BK * 2;        // 256 rows x 128 B
-constexpr int B_BYTES = BK * kTileN * 2;        // 64 k-rows x 512 B
-constexpr int STAGE = A_BYTES + B_BYTES;        // 64 KiB
 
 struct GemmArgs {
   const uint16_t* A;
@@ -33,15 +28,41 @@ struct GemmArgs {
   EpiArgs ep;
 };
 
-// A row r keeps its 8 chunks (8 k each) at slots c ^ swz_a(r).
-__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
-// B k-row kr keeps its 32 chunks (8 n each) at slots q ^ swz_b(kr).
-__device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 1; }
+// Tile sizes of one pipeline stage of depth BK: A is 256 rows of BK bf16
+// (CPR 16-byte chunks per row), B is BK k-rows of 256 bf16 (32 chunks per row).
+template <int BK>
+struct Stage {
+  static constexpr int CPR = BK / 8;
+  static constexpr int A_BYTES = kTileM * BK * 2;
+  static constexpr int B_BYTES = BK * kTileN * 2;
+  static constexpr int BYTES = A_BYTES + B_BYTES;
+};
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
-__global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// B k-row kr keeps its 32 chunks (8 n each) at slots q ^ swz_b(kr). A
+// ds_read_b64_tr_b16 served 32 lanes at a time reads 4 consecutive k-rows x
+// 4 chunks; XOR with 4 (kr & 3) puts the four rows' chunks in four disjoint
+// quarters of the 64 banks.
+__device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
+
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES>
+__global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
+  using St = Stage<BK>;
+  constexpr int NJ = 16 / WAVES;                      // 32-column blocks per wave
+  constexpr int RA = kTileM / WAVES;                  // A rows loaded per wave
+  constexpr int LA = RA * St::CPR * 16 / 1024;        // 1 KiB A loads per wave and stage
+  constexpr int RB = BK / WAVES;                      // B k-rows loaded per wave
+  constexpr int LB = RB / 2;                          // 1 KiB B loads per wave and stage
+  static_assert(LA >= 1 && LB >= 1, "tile too small for the wave count");
+  // one array per stage: distinct objects let the compiler see that the LDS-DMA
+  // of a later stage cannot alias the reads of the current one (no vmcnt wait)
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[St::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGES > 2 ? St::BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[STAGES > 3 ? St::BYTES : 16];
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+  auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? sm0 : s == 1 ? sm1 : s == 2 ? sm2 : sm3; };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int wm = wave & 1, wn = wave >> 1;
   const int M = a.ep.M, K = a.K, NB = a.ep.n_b, F = a.ep.F;
   const int tiles_m = (M + kTileM - 1) / kTileM;
@@ -51,23 +72,24 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmArgs a) {
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
 
-  // ---- loaders: wave w fills A rows [64w, 64w + 64) and B k-rows [16w, 16w + 16),
-  // 1 KiB (8 A rows / 2 B rows) per instruction j
+  // ---- loaders: wave w fills A rows [w RA, (w + 1) RA) and B k-rows [w RB, (w + 1) RB)
   const int rows_a = min(M - m0, kTileM);
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K * 2);
-  uint32_t off_a[8];
-  int kc_a[8];
+  uint32_t off_a[LA];
+  int kc_a[LA];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + j * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_a(r);
+  for (int j = 0; j < LA; ++j) {
+    const int r = wave * RA + j * (64 / St::CPR) + lane / St::CPR;
+    const int c = (lane % St::CPR) ^ chunk_swizzle<St::CPR>(r);
     off_a[j] = (uint32_t)r * K * 2 + c * 16;
     kc_a[j] = c * 8;
   }
-  uint32_t off_b[8];
+  // the whole B operand (K * NB * 2 < 2^31 bytes, checked by the launcher)
+  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.B, (uint32_t)K * NB * 2);
+  uint32_t off_b[LB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int kr = wave * 16 + j * 2 + (lane >> 5);
+  for (int j = 0; j < LB; ++j) {
+    const int kr = wave * RB + j * 2 + (lane >> 5);
     const int q = (lane & 31) ^ swz_b(kr);
     int n;
     if constexpr (GATED) n = q < 16 ? n0 + 8 * q : F + n0 + 8 * (q - 16);
@@ -76,83 +98,133 @@ __global__ void __launch_bounds__(256, 1) gemm_bf16_kernel(GemmArgs a) {
   }
   auto issue_stage = [&](int kt, int s) {
     const int k0 = kt * BK;
-    uint8_t* As = smem + s * STAGE;
-    uint8_t* Bs = As + A_BYTES;
+    uint8_t* As = stage_ptr(s);
+    uint8_t* Bs = As + St::A_BYTES;
     const bool tail = k0 + BK > K;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < LA; ++j) {
       const uint32_t v = (tail && k0 + kc_a[j] >= K) ? kOffNone : off_a[j];
-      load_lds16(rsrc_a, As + wave * 8192 + j * 1024, v, (uint32_t)k0 * 2);
+      load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * 2);
     }
-    const int krows = min(K - k0, BK);
-    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.B + (int64_t)k0 * NB, (uint32_t)krows * NB * 2);
+    // rows at or past K (including whole stages past the end) read as zero
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load_lds16(rsrc_b, Bs + wave * 8192 + j * 1024, off_b[j], 0);
+    for (int j = 0; j < LB; ++j)
+      load_lds16(rsrc_b, Bs + wave * RB * 512 + j * 1024, off_b[j], (uint32_t)k0 * NB * 2);
   };
 
   // ---- fragment addresses (byte offsets inside a stage)
   const int lr = lane & 31, lh = lane >> 5;
-  int a_off[4];
+  int a_off[BK / 16];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    a_off[kk] = (wm * 128 + lr) * 128 + 16 * ((2 * kk + lh) ^ swz_a(lr));
+  for (int kk = 0; kk < BK / 16; ++kk)
+    a_off[kk] = (wm * 128 + lr) * BK * 2 + 16 * ((2 * kk + lh) ^ chunk_swizzle<St::CPR>(lr));
   const int g = lane >> 4, i4 = (lane >> 2) & 3, c4 = lane & 3;
-  int b_off[4];
+  int b_off[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n_local = b_block_row<GATED>(wn, j) + 16 * (g & 1) + 4 * c4;
-    b_off[j] = A_BYTES + (8 * (g >> 1) + i4) * 512 + 16 * ((n_local >> 3) ^ (2 * i4)) + 8 * (c4 & 1);
+  for (int j = 0; j < NJ; ++j) {
+    const int n_local = b_block_row<GATED, NJ>(wn, j) + 16 * (g & 1) + 4 * c4;
+    b_off[j] = St::A_BYTES + (8 * (g >> 1) + i4) * 512 + 16 * ((n_local >> 3) ^ swz_b(i4)) + 8 * (c4 & 1);
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (K + BK - 1) / BK;
-  issue_stage(0, 0);
-  wait_loads_and_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) issue_stage(kt + 1, cur ^ 1);
-    const uint8_t* S = smem + cur * STAGE;
+  // ---- one k-substep: fragment reads and the MFMAs that consume them
+  constexpr int KS = BK / 16;                         // substeps per stage
+  static_assert(KS == 2, "the step schedule below splits a stage into two substeps");
+  struct Frags {
+    bf16x8_t a[4];
+    bf16x8_t b[NJ];
+  };
+  auto read_frags = [&](int s, int kk, Frags& f) {
+    const uint8_t* S = stage_ptr(s);
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t af[4], bfr[4];
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[kk] + i * 32 * BK * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[kk] + i * 32 * 128);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const i16x4_t lo = lds_read_tr16(S + b_off[j] + (16 * kk) * 512);
-        const i16x4_t hi = lds_read_tr16(S + b_off[j] + (16 * kk + 4) * 512);
-        bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < NJ; ++j) {
+      const i16x4_t lo = lds_read_tr16(S + b_off[j] + (16 * kk) * 512);
+      const i16x4_t hi = lds_read_tr16(S + b_off[j] + (16 * kk + 4) * 512);
+      f.b[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    wait_loads_and_barrier();
-  }
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+  // interleave one fragment read after each MFMA (4 A + 2 NJ B reads, 4 NJ MFMAs)
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4 + 2 * NJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+  };
 
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX>(acc, a.ep, m0, n0, wm, wn, lane, 1.0f);
+  // ---- pipeline. Step kt, with stage kt's first-substep fragments in f0:
+  //   MFMAs(f0) || reads of f1 (stage kt, second substep)
+  //   wait: own LDS reads and the DMA of stage kt+1; barrier (all waves)
+  //   DMA of stage kt+3 into the buffer of stage kt-1 (no longer read)
+  //   MFMAs(f1) || reads of f0 for stage kt+1
+  // Every step issues exactly one stage (past K it reads nothing), so the
+  // wait before the barrier always leaves the newest STAGES - 3 stages in flight.
+  static_assert(STAGES == 4, "three stages ahead of the one being consumed");
+  Frags f0, f1;
+  auto step = [&](int kt, int s) {
+    read_frags(s, 1, f1);
+    mfmas(f0);
+    interleave();
+    wait_vmcnt_lgkm0<(STAGES - 3) * (LA + LB)>();
+    block_barrier();
+    issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+    __builtin_amdgcn_sched_group_barrier(0x020, LA + LB, 0);   // the DMA goes out first
+    read_frags((s + 1) % STAGES, 0, f0);
+    mfmas(f1);
+    interleave();
+  };
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+  wait_vmcnt<(STAGES - 2) * (LA + LB)>();
+  block_barrier();
+  read_frags(0, 0, f0);
+  int kb = 0;
+  for (; kb + STAGES <= nk; kb += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) step(kb + s, s);
+  }
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (kb + s < nk) step(kb + s, s);
+  wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0);
+
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ>(acc, a.ep, m0, n0, wm, wn, lane, 1.0f);
 }
+
+constexpr int kWaves = TE_GEMM_WAVES;
+constexpr int kBK = TE_GEMM_BK;
+constexpr int kStages = TE_GEMM_STAGES;
 
 template <int ACT, bool GATED>
 hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
+  constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true><<<grid, 256, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, false, true><<<grid, 256, 0, s>>>(a);
+    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false><<<grid, 256, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, true, false><<<grid, 256, 0, s>>>(a);
+    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_bf16_kernel<ACT, GATED, true, false, false><<<grid, 256, 0, s>>>(a);
+    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 // Tile geometry and the fused epilogue shared by the bf16 and fp8 MFMA GEMMs.
 //
-// Work split: a 256-thread workgroup (4 waves) computes a 256 x 256 tile of
-// h = A * B. Wave w = (wm, wn) = (w % 2, w / 2) owns 128 rows x 128 columns
-// as 4 x 4 blocks of 32 x 32. The GEMMs issue the MFMA with the B fragment as
+// Work split: a workgroup of 2 x WN waves computes a 256 x 256 tile of
+// h = A * B. Wave w = (wm, wn) = (w % 2, w / 2) owns 128 rows x (256 / WN)
+// columns as 4 x NJ blocks of 32 x 32 (NJ = 8 / WN). The GEMMs issue the MFMA with the B fragment as
 // the first operand, so each accumulator block holds the transposed tile:
 // lane l owns row m = 32 i + (l % 32) and, for register group g = 0..3, the
 // four consecutive columns 32 j + 8 g + 4 (l / 32) + {0,1,2,3} in
@@ -12,14 +12,34 @@
 // Gated activations ((f, linear) pairs, "NVIDIA TransformerEngine JAX
 // Activation", Inputs: activation_type ("silu", "linear")): the tile's 256 B
 // columns are the 128 first-half columns [j0, j0 + 128) followed by the
-// matching second-half columns [F + j0, F + j0 + 128); wave wn owns first-half
-// blocks j = 0, 1 at [j0 + 64 wn, +64) and their partners j = 2, 3, so the
-// gate product f(a) * b happens in registers.
+// matching second-half columns [F + j0, F + j0 + 128); wave wn owns the
+// first-half blocks j < NJ / 2 at [j0 + 16 NJ wn, +16 NJ) and their partners
+// j + NJ / 2, so the gate product f(a) * b happens in registers.
 #pragma once
 
 #include "te_common.hpp"
 
 namespace te {
+
+// Waves per GEMM workgroup (4: one per SIMD, 128 x 128 each; 8: two per SIMD,
+// 128 x 64 each).
+#ifndef TE_GEMM_WAVES
+#define TE_GEMM_WAVES 8
+#endif
+// bf16 pipeline: k depth per LDS stage and number of stages (STAGES * BK * 1 KiB of LDS).
+#ifndef TE_GEMM_BK
+#define TE_GEMM_BK 32
+#endif
+#ifndef TE_GEMM_STAGES
+#define TE_GEMM_STAGES 4
+#endif
+// fp8 pipeline: k bytes per LDS stage and number of stages.
+#ifndef TE_GEMM_FP8_BK
+#define TE_GEMM_FP8_BK 64
+#endif
+#ifndef TE_GEMM_FP8_STAGES
+#define TE_GEMM_FP8_STAGES 4
+#endif
 
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
@@ -32,11 +52,15 @@ struct EpiArgs {
   int M, n_b, F;          // F = n_b / 2 when gated, else n_b
 };
 
-// LDS row (0..255) of B-fragment block j for wave column wn.
-template <bool GATED>
+// LDS row (0..255) of B-fragment block j (of NJ) for wave column wn.
+template <bool GATED, int NJ>
 __device__ __forceinline__ int b_block_row(int wn, int j) {
-  if constexpr (GATED) return j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32;
-  else return wn * 128 + j * 32;
+  if constexpr (GATED) {
+    constexpr int H = NJ / 2;
+    return j < H ? wn * 32 * H + j * 32 : 128 + wn * 32 * H + (j - H) * 32;
+  } else {
+    return wn * 32 * NJ + j * 32;
+  }
 }
 
 // Maps the linear workgroup index to a (tile_m, tile_n) pair. Workgroups are
@@ -79,8 +103,8 @@ __device__ __forceinline__ void round_bf16x4(float* v) {
 // h = acc * scale + bias; then the stores / amax selected by the flags.
 // AMAX evaluates the activation from h rounded to bf16, exactly as a later
 // pass reading the stored h would.
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
-__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], const EpiArgs& ep,
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ>
+__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const EpiArgs& ep,
                                               int m0, int n0, int wm, int wn, int lane,
                                               float scale) {
   const int lm = lane & 31, lh = lane >> 5;
@@ -91,10 +115,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], const
     if (m < ep.M) {
       if constexpr (!GATED) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 128 + j * 32 + g * 8 + lh * 4;
+            const int col = n0 + wn * 32 * NJ + j * 32 + g * 8 + lh * 4;
             if (col < ep.n_b) {
               float h[4], b[4];
               load_bias4(ep.bias, col, b);
@@ -115,10 +139,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], const
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ / 2; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 64 + j * 32 + g * 8 + lh * 4;   // first-half column
+            const int col = n0 + wn * 16 * NJ + j * 32 + g * 8 + lh * 4;   // first-half column
             if (col < ep.F) {
               float ha[4], hb[4], ba[4], bb[4];
               load_bias4(ep.bias, col, ba);
@@ -126,7 +150,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][4], const
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 ha[r] = acc[i][j][4 * g + r] * scale + ba[r];
-                hb[r] = acc[i][j + 2][4 * g + r] * scale + bb[r];
+                hb[r] = acc[i][j + NJ / 2][4 * g + r] * scale + bb[r];
               }
               if constexpr (STORE_H) {
                 store_bf16x4(ep.h_out + (int64_t)m * ep.n_b + col, ha);

@@ -5,12 +5,12 @@
 // "... LayerNorm MLP" (Description: the same for GEMM1 and GEMM2).
 //
 // Both operands arrive K-contiguous: A codes [M, K] and B^T codes [n_b, K]
-// (the weight quantiser writes the kernel transposed). A 128-deep k stage of
-// each operand (256 rows x 128 bytes) moves to LDS with buffer_load ... lds,
+// (the weight quantiser writes the kernel transposed). A BK-deep k stage of
+// each operand (256 rows x BK bytes) moves to LDS with buffer_load ... lds,
 // 16-byte chunks XOR-swizzled per row; each lane then reads its 32
 // consecutive k bytes per operand with two ds_read_b128 and issues
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 for both operands, unit block
-// scales). Two LDS stages (128 KiB), one barrier per stage.
+// scales). STAGES LDS stages (128 KiB in all), one barrier per stage.
 //
 // The accumulator is multiplied by scale_inv(A) * scale_inv(B), which the
 // kernel derives from the two amax values exactly as the quantisers did.
@@ -21,10 +21,6 @@
 namespace te {
 namespace {
 
-constexpr int BK = 128;                         // k bytes per stage
-constexpr int OP_BYTES = kTileM * BK;           // 256 rows x 128 B per operand
-constexpr int STAGE = 2 * OP_BYTES;             // 64 KiB
-
 struct GemmArgs {
   const uint8_t* A;
   const uint8_t* Bt;
@@ -34,13 +30,25 @@ struct GemmArgs {
   EpiArgs ep;
 };
 
-// Row r keeps its 8 chunks (16 k each) at slots c ^ swz(r).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
-__global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES>
+__global__ void __launch_bounds__(64 * WAVES, 1) gemm_fp8_kernel(GemmArgs a) {
+  constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
+  constexpr int OP_BYTES = kTileM * BK;         // one operand of one stage
+  constexpr int BYTES = 2 * OP_BYTES;
+  constexpr int NJ = 16 / WAVES;                // 32-column blocks per wave
+  constexpr int RW = kTileM / WAVES;            // tile rows loaded per wave and operand
+  constexpr int LJ = RW * BK / 1024;            // 1 KiB loads per wave, operand and stage
+  constexpr int KS = BK / 64;                   // MFMA k-steps per stage
+  static_assert(LJ >= 1 && KS >= 1, "tile too small for the wave count");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
+  // one array per stage (see the bf16 GEMM): no false LDS-DMA dependencies
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGES > 2 ? BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[STAGES > 3 ? BYTES : 16];
+  auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? sm0 : s == 1 ? sm1 : s == 2 ? sm2 : sm3; };
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int wm = wave & 1, wn = wave >> 1;
   const int M = a.ep.M, K = a.K, NB = a.ep.n_b, F = a.ep.F;
   const int tiles_m = (M + kTileM - 1) / kTileM;
@@ -50,117 +58,139 @@ __global__ void __launch_bounds__(256, 1) gemm_fp8_kernel(GemmArgs a) {
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
 
-  // ---- loaders: wave w fills rows [64w, 64w + 64) of both tiles, 8 rows per instruction
+  // ---- loaders: wave w fills rows [w RW, (w + 1) RW) of both tiles
   const int rows_a = min(M - m0, kTileM);
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K);
   // B^T rows of this tile: [n0, n0 + 256), or for gated the first-half rows
-  // [n0, n0 + 128) (waves 0, 1) and the second-half rows [F + n0, F + n0 + 128) (waves 2, 3)
+  // [n0, n0 + 128) (first half of the waves) and the second-half rows
+  // [F + n0, F + n0 + 128) (second half of the waves)
   int b_row0, b_rows;
   if constexpr (GATED) {
-    b_row0 = (wave < 2 ? 0 : F) + n0;
+    b_row0 = (wave < WAVES / 2 ? 0 : F) + n0;
     b_rows = min(F - n0, 128);
   } else {
     b_row0 = n0;
     b_rows = min(NB - n0, kTileN);
   }
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.Bt + (int64_t)b_row0 * K, (uint32_t)b_rows * K);
-  const int b_first = GATED ? (wave & 1) * 64 : wave * 64;   // first row of this wave inside its part
-  uint32_t off_a[8], off_b[8];
-  int kc[8];
+  const int b_first = GATED ? (wave % (WAVES / 2)) * RW : wave * RW;   // first row inside its part
+  uint32_t off_a[LJ], off_b[LJ];
+  int kc[LJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = wave * 64 + j * 8 + (lane >> 3);            // row inside the LDS tile
-    const int c = (lane & 7) ^ swz(r);
+  for (int j = 0; j < LJ; ++j) {
+    const int r = wave * RW + j * (64 / CPR) + lane / CPR;    // row inside the LDS tile
+    const int c = (lane % CPR) ^ chunk_swizzle<CPR>(r);
     off_a[j] = (uint32_t)r * K + c * 16;
-    off_b[j] = (uint32_t)(b_first + j * 8 + (lane >> 3)) * K + c * 16;
+    off_b[j] = (uint32_t)(b_first + j * (64 / CPR) + lane / CPR) * K + c * 16;
     kc[j] = c * 16;
   }
   auto issue_stage = [&](int kt, int s) {
     const int k0 = kt * BK;
-    uint8_t* As = smem + s * STAGE;
+    uint8_t* As = stage_ptr(s);
     uint8_t* Bs = As + OP_BYTES;
-    const bool tail = k0 + BK > K;
+    // chunks at or past K (including whole stages past the end) read as zero
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool out = tail && k0 + kc[j] >= K;
-      load_lds16(rsrc_a, As + wave * 8192 + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0);
-      load_lds16(rsrc_b, Bs + wave * 8192 + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0);
+    for (int j = 0; j < LJ; ++j) {
+      const bool out = k0 + kc[j] >= K;
+      load_lds16(rsrc_a, As + wave * RW * BK + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0);
+      load_lds16(rsrc_b, Bs + wave * RW * BK + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0);
     }
   };
 
-  // ---- fragment addresses: 32 k bytes = logical chunks 4 kk + 2 h and + 1
+  // ---- fragment addresses: 32 k bytes = logical chunks 4 ks + 2 h and + 1
   const int lr = lane & 31, lh = lane >> 5;
-  int a_lo[2], a_hi[2], b_lo[4][2], b_hi[4][2];
+  int a_lo[KS], a_hi[KS], b_lo[NJ][KS], b_hi[NJ][KS];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    const int c = 4 * kk + 2 * lh;
-    a_lo[kk] = (wm * 128 + lr) * 128 + 16 * (c ^ swz(lr));
-    a_hi[kk] = (wm * 128 + lr) * 128 + 16 * ((c + 1) ^ swz(lr));
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = 4 * ks + 2 * lh;
+    const int sw = chunk_swizzle<CPR>(lr);
+    a_lo[ks] = (wm * 128 + lr) * BK + 16 * (c ^ sw);
+    a_hi[ks] = (wm * 128 + lr) * BK + 16 * ((c + 1) ^ sw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = b_block_row<GATED>(wn, j) + lr;
-      b_lo[j][kk] = OP_BYTES + row * 128 + 16 * (c ^ swz(lr));
-      b_hi[j][kk] = OP_BYTES + row * 128 + 16 * ((c + 1) ^ swz(lr));
+    for (int j = 0; j < NJ; ++j) {
+      const int row = b_block_row<GATED, NJ>(wn, j) + lr;
+      b_lo[j][ks] = OP_BYTES + row * BK + 16 * (c ^ sw);
+      b_hi[j][ks] = OP_BYTES + row * BK + 16 * ((c + 1) ^ sw);
     }
   }
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (K + BK - 1) / BK;
-  issue_stage(0, 0);
-  wait_loads_and_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) issue_stage(kt + 1, cur ^ 1);
-    const uint8_t* S = smem + cur * STAGE;
+  auto compute_stage = [&](int s) {
+    const uint8_t* S = stage_ptr(s);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      i32x8_t af[4], bfr[4];
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x8_t af[4], bfr[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(S + a_lo[kk] + i * 32 * 128);
-        const uint4 hi = *reinterpret_cast<const uint4*>(S + a_hi[kk] + i * 32 * 128);
+        const uint4 lo = *reinterpret_cast<const uint4*>(S + a_lo[ks] + i * 32 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(S + a_hi[ks] + i * 32 * BK);
         af[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(S + b_lo[j][kk]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(S + b_hi[j][kk]);
+      for (int j = 0; j < NJ; ++j) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(S + b_lo[j][ks]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(S + b_hi[j][ks]);
         bfr[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           // cbsz/blgp = 0: both operands E4M3; scales 127 = 2^0 (no block scaling)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0,
                                                                        0, 127, 0, 127);
     }
-    wait_loads_and_barrier();
+  };
+
+  // ---- pipeline (as in the bf16 GEMM): one stage issued per step, the
+  // newest STAGES - 2 stages stay in flight across the barrier
+  auto step = [&](int kt, int s) {
+    wait_vmcnt<(STAGES - 2) * 2 * LJ>();
+    block_barrier();
+    issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+    compute_stage(s);
+  };
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+  int kb = 0;
+  for (; kb + STAGES <= nk; kb += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) step(kb + s, s);
   }
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (kb + s < nk) step(kb + s, s);
+  wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
 
   const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
   const float scale = (1.0f / sa) * (1.0f / sb);
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX>(acc, a.ep, m0, n0, wm, wn, lane, scale);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ>(acc, a.ep, m0, n0, wm, wn, lane, scale);
 }
+
+constexpr int kWaves = TE_GEMM_WAVES;
+constexpr int kBK = TE_GEMM_FP8_BK;
+constexpr int kStages = TE_GEMM_FP8_STAGES;
 
 template <int ACT, bool GATED>
 hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
+  constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_fp8_kernel<ACT, GATED, false, true, true><<<grid, 256, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, false, true><<<grid, 256, 0, s>>>(a);
+    if (h) gemm_fp8_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    else gemm_fp8_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_fp8_kernel<ACT, GATED, true, true, false><<<grid, 256, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, true, false><<<grid, 256, 0, s>>>(a);
+    if (out) gemm_fp8_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    else gemm_fp8_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_fp8_kernel<ACT, GATED, true, false, false><<<grid, 256, 0, s>>>(a);
+    gemm_fp8_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }

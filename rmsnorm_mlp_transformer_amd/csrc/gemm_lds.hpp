@@ -41,11 +41,40 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
 }
 
-// Wait until every outstanding global/buffer load (including LDS-DMA) of the
-// wave has landed, then synchronise the workgroup.
-__device__ __forceinline__ void wait_loads_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+// Wait until at most N vector-memory loads (including LDS-DMA) of the wave
+// are still in flight (gfx9 s_waitcnt encoding: vmcnt split over bits 3:0 and
+// 15:14; expcnt and lgkmcnt left at their maxima so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// As wait_vmcnt<N>(), and also wait for every LDS read of the wave.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// would wait for every outstanding load (vmcnt 0) and drain the LDS-DMA
+// pipeline. LDS-DMA completion is ordered explicitly with wait_vmcnt<N>()
+// before the barrier, and every LDS read of a stage completes before its
+// MFMAs issue; the empty asm statements keep the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Chunk slot swizzle for a tile whose rows hold CPR 16-byte chunks: slot =
+// chunk ^ swz(row). Rows r .. r + 15 read at the same chunk then fall on 16
+// distinct 4-dword bank groups (row stride CPR * 4 dwords, 64 banks).
+template <int CPR>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  return (r / (16 / CPR)) & (CPR - 1);
 }
 
 }  // namespace te

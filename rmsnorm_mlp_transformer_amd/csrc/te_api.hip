@@ -49,8 +49,12 @@ te_status hip_status(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_status(e_, what);       \
   } while (0)
 
+size_t esize(int dt) { return dt == TE_F32 ? 4 : dt == TE_BF16 ? 2 : 1; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool feature_ok(int64_t n) { return n > 0 && n % 16 == 0 && n <= (int64_t)1 << 30; }
+bool feature_ok(int64_t n) { return n > 0 && n % 16 == 0 && n <= (int64_t)1 << 22; }
+// The GEMMs address a weight matrix through one buffer descriptor with 32-bit
+// byte offsets: it must stay below 2 GiB.
+bool weight_ok(int64_t rows, int64_t cols, int dtype) { return rows * cols * (int64_t)esize(dtype) < ((int64_t)1 << 31); }
 bool valid_act(int a) { return a >= TE_ACT_RELU && a <= TE_ACT_SWIGLU; }
 bool is_gated(int a) { return a >= TE_ACT_REGLU; }
 int act_kind(int a) {
@@ -62,7 +66,6 @@ int act_kind(int a) {
     default: return te::kLinear;
   }
 }
-size_t esize(int dt) { return dt == TE_F32 ? 4 : dt == TE_BF16 ? 2 : 1; }
 bool meta_ok(const te_fp8_meta* m) {
   return m != nullptr && m->amax != nullptr && m->scale != nullptr && m->scale_inv != nullptr;
 }
@@ -180,7 +183,7 @@ te_status check_dtype_quant(te_dtype dtype, te_quant quant) {
 te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                      int64_t hidden, te_norm_type nt, float eps) {
   TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows must be in [0, 2^31], got %lld", (long long)rows);
-  TE_ARG(feature_ok(hidden), "hidden must be a positive multiple of 16, got %lld", (long long)hidden);
+  TE_ARG(feature_ok(hidden), "hidden must be a positive multiple of 16 (at most 2^22), got %lld", (long long)hidden);
   TE_ARG(nt == TE_LAYERNORM || nt == TE_RMSNORM, "invalid norm_type %d", (int)nt);
   TE_ARG(eps >= 0.0f && eps < 1e30f, "epsilon must be finite and >= 0");
   TE_ARG(gamma != nullptr && (x != nullptr || rows == 0), "x and gamma are required");
@@ -399,7 +402,8 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   if (st != TE_SUCCESS) return st;
   st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
-  TE_ARG(feature_ok(out_features), "out_features must be a positive multiple of 16");
+  TE_ARG(feature_ok(out_features), "out_features must be a positive multiple of 16 (at most 2^22)");
+  TE_REQUIRE(weight_ok(hidden, out_features, dtype), TE_ERR_UNSUPPORTED, "kernel must be smaller than 2 GiB");
   TE_ARG(kernel != nullptr && (y != nullptr || rows == 0) && aligned16(kernel) && aligned16(y),
          "kernel and y are required, 16-byte aligned");
   TE_ARG(bias == nullptr || aligned16(bias), "bias must be 16-byte aligned");
@@ -457,8 +461,10 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
   if (st != TE_SUCCESS) return st;
   st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
-  TE_ARG(feature_ok(ffn), "ffn must be a positive multiple of 16, got %lld", (long long)ffn);
+  TE_ARG(feature_ok(ffn), "ffn must be a positive multiple of 16 (at most 2^22), got %lld", (long long)ffn);
   TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_REQUIRE(weight_ok(hidden, (is_gated(act_type) ? 2 : 1) * ffn, dtype) && weight_ok(ffn, hidden, dtype),
+             TE_ERR_UNSUPPORTED, "kernels must be smaller than 2 GiB");
   TE_ARG(kernel1 != nullptr && kernel2 != nullptr && (y != nullptr || rows == 0),
          "kernel1, kernel2 and y are required");
   TE_ARG(aligned16(kernel1) && aligned16(kernel2) && aligned16(y) && (bias1 == nullptr || aligned16(bias1)) &&

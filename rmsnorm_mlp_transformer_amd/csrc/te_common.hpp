@@ -67,6 +67,9 @@ __device__ __forceinline__ float fp8_scale_from_amax(float amax) {
 constexpr float kGeluK0 = 0.7978845608028654f;   // sqrt(2/pi)
 constexpr float kGeluK1 = 0.044715f;
 constexpr float kInvSqrt2 = 0.70710678118654752f;
+// -2 K0 log2(e) and -2 K0 K1 log2(e): the exponent of the sigmoid form of GELU
+constexpr float kGeluE0 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+constexpr float kGeluE1 = -2.0f * 0.7978845608028654f * 0.044715f * 1.4426950408889634f;
 constexpr float kInvSqrt2Pi = 0.39894228040143268f;
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -81,8 +84,10 @@ __device__ __forceinline__ float act_fwd(float x) {
   if constexpr (A == kRelu) {
     return x > 0.0f ? x : 0.0f;
   } else if constexpr (A == kGelu) {
-    const float u = kGeluK0 * (x + kGeluK1 * x * x * x);
-    return 0.5f * x * (1.0f + tanh_fast(u));
+    // 0.5 x (1 + tanh(u)) = x * sigmoid(2u) = x / (1 + 2^(-2u log2 e)),
+    // u = K0 (x + K1 x^3): one exp2 and one reciprocal
+    const float t = x * fmaf(kGeluE1, x * x, kGeluE0);
+    return x * fast_rcp(1.0f + __builtin_amdgcn_exp2f(t));
   } else if constexpr (A == kGeluErf) {
     return 0.5f * x * (1.0f + erff(x * kInvSqrt2));
   } else if constexpr (A == kSilu) {
