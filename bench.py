@@ -12,10 +12,18 @@ of its launches on the launch stream (te_timing_enable) during the timed
 region; the dominant kernel's figure is the "roofline" entry. The
 "cpu_baseline" entry times the fp64 oracle on a bounded row sample.
 
+The "traffic" entry is the HBM traffic per launch of the dominant kernel
+measured with rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each in its own
+run, scaled by what the same counters report for a plain device copy of
+known size); it is stored in TRAFFIC below together with a hash of the
+kernel's source files and reported as null once those sources change.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-parts]
                        [--no-cpu-baseline] [--workload NAME]
+       python bench.py --copy-probe MIB      (plain copy, for counter scaling)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +38,27 @@ import torch  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
+CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
+# Source files that define each kernel (for the staleness check of TRAFFIC).
+KERNEL_SOURCES = {
+    "gemm_bf16_act": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
+    "gemm_bf16": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
+    "gemm_bf16_gated": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
+    "gemm_fp8_h_amax": ["gemm_fp8.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
+    "dact_dbias": ["elementwise.hip", "te_common.hpp"],
+}
+# Counter-measured HBM bytes per launch: {(workload, kernel): (bytes, source hash)}.
+TRAFFIC = {}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused LN-MLP fwd TFLOP/s + % of MI355X bf16/fp8 MFMA peak; dact+dbias GB/s"
 
@@ -72,15 +101,14 @@ class Case:
 
 
 class DactCase:
-    """dact + dbias on grad [M, F] and the saved pre-activation h1 [M, F]."""
+    """dact + dbias on grad [M, F] ~ N(0, 1) and a pre-activation h1 [M, F]
+    with the spread of GEMM1's output (N(0, 1.3^2)), both bf16."""
 
     def __init__(self, w: W.Workload, te, dev):
         self.w = w
-        t = W.make_inputs(w)
-        self.grad = t["grad"].to(dev)
-        gen = torch.Generator().manual_seed(1)
-        # h1 of the same shape and a GEMM1-like spread
-        self.h1 = (torch.randn(w.rows, w.ffn, generator=gen) * 1.5).to(torch.bfloat16).to(dev)
+        a = W.make_act_inputs(w.rows, w.ffn, gated=False, dtype="bf16", seed=0, std=1.3)
+        self.grad = a["grad"].to(dev)
+        self.h1 = a["x"].to(dev)
         self.dx = torch.empty_like(self.h1)
         self.dbias = torch.empty(w.ffn, dtype=torch.float32, device=dev)
         act = te.act_type_of(w.activation_type)
@@ -138,7 +166,14 @@ def kernel_work(w: W.Workload, name: str):
     return None
 
 
-def roofline(w, kernels, dtype_key):
+def traffic_of(workload, kernel):
+    rec = TRAFFIC.get((workload, kernel))
+    if rec is None or kernel not in KERNEL_SOURCES or rec[1] != source_hash(kernel):
+        return None
+    return rec[0]
+
+
+def roofline(w, kernels, dtype_key, wname=None):
     if not kernels:
         return None
     name, (cnt, total) = max(kernels.items(), key=lambda kv: kv[1][1])
@@ -156,7 +191,8 @@ def roofline(w, kernels, dtype_key):
         peak = HBM_PEAK_GBS
         u = "GB/s"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": u,
-            "frac": round(achieved / peak, 4), "traffic": None, "avg_ms": round(total / cnt, 4),
+            "frac": round(achieved / peak, 4), "traffic": traffic_of(wname or w.name, name),
+            "work_per_launch": amount, "work_unit": unit, "avg_ms": round(total / cnt, 4),
             "launches": cnt}
 
 
@@ -194,7 +230,18 @@ def main():
     ap.add_argument("--workload", default="ln_mlp_gelu_bf16")
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times)")
     args = ap.parse_args()
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this library has no "
               "multi-GPU path; the value is the single-GPU throughput", file=sys.stderr)
@@ -244,7 +291,8 @@ def main():
                                          "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                                          "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
                                          "roofline": roofline(dw, {k: v for k, v in dk.items()
-                                                                   if k == "dact_dbias"}, "bf16")}
+                                                                   if k == "dact_dbias"}, "bf16",
+                                                              "dact_dbias_gelu_bf16")}
         log(f"bench part dact_dbias: {dms:.4f} ms, {gbs:.0f} GB/s")
         result["parts"] = parts
     if not args.no_cpu_baseline:

@@ -104,6 +104,16 @@ def e4m3_encode(v) -> np.ndarray:
     return code.astype(np.uint8)
 
 
+def e4m3_encode_fp32(v) -> np.ndarray:
+    """e4m3_encode for fp32-representable inputs, via a library routine:
+    saturate to +-448, then torch's round-to-nearest-even float8_e4m3fn cast.
+    Used for large tensors; pinned against e4m3_encode in the tests."""
+    import torch
+    v = np.asarray(v, dtype=np.float32)
+    c = np.clip(v, -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(np.ascontiguousarray(c)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def current_scaling(t) -> Dict[str, float]:
     """Per-tensor current scaling ([ACT] Description: the activation output is
     quantized; [DENSE] Description: the normalized output and the kernel are
@@ -122,7 +132,7 @@ def quantize(t, meta: Optional[Dict[str, float]] = None):
     if meta is None:
         meta = current_scaling(t)
     prod = fl32(fl32(t) * meta["scale"])
-    return e4m3_encode(prod), meta
+    return e4m3_encode_fp32(prod), meta
 
 
 def dequantize(codes, meta) -> np.ndarray:

@@ -87,19 +87,33 @@ __global__ void empty_meta_kernel(float* amax, float* scale, float* scale_inv) {
 }
 
 // ------------------------------------------------------------------ amax
-// n is a multiple of 8 (every tensor size here is a multiple of 16).
+// n is a multiple of 8 (every tensor size here is a multiple of 16). Each
+// lane keeps kUnroll 16-byte loads in flight per iteration.
+constexpr int kUnroll = 8;
+
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) amax_kernel(const void* x, int64_t n8, float* amax) {
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n8; c += stride) {
-    float f[8];
-    load8<BF16>(x, c * 8, f);
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < n8; c0 += stride * kUnroll) {
+    float f[kUnroll][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t c = c0 + u * stride;
+      if (c < n8) {
+        load8<BF16>(x, c * 8, f[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[u][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[u][i]));
   }
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  __shared__ float red[kThreads / 64];
+  block_max_atomic(m, amax, red);
 }
 
 template <bool BF16>
@@ -111,11 +125,20 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64
     *scale_out = scale;
     *scale_inv_out = 1.0f / scale;
   }
+  constexpr int U = 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < n8; c += stride) {
-    float f[8];
-    load8<BF16>(x, c * 8, f);
-    *reinterpret_cast<uint2*>(codes + c * 8) = encode8(f, scale);
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < n8; c0 += stride * U) {
+    float f[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      if (c < n8) load8<BF16>(x, c * 8, f[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * stride;
+      if (c < n8) *reinterpret_cast<uint2*>(codes + c * 8) = encode8(f[u], scale);
+    }
   }
 }
 
@@ -222,8 +245,8 @@ __global__ void __launch_bounds__(kThreads) act_kernel(const void* x, int64_t ro
     }
   }
   if constexpr (MODE == 1) {
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+    __shared__ float red[kThreads / 64];
+    block_max_atomic(m, amax, red);
   }
 }
 
@@ -321,8 +344,10 @@ template <bool BF16>
 hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool gated, int mode,
                         void* y, int y_dtype, float* amax, float* so, float* sio, hipStream_t s) {
   const dim3 grid = act_grid(rows, cols);
+  dim3 grid_amax = grid;                         // amax pass: at most ~1024 workgroups
+  if (grid_amax.x * grid_amax.y > 1024) grid_amax.y = max(1u, 1024u / grid_amax.x);
 #define TE_ACT_CASE(A, G)                                                                         \
-  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
+  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid_amax, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
   else if (mode == 2) act_kernel<BF16, A, G, 2, kE4M3><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
   else if (y_dtype == kBF16) act_kernel<BF16, A, G, 0, kBF16><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
   else act_kernel<BF16, A, G, 0, kF32><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio);
@@ -362,7 +387,7 @@ hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStr
 
 hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s) {
   LaunchScope scope("amax", s);
-  const unsigned grid = grid_for(n / 8, 8);
+  const unsigned grid = min(grid_for(n / 8, kUnroll), 4096u);
   if (x_dtype == kBF16) amax_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
   else amax_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
   return hipGetLastError();

@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ>(acc, a.ep, m0, n0, wm, wn, lane, 1.0f);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, a.ep, m0, n0, wm, wn, lane, tid, 1.0f, stage_ptr);
 }
 
 constexpr int kWaves = TE_GEMM_WAVES;

@@ -100,41 +100,150 @@ __device__ __forceinline__ void round_bf16x4(float* v) {
   for (int r = 0; r < 4; ++r) v[r] = bf16_to_f32(f32_to_bf16(v[r]));
 }
 
-// h = acc * scale + bias; then the stores / amax selected by the flags.
+// The four LDS stage arrays of a GEMM (32 KiB each) are reused after the main
+// loop as a 256 x C bf16 staging tile: rows [64 a, 64 a + 64) live in array a,
+// which the callable st(a) returns.
+
+// Staging layout: row r holds C bf16 as C / 4 units of 8 bytes; unit u sits at
+// u ^ (r % 32). A wave's 8-byte writes (32 rows, one unit each) and its
+// 16-byte reads (16 chunks of one row) then touch 64 distinct banks.
+template <int C, typename St>
+__device__ __forceinline__ uint8_t* stage_unit(St st, int r, int u) {
+  return st(r >> 6) + (r & 63) * (C * 2) + 8 * (u ^ (r & 31));
+}
+
+// Copies the staged tile to global memory: every lane moves 16 bytes, a wave
+// covers whole rows (fully coalesced). dst(r, c) returns the destination of
+// tile row r, columns [c, c + 8), or nullptr when it is outside the matrix.
+template <int C, int NT, typename St, typename Dst>
+__device__ __forceinline__ void stage_copy_out(St st, int tid, int rows_valid, Dst dst) {
+  constexpr int CH = C / 8;                        // 16-byte chunks per row
+#pragma unroll 4
+  for (int idx = tid; idx < kTileM * CH; idx += NT) {
+    const int r = idx / CH, q = idx % CH;
+    if (r >= rows_valid) break;                    // rows only grow with idx
+    uint16_t* d = dst(r, 8 * q);
+    if (d == nullptr) continue;
+    const uint8_t* src = st(r >> 6) + (r & 63) * (C * 2) + 16 * (q ^ ((r & 31) >> 1));
+    uint4 v = *reinterpret_cast<const uint4*>(src);
+    if (r & 1) v = make_uint4(v.z, v.w, v.x, v.y);  // odd rows swap the two 8-byte units
+    *reinterpret_cast<uint4*>(d) = v;
+  }
+}
+
+// h = acc * scale + bias; then the stores / amax selected by the flags. Both
+// stores go through the LDS staging tile (the main loop's LDS is free here).
 // AMAX evaluates the activation from h rounded to bf16, exactly as a later
 // pass reading the stored h would.
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ>
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ, int NT, typename St>
 __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const EpiArgs& ep,
-                                              int m0, int n0, int wm, int wn, int lane,
-                                              float scale) {
+                                              int m0, int n0, int wm, int wn, int lane, int tid,
+                                              float scale, St st) {
   const int lm = lane & 31, lh = lane >> 5;
+  const int rows_valid = min(ep.M - m0, kTileM);
   float lmax = 0.0f;
+  // every wave's LDS reads of the main loop are done before the staging writes
+  __syncthreads();
+
+  // ---- pre-activation h: tile columns follow the B tile (gated: first half, then second half)
+  if constexpr (STORE_H || AMAX) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + lm;
-    if (m < ep.M) {
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + lm;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int tc0 = b_block_row<GATED, NJ>(wn, j);       // tile column of the block
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int tc = tc0 + g * 8 + lh * 4;
+          int col;
+          if constexpr (GATED) col = tc < 128 ? n0 + tc : ep.F + n0 + tc - 128;
+          else col = n0 + tc;
+          float h[4], b[4];
+          const bool in_range = GATED ? (n0 + (tc & 127) < ep.F) : (col < ep.n_b);
+          if (in_range) load_bias4(ep.bias, col, b);
+          else b[0] = b[1] = b[2] = b[3] = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale + b[q];
+          if constexpr (STORE_H) {
+            *reinterpret_cast<uint2*>(stage_unit<256>(st, r, tc >> 2)) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          }
+          if constexpr (AMAX && !GATED) {
+            if (in_range && m0 + r < ep.M) {
+              round_bf16x4(h);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(h[q])));
+            }
+          }
+        }
+      }
+      if constexpr (AMAX && GATED) {
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn * 16 * NJ + j * 32 + g * 8 + lh * 4;   // first-half column
+            if (col < ep.F && m0 + r < ep.M) {
+              float ha[4], hb[4], ba[4], bb[4];
+              load_bias4(ep.bias, col, ba);
+              load_bias4(ep.bias, ep.F + col, bb);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                ha[q] = acc[i][j][4 * g + q] * scale + ba[q];
+                hb[q] = acc[i][j + NJ / 2][4 * g + q] * scale + bb[q];
+              }
+              round_bf16x4(ha);
+              round_bf16x4(hb);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(ha[q]) * hb[q]));
+            }
+          }
+        }
+      }
+    }
+    if constexpr (STORE_H) {
+      __syncthreads();
+      stage_copy_out<256, NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
+        int col;
+        bool ok;
+        if constexpr (GATED) {
+          ok = n0 + (c & 127) < ep.F;
+          col = c < 128 ? n0 + c : ep.F + n0 + c - 128;
+        } else {
+          col = n0 + c;
+          ok = col < ep.n_b;
+        }
+        return ok ? ep.h_out + (int64_t)(m0 + r) * ep.n_b + col : nullptr;
+      });
+      if constexpr (STORE_OUT) __syncthreads();      // the staging tile is reused below
+    }
+  }
+
+  // ---- activation output
+  if constexpr (STORE_OUT) {
+    constexpr int C = GATED ? 128 : 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + lm;
       if constexpr (!GATED) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 32 * NJ + j * 32 + g * 8 + lh * 4;
-            if (col < ep.n_b) {
-              float h[4], b[4];
-              load_bias4(ep.bias, col, b);
+            const int tc = wn * 32 * NJ + j * 32 + g * 8 + lh * 4;
+            const int col = n0 + tc;
+            float h[4], b[4];
+            if (col < ep.n_b) load_bias4(ep.bias, col, b);
+            else b[0] = b[1] = b[2] = b[3] = 0.0f;
+            float o[4];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) h[r] = acc[i][j][4 * g + r] * scale + b[r];
-              if constexpr (STORE_H) store_bf16x4(ep.h_out + (int64_t)m * ep.n_b + col, h);
-              if constexpr (AMAX) round_bf16x4(h);
-              float o[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[r] = act_fwd<ACT>(h[r]);
-              if constexpr (STORE_OUT) store_bf16x4(ep.out + (int64_t)m * ep.n_b + col, o);
-              if constexpr (AMAX) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, fabsf(o[r]));
-              }
+            for (int q = 0; q < 4; ++q) {
+              h[q] = acc[i][j][4 * g + q] * scale + b[q];
+              o[q] = act_fwd<ACT>(h[q]);
             }
+            *reinterpret_cast<uint2*>(stage_unit<C>(st, r, tc >> 2)) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
         }
       } else {
@@ -142,41 +251,35 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
         for (int j = 0; j < NJ / 2; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 16 * NJ + j * 32 + g * 8 + lh * 4;   // first-half column
+            const int tc = wn * 16 * NJ + j * 32 + g * 8 + lh * 4;        // first-half tile column
+            const int col = n0 + tc;
+            float ba[4], bb[4];
             if (col < ep.F) {
-              float ha[4], hb[4], ba[4], bb[4];
               load_bias4(ep.bias, col, ba);
               load_bias4(ep.bias, ep.F + col, bb);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                ha[r] = acc[i][j][4 * g + r] * scale + ba[r];
-                hb[r] = acc[i][j + NJ / 2][4 * g + r] * scale + bb[r];
-              }
-              if constexpr (STORE_H) {
-                store_bf16x4(ep.h_out + (int64_t)m * ep.n_b + col, ha);
-                store_bf16x4(ep.h_out + (int64_t)m * ep.n_b + ep.F + col, hb);
-              }
-              if constexpr (AMAX) {
-                round_bf16x4(ha);
-                round_bf16x4(hb);
-              }
-              float o[4];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[r] = act_fwd<ACT>(ha[r]) * hb[r];
-              if constexpr (STORE_OUT) store_bf16x4(ep.out + (int64_t)m * ep.F + col, o);
-              if constexpr (AMAX) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) lmax = fmaxf(lmax, fabsf(o[r]));
-              }
+            } else {
+              ba[0] = ba[1] = ba[2] = ba[3] = bb[0] = bb[1] = bb[2] = bb[3] = 0.0f;
             }
+            float o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
+            *reinterpret_cast<uint2*>(stage_unit<C>(st, r, tc >> 2)) =
+                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
         }
       }
     }
+    __syncthreads();
+    const int n_out = GATED ? ep.F : ep.n_b;
+    stage_copy_out<C, NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
+      return n0 + c < n_out ? ep.out + (int64_t)(m0 + r) * n_out + n0 + c : nullptr;
+    });
   }
+
   if constexpr (AMAX) {
-    lmax = wave_max(lmax);
-    if (lane == 0) atomic_max_nonneg(ep.amax, lmax);
+    __shared__ float red[NT / 64];
+    block_max_atomic(lmax, ep.amax, red);
   }
 }
 

@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_fp8_kernel(GemmArgs a) {
 
   const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
   const float scale = (1.0f / sa) * (1.0f / sb);
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ>(acc, a.ep, m0, n0, wm, wn, lane, scale);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, a.ep, m0, n0, wm, wn, lane, tid, scale, stage_ptr);
 }
 
 constexpr int kWaves = TE_GEMM_WAVES;

@@ -80,10 +80,7 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   using I = Io<BF16>;
   constexpr int VEC = I::VEC;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
   const int64_t nch = a.hidden / VEC;
-  const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
   const uint4* gr = reinterpret_cast<const uint4*>(a.gamma);
   const uint4* br = reinterpret_cast<const uint4*>(a.beta);
   const float inv_h = 1.0f / (float)a.hidden;
@@ -91,109 +88,112 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   float qscale = 1.0f;
   if constexpr (MODE == kNormQuant) {
     qscale = fp8_scale_from_amax(*a.amax);
-    if (row == 0 && lane == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
       *a.scale_out = qscale;
       *a.scale_inv_out = 1.0f / qscale;
     }
   }
-
-  float mean = 0.0f, rs;
   float lmax = 0.0f;
-  if constexpr (NCH > 0) {
-    float v[NCH][VEC];
-    float s = 0.0f;
+  // one wave per row (the loop covers grids smaller than rows / 4)
+  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < a.rows; row += (int64_t)gridDim.x * 4) {
+    const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
+    float mean = 0.0f, rs;
+    if constexpr (NCH > 0) {
+      float v[NCH][VEC];
+      float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int64_t c = lane + 64 * j;
-      if (c < nch) {
-        I::unpack(xr[c], v[j]);
-      } else {
+      for (int j = 0; j < NCH; ++j) {
+        const int64_t c = lane + 64 * j;
+        if (c < nch) {
+          I::unpack(xr[c], v[j]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) v[j][i] = 0.0f;
+          for (int i = 0; i < VEC; ++i) v[j][i] = 0.0f;
+        }
+        if constexpr (!RMS) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) s += v[j][i];
+        }
       }
+      if constexpr (!RMS) mean = wave_sum(s) * inv_h;
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        if (lane + 64 * j < nch) {
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const float d = v[j][i] - mean;
+            ss += d * d;
+          }
+        }
+      }
+      rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
+      if constexpr (MODE != kNormQuant) {
+        if (lane == 0) {
+          if (a.mu != nullptr && !RMS) a.mu[row] = mean;
+          if (a.rsigma != nullptr) a.rsigma[row] = rs;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int64_t c = lane + 64 * j;
+        if (c < nch) {
+          float g[VEC], b[VEC], y[VEC];
+          I::unpack(gr[c], g);
+          if constexpr (!RMS) I::unpack(br[c], b);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) {
+            const float gi = a.zcg ? 1.0f + g[i] : g[i];
+            y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
+            lmax = fmaxf(lmax, fabsf(y[i]));
+          }
+          if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+        }
+      }
+    } else {
+      float s = 0.0f, v[VEC];
       if constexpr (!RMS) {
+        for (int64_t c = lane; c < nch; c += 64) {
+          I::unpack(xr[c], v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s += v[j][i];
+          for (int i = 0; i < VEC; ++i) s += v[i];
+        }
+        mean = wave_sum(s) * inv_h;
       }
-    }
-    if constexpr (!RMS) mean = wave_sum(s) * inv_h;
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      if (lane + 64 * j < nch) {
+      float ss = 0.0f;
+      for (int64_t c = lane; c < nch; c += 64) {
+        I::unpack(xr[c], v);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          const float d = v[j][i] - mean;
+          const float d = v[i] - mean;
           ss += d * d;
         }
       }
-    }
-    rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
-    if constexpr (MODE != kNormQuant) {
-      if (lane == 0) {
-        if (a.mu != nullptr && !RMS) a.mu[row] = mean;
-        if (a.rsigma != nullptr) a.rsigma[row] = rs;
+      rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
+      if constexpr (MODE != kNormQuant) {
+        if (lane == 0) {
+          if (a.mu != nullptr && !RMS) a.mu[row] = mean;
+          if (a.rsigma != nullptr) a.rsigma[row] = rs;
+        }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int64_t c = lane + 64 * j;
-      if (c < nch) {
+      for (int64_t c = lane; c < nch; c += 64) {
         float g[VEC], b[VEC], y[VEC];
+        I::unpack(xr[c], v);
         I::unpack(gr[c], g);
         if constexpr (!RMS) I::unpack(br[c], b);
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
           const float gi = a.zcg ? 1.0f + g[i] : g[i];
-          y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
+          y[i] = norm_value(v[i], mean, rs, gi, RMS ? 0.0f : b[i]);
           lmax = fmaxf(lmax, fabsf(y[i]));
         }
         if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
       }
     }
-  } else {
-    float s = 0.0f, v[VEC];
-    if constexpr (!RMS) {
-      for (int64_t c = lane; c < nch; c += 64) {
-        I::unpack(xr[c], v);
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) s += v[i];
-      }
-      mean = wave_sum(s) * inv_h;
-    }
-    float ss = 0.0f;
-    for (int64_t c = lane; c < nch; c += 64) {
-      I::unpack(xr[c], v);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float d = v[i] - mean;
-        ss += d * d;
-      }
-    }
-    rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
-    if constexpr (MODE != kNormQuant) {
-      if (lane == 0) {
-        if (a.mu != nullptr && !RMS) a.mu[row] = mean;
-        if (a.rsigma != nullptr) a.rsigma[row] = rs;
-      }
-    }
-    for (int64_t c = lane; c < nch; c += 64) {
-      float g[VEC], b[VEC], y[VEC];
-      I::unpack(xr[c], v);
-      I::unpack(gr[c], g);
-      if constexpr (!RMS) I::unpack(br[c], b);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        const float gi = a.zcg ? 1.0f + g[i] : g[i];
-        y[i] = norm_value(v[i], mean, rs, gi, RMS ? 0.0f : b[i]);
-        lmax = fmaxf(lmax, fabsf(y[i]));
-      }
-      if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
-    }
   }
   if constexpr (MODE == kNormAmax) {
-    lmax = wave_max(lmax);
-    if (lane == 0) atomic_max_nonneg(a.amax, lmax);
+    __shared__ float red[4];
+    block_max_atomic(lmax, a.amax, red);
   }
 }
 

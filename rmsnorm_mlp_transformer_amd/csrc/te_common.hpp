@@ -132,4 +132,20 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
 }
 
+// Workgroup-wide max of a non-negative value followed by a single atomic:
+// thousands of waves hitting one address serialise in the L2, so each
+// workgroup contributes one atomic. Must be reached by every thread of the
+// workgroup (it synchronises); red must hold one float per wave.
+__device__ __forceinline__ void block_max_atomic(float v, float* amax, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+    for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
+    atomic_max_nonneg(amax, m);
+  }
+}
+
 }  // namespace te

@@ -9,7 +9,8 @@ import torch
 import oracle as O
 import rmsnorm_mlp_transformer_amd as te
 import workloads as W
-from gpu_util import TOL, assert_rel, check_codes, codes_np, dev, f64, to_dev
+from gpu_util import (ACT_CODE_ONE_STEP_MAX, CODE_ONE_STEP_MAX, TOL, assert_rel, check_codes,
+                      check_codes_combined, codes_np, dev, f64, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -150,8 +151,10 @@ def test_mlp_fp8(name, rows, hidden, ffn, gated):
     # the kernels' codes are computed from exact inputs: bit-exact
     assert np.array_equal(codes_np(saved["w1q_t"]), o["w1q"].T)
     assert np.array_equal(codes_np(saved["w2q_t"]), o["w2q"].T)
-    check_codes(codes_np(saved["xq"]), o["xq"], "xq")
-    check_codes(codes_np(saved["actq"]), o["actq"], "actq")
+    check_codes_combined([("xq", codes_np(saved["xq"]), o["xq"], CODE_ONE_STEP_MAX),
+                          ("w1q", codes_np(saved["w1q_t"]).T, o["w1q"], CODE_ONE_STEP_MAX),
+                          ("w2q", codes_np(saved["w2q_t"]).T, o["w2q"], CODE_ONE_STEP_MAX),
+                          ("actq", codes_np(saved["actq"]), o["actq"], ACT_CODE_ONE_STEP_MAX)])
     assert_rel(f64(saved["h1"]), o["h1"], TOL["bf16"], "h1")
     assert_rel(f64(y), o["y"], TOL["fp8"], "y")
 

@@ -98,6 +98,16 @@ def test_e4m3_matches_torch_cast_in_range():
     assert np.array_equal(O.e4m3_encode(v.astype(np.float32).astype(np.float64)), ref)
 
 
+def test_e4m3_fp32_fast_path_matches_definition():
+    pos = O.e4m3_decode(np.arange(0, 0x7F))
+    m32 = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    v = np.concatenate([pos, m32, np.nextafter(m32, np.float32(0)), np.nextafter(m32, np.float32(1e9)),
+                        RNG.standard_normal(100000) * 2.0 ** RNG.integers(-14, 11, 100000),
+                        [0.0, -0.0, 448.0, 449.0, 1e6, 1e-12, -1e-12]]).astype(np.float32)
+    v = np.concatenate([v, -v])
+    assert np.array_equal(O.e4m3_encode_fp32(v), O.e4m3_encode(v.astype(np.float64)))
+
+
 def test_e4m3_encode_is_nearest_by_brute_force():
     table = O.e4m3_decode(np.arange(0, 0x7F))
     v = np.abs(RNG.standard_normal(3000)) * 2.0 ** RNG.integers(-11, 9, 3000)
