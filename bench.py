@@ -40,11 +40,10 @@ import workloads as W  # noqa: E402
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
 CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
+_GEMM = ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
 KERNEL_SOURCES = {
-    "gemm_bf16_act": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
-    "gemm_bf16": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
-    "gemm_bf16_gated": ["gemm_bf16.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
-    "gemm_fp8_h_amax": ["gemm_fp8.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"],
+    "gemm_bf16_act": _GEMM, "gemm_bf16": _GEMM, "gemm_bf16_gated": _GEMM, "gemm_fp8_h_amax": _GEMM,
+    "gemm_fp8": _GEMM,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
 }
 # Counter-measured HBM bytes per launch: {(workload, kernel): (bytes, source hash)}.

@@ -151,11 +151,12 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
     float* scale_out, float* scale_inv_out) {
   __shared__ uint8_t tile[64][64 + 4];
   const float scale = fp8_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && scale_out != nullptr) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out != nullptr) {
     *scale_out = scale;
     *scale_inv_out = 1.0f / scale;
   }
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
   const int t = threadIdx.x;
   // read: 64 rows x 8 column-chunks = 512 chunks, 2 per thread
 #pragma unroll
@@ -408,7 +409,7 @@ hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, 
                                      uint8_t* codes_t, const float* amax, float* scale_out,
                                      float* scale_inv_out, hipStream_t s) {
   LaunchScope scope("quantize_transpose", s);
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  const unsigned grid = (unsigned)(((cols + 63) / 64) * ((rows + 63) / 64));   // < 2^18 for weights < 2 GiB
   if (x_dtype == kBF16)
     quantize_transpose_kernel<true><<<grid, kThreads, 0, s>>>(x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
   else

@@ -44,7 +44,7 @@ struct Stage {
 // quarters of the 64 banks.
 __device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES>
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES, bool PP>
 __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   using St = Stage<BK>;
   constexpr int NJ = 16 / WAVES;                      // 32-column blocks per wave
@@ -87,9 +87,11 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   // the whole B operand (K * NB * 2 < 2^31 bytes, checked by the launcher)
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.B, (uint32_t)K * NB * 2);
   uint32_t off_b[LB];
+  int kr_b[LB];
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
     const int kr = wave * RB + j * 2 + (lane >> 5);
+    kr_b[j] = kr;
     const int q = (lane & 31) ^ swz_b(kr);
     int n;
     if constexpr (GATED) n = q < 16 ? n0 + 8 * q : F + n0 + 8 * (q - 16);
@@ -106,10 +108,14 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
       const uint32_t v = (tail && k0 + kc_a[j] >= K) ? kOffNone : off_a[j];
       load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * 2);
     }
-    // rows at or past K (including whole stages past the end) read as zero
+    // k-rows at or past K (including whole stages past the end) read as zero:
+    // their lanes take an offset beyond the range, so the check fails on the
+    // per-lane offset alone
 #pragma unroll
-    for (int j = 0; j < LB; ++j)
-      load_lds16(rsrc_b, Bs + wave * RB * 512 + j * 1024, off_b[j], (uint32_t)k0 * NB * 2);
+    for (int j = 0; j < LB; ++j) {
+      const uint32_t v = k0 + kr_b[j] >= K ? kOffNone : off_b[j];
+      load_lds16(rsrc_b, Bs + wave * RB * 512 + j * 1024, v, (uint32_t)k0 * NB * 2);
+    }
   };
 
   // ---- fragment addresses (byte offsets inside a stage)
@@ -125,6 +131,9 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     const int n_local = b_block_row<GATED, NJ>(wn, j) + 16 * (g & 1) + 4 * c4;
     b_off[j] = St::A_BYTES + (8 * (g >> 1) + i4) * 512 + 16 * ((n_local >> 3) ^ swz_b(i4)) + 8 * (c4 & 1);
   }
+
+  uint2 bv[NJ][4];   // the epilogue's bias values, loaded while the main loop runs
+  load_bias_frag<GATED, NJ>(a.ep, n0, wn, lane, bv);
 
   f32x16_t acc[4][NJ];
 #pragma unroll
@@ -168,63 +177,110 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     }
   };
 
-  // ---- pipeline. Step kt, with stage kt's first-substep fragments in f0:
-  //   MFMAs(f0) || reads of f1 (stage kt, second substep)
-  //   wait: own LDS reads and the DMA of stage kt+1; barrier (all waves)
-  //   DMA of stage kt+3 into the buffer of stage kt-1 (no longer read)
-  //   MFMAs(f1) || reads of f0 for stage kt+1
-  // Every step issues exactly one stage (past K it reads nothing), so the
-  // wait before the barrier always leaves the newest STAGES - 3 stages in flight.
-  static_assert(STAGES == 4, "three stages ahead of the one being consumed");
-  Frags f0, f1;
-  auto step = [&](int kt, int s) {
-    read_frags(s, 1, f1);
-    mfmas(f0);
-    interleave();
-    wait_vmcnt_lgkm0<(STAGES - 3) * (LA + LB)>();
-    block_barrier();
-    issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-    __builtin_amdgcn_sched_group_barrier(0x020, LA + LB, 0);   // the DMA goes out first
-    read_frags((s + 1) % STAGES, 0, f0);
-    mfmas(f1);
-    interleave();
-  };
   const int nk = (K + BK - 1) / BK;
+  static_assert(STAGES == 4, "three stages ahead of the one being consumed");
+  if constexpr (PP) {
+    // ---- ping-pong pipeline. Waves 0-3 and 4-7 form two groups with one
+    // wave of each on every SIMD. Each wave alternates a memory phase M(t)
+    // (its share of the DMA of stage t+3, all fragment reads of stage t, then
+    // waits) and a compute phase C(t) (the stage's 16 MFMAs), with a barrier
+    // after each. Group 1 starts one phase late, so on every SIMD one wave
+    // issues MFMAs while the other feeds LDS and registers.
+    //   phase 2t:   group 0 M(t),  group 1 C(t-1)
+    //   phase 2t+1: group 0 C(t),  group 1 M(t)
+    // The DMA of M(t) refills the buffer of stage t-1, last read by group 1 in
+    // phase 2t-1 and waited for (lgkmcnt 0) before that phase's barrier. The
+    // wait at the end of M(t) completes the wave's share of stage t+1 (two
+    // newer stages stay in flight); both groups' shares of stage t+1 are then
+    // complete before phase 2t+2, where it is first read.
+    const bool late = wave >= WAVES / 2;
+    Frags fa, fb;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
-  wait_vmcnt<(STAGES - 2) * (LA + LB)>();
-  block_barrier();
-  read_frags(0, 0, f0);
-  int kb = 0;
-  for (; kb + STAGES <= nk; kb += STAGES) {
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+    wait_vmcnt<(STAGES - 2) * (LA + LB)>();
+    block_barrier();
+    if (late) block_barrier();
+    auto pp_step = [&](int kt, int s) {
+      issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+      read_frags(s, 0, fa);
+      read_frags(s, 1, fb);
+      wait_vmcnt_lgkm0<(STAGES - 2) * (LA + LB)>();
+      block_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+      mfmas(fa);
+      mfmas(fb);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+      block_barrier();
+    };
+    int kb = 0;
+    for (; kb + STAGES <= nk; kb += STAGES) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) step(kb + s, s);
+      for (int s = 0; s < STAGES; ++s) pp_step(kb + s, s);
+    }
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (kb + s < nk) pp_step(kb + s, s);
+    if (!late) block_barrier();   // the same number of barriers in both groups
+  } else {
+    // ---- interleaved pipeline. Step kt, with stage kt's first-substep fragments in f0:
+    //   MFMAs(f0) || reads of f1 (stage kt, second substep)
+    //   wait: own LDS reads and the DMA of stage kt+1; barrier (all waves)
+    //   DMA of stage kt+3 into the buffer of stage kt-1 (no longer read)
+    //   MFMAs(f1) || reads of f0 for stage kt+1
+    // Every step issues exactly one stage (past K it reads nothing), so the
+    // wait before the barrier always leaves the newest STAGES - 3 stages in flight.
+    Frags f0, f1;
+    auto step = [&](int kt, int s) {
+      read_frags(s, 1, f1);
+      mfmas(f0);
+      interleave();
+      wait_vmcnt_lgkm0<(STAGES - 3) * (LA + LB)>();
+      block_barrier();
+      issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+      __builtin_amdgcn_sched_group_barrier(0x020, LA + LB, 0);   // the DMA goes out first
+      read_frags((s + 1) % STAGES, 0, f0);
+      mfmas(f1);
+      interleave();
+    };
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+    wait_vmcnt<(STAGES - 2) * (LA + LB)>();
+    block_barrier();
+    read_frags(0, 0, f0);
+    int kb = 0;
+    for (; kb + STAGES <= nk; kb += STAGES) {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) step(kb + s, s);
+    }
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (kb + s < nk) step(kb + s, s);
   }
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (kb + s < nk) step(kb + s, s);
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, a.ep, m0, n0, wm, wn, lane, tid, 1.0f, stage_ptr);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid, 1.0f, stage_ptr);
 }
 
 constexpr int kWaves = TE_GEMM_WAVES;
 constexpr int kBK = TE_GEMM_BK;
 constexpr int kStages = TE_GEMM_STAGES;
+constexpr bool kPingPong = TE_GEMM_PINGPONG != 0;
 
 template <int ACT, bool GATED>
 hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }

@@ -33,12 +33,10 @@ namespace te {
 #ifndef TE_GEMM_STAGES
 #define TE_GEMM_STAGES 4
 #endif
-// fp8 pipeline: k bytes per LDS stage and number of stages.
-#ifndef TE_GEMM_FP8_BK
-#define TE_GEMM_FP8_BK 64
-#endif
-#ifndef TE_GEMM_FP8_STAGES
-#define TE_GEMM_FP8_STAGES 4
+// bf16 schedule: 1 = ping-pong (the two waves of a SIMD alternate between
+// MFMA and memory phases), 0 = every wave interleaves reads and MFMAs.
+#ifndef TE_GEMM_PINGPONG
+#define TE_GEMM_PINGPONG 1
 #endif
 
 constexpr int kTileM = 256;
@@ -82,12 +80,38 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = in_group / gsz;
 }
 
-__device__ __forceinline__ void load_bias4(const uint16_t* bias, int col, float* b) {
-  if (bias == nullptr) {
-    b[0] = b[1] = b[2] = b[3] = 0.0f;
-    return;
+// Global column of tile column tc (gated tiles hold [n0, n0 + 128) of the
+// first half and the same columns of the second half); in_range is false
+// for columns outside the matrix.
+template <bool GATED>
+__device__ __forceinline__ int tile_col(const EpiArgs& ep, int n0, int tc, bool& in_range) {
+  if constexpr (GATED) {
+    in_range = n0 + (tc & 127) < ep.F;
+    return tc < 128 ? n0 + tc : ep.F + n0 + tc - 128;
+  } else {
+    in_range = n0 + tc < ep.n_b;
+    return n0 + tc;
   }
-  const uint2 w = *reinterpret_cast<const uint2*>(bias + col);
+}
+
+// The bias values of the columns a lane owns in the epilogue (block j of NJ,
+// group g of 4: tile columns b_block_row(wn, j) + 8 g + 4 (lane / 32) + 0..3)
+// as packed bf16 pairs; zero without a bias or outside the matrix. Loaded
+// before the main loop, so the epilogue never waits for them.
+template <bool GATED, int NJ>
+__device__ __forceinline__ void load_bias_frag(const EpiArgs& ep, int n0, int wn, int lane, uint2 (&bv)[NJ][4]) {
+  const int lh = (lane & 63) >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bool ok;
+      const int col = tile_col<GATED>(ep, n0, b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4, ok);
+      bv[j][g] = ep.bias != nullptr && ok ? *reinterpret_cast<const uint2*>(ep.bias + col) : make_uint2(0u, 0u);
+    }
+}
+
+__device__ __forceinline__ void unpack_bias4(const uint2& w, float* b) {
   b[0] = bf16_lo(w.x); b[1] = bf16_hi(w.x); b[2] = bf16_lo(w.y); b[3] = bf16_hi(w.y);
 }
 
@@ -113,32 +137,46 @@ __device__ __forceinline__ uint8_t* stage_unit(St st, int r, int u) {
 }
 
 // Copies the staged tile to global memory: every lane moves 16 bytes, a wave
-// covers whole rows (fully coalesced). dst(r, c) returns the destination of
-// tile row r, columns [c, c + 8), or nullptr when it is outside the matrix.
-template <int C, int NT, typename St, typename Dst>
+// covers whole rows (fully coalesced). The LDS reads of a batch of BATCH
+// chunks per thread are issued before its stores. dst(r, c) returns the
+// destination of tile row r, columns [c, c + 8), or nullptr when it is
+// outside the matrix.
+template <int C, int NT, int BATCH, typename St, typename Dst>
 __device__ __forceinline__ void stage_copy_out(St st, int tid, int rows_valid, Dst dst) {
   constexpr int CH = C / 8;                        // 16-byte chunks per row
-#pragma unroll 4
-  for (int idx = tid; idx < kTileM * CH; idx += NT) {
-    const int r = idx / CH, q = idx % CH;
-    if (r >= rows_valid) break;                    // rows only grow with idx
-    uint16_t* d = dst(r, 8 * q);
-    if (d == nullptr) continue;
-    const uint8_t* src = st(r >> 6) + (r & 63) * (C * 2) + 16 * (q ^ ((r & 31) >> 1));
-    uint4 v = *reinterpret_cast<const uint4*>(src);
-    if (r & 1) v = make_uint4(v.z, v.w, v.x, v.y);  // odd rows swap the two 8-byte units
-    *reinterpret_cast<uint4*>(d) = v;
+  constexpr int N = kTileM * CH / NT;              // chunks per thread
+  static_assert(kTileM * CH % NT == 0 && NT % CH == 0, "whole rows per pass");
+  static_assert(N % BATCH == 0, "whole batches");
+#pragma unroll
+  for (int k0 = 0; k0 < N; k0 += BATCH) {
+    uint4 v[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int r = (tid + (k0 + k) * NT) / CH, q = (tid + (k0 + k) * NT) % CH;
+      v[k] = *reinterpret_cast<const uint4*>(st(r >> 6) + (r & 63) * (C * 2) + 16 * (q ^ ((r & 31) >> 1)));
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int r = (tid + (k0 + k) * NT) / CH, q = (tid + (k0 + k) * NT) % CH;
+      if (r < rows_valid) {
+        uint16_t* d = dst(r, 8 * q);
+        if (d != nullptr) {
+          const uint4 w = (r & 1) ? make_uint4(v[k].z, v[k].w, v[k].x, v[k].y) : v[k];  // odd rows swap 8-byte units
+          *reinterpret_cast<uint4*>(d) = w;
+        }
+      }
+    }
   }
 }
 
 // h = acc * scale + bias; then the stores / amax selected by the flags. Both
 // stores go through the LDS staging tile (the main loop's LDS is free here).
 // AMAX evaluates the activation from h rounded to bf16, exactly as a later
-// pass reading the stored h would.
+// pass reading the stored h would. bv: load_bias_frag() of the same lane.
 template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ, int NT, typename St>
-__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const EpiArgs& ep,
-                                              int m0, int n0, int wm, int wn, int lane, int tid,
-                                              float scale, St st) {
+__device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const uint2 (&bv)[NJ][4],
+                                              const EpiArgs& ep, int m0, int n0, int wm, int wn, int lane,
+                                              int tid, float scale, St st) {
   const int lm = lane & 31, lh = lane >> 5;
   const int rows_valid = min(ep.M - m0, kTileM);
   float lmax = 0.0f;
@@ -152,17 +190,11 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
       const int r = wm * 128 + i * 32 + lm;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int tc0 = b_block_row<GATED, NJ>(wn, j);       // tile column of the block
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int tc = tc0 + g * 8 + lh * 4;
-          int col;
-          if constexpr (GATED) col = tc < 128 ? n0 + tc : ep.F + n0 + tc - 128;
-          else col = n0 + tc;
+          const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;
           float h[4], b[4];
-          const bool in_range = GATED ? (n0 + (tc & 127) < ep.F) : (col < ep.n_b);
-          if (in_range) load_bias4(ep.bias, col, b);
-          else b[0] = b[1] = b[2] = b[3] = 0.0f;
+          unpack_bias4(bv[j][g], b);
 #pragma unroll
           for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale + b[q];
           if constexpr (STORE_H) {
@@ -170,6 +202,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
                 make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           }
           if constexpr (AMAX && !GATED) {
+            bool in_range;
+            tile_col<GATED>(ep, n0, tc, in_range);
             if (in_range && m0 + r < ep.M) {
               round_bf16x4(h);
 #pragma unroll
@@ -179,15 +213,16 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
         }
       }
       if constexpr (AMAX && GATED) {
+        // block j (first half) pairs with block j + NJ / 2 (the same columns of the second half)
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * 16 * NJ + j * 32 + g * 8 + lh * 4;   // first-half column
+            const int col = n0 + b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;   // first-half column
             if (col < ep.F && m0 + r < ep.M) {
               float ha[4], hb[4], ba[4], bb[4];
-              load_bias4(ep.bias, col, ba);
-              load_bias4(ep.bias, ep.F + col, bb);
+              unpack_bias4(bv[j][g], ba);
+              unpack_bias4(bv[j + NJ / 2][g], bb);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 ha[q] = acc[i][j][4 * g + q] * scale + ba[q];
@@ -204,16 +239,11 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     }
     if constexpr (STORE_H) {
       __syncthreads();
-      stage_copy_out<256, NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
-        int col;
+      // while the accumulators are still live (STORE_OUT follows), smaller batches
+      constexpr int kHChunks = kTileM * 32 / NT;
+      stage_copy_out<256, NT, STORE_OUT ? 4 : kHChunks>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
         bool ok;
-        if constexpr (GATED) {
-          ok = n0 + (c & 127) < ep.F;
-          col = c < 128 ? n0 + c : ep.F + n0 + c - 128;
-        } else {
-          col = n0 + c;
-          ok = col < ep.n_b;
-        }
+        const int col = tile_col<GATED>(ep, n0, c, ok);
         return ok ? ep.h_out + (int64_t)(m0 + r) * ep.n_b + col : nullptr;
       });
       if constexpr (STORE_OUT) __syncthreads();      // the staging tile is reused below
@@ -231,17 +261,11 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
         for (int j = 0; j < NJ; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int tc = wn * 32 * NJ + j * 32 + g * 8 + lh * 4;
-            const int col = n0 + tc;
-            float h[4], b[4];
-            if (col < ep.n_b) load_bias4(ep.bias, col, b);
-            else b[0] = b[1] = b[2] = b[3] = 0.0f;
-            float o[4];
+            const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;
+            float b[4], o[4];
+            unpack_bias4(bv[j][g], b);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              h[q] = acc[i][j][4 * g + q] * scale + b[q];
-              o[q] = act_fwd<ACT>(h[q]);
-            }
+            for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + b[q]);
             *reinterpret_cast<uint2*>(stage_unit<C>(st, r, tc >> 2)) =
                 make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
@@ -251,16 +275,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
         for (int j = 0; j < NJ / 2; ++j) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int tc = wn * 16 * NJ + j * 32 + g * 8 + lh * 4;        // first-half tile column
-            const int col = n0 + tc;
-            float ba[4], bb[4];
-            if (col < ep.F) {
-              load_bias4(ep.bias, col, ba);
-              load_bias4(ep.bias, ep.F + col, bb);
-            } else {
-              ba[0] = ba[1] = ba[2] = ba[3] = bb[0] = bb[1] = bb[2] = bb[3] = 0.0f;
-            }
-            float o[4];
+            const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;   // first-half tile column
+            float ba[4], bb[4], o[4];
+            unpack_bias4(bv[j][g], ba);
+            unpack_bias4(bv[j + NJ / 2][g], bb);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
@@ -272,7 +290,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     }
     __syncthreads();
     const int n_out = GATED ? ep.F : ep.n_b;
-    stage_copy_out<C, NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
+    stage_copy_out<C, NT, kTileM * (C / 8) / NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
       return n0 + c < n_out ? ep.out + (int64_t)(m0 + r) * n_out + n0 + c : nullptr;
     });
   }

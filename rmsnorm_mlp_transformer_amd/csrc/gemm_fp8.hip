@@ -1,19 +1,27 @@
 // fp8 (E4M3 x E4M3) MFMA GEMM for gfx950 with fp32 accumulation and the
-// fused epilogue. Used when the quantizer set enables per-tensor current
-// scaling: "NVIDIA TransformerEngine JAX LayerNorm Dense" (Description: the
-// normalised output and the kernel are quantised, then the GEMM runs) and
-// "... LayerNorm MLP" (Description: the same for GEMM1 and GEMM2).
+// fused bias / activation / gate / amax epilogue. Used when the quantizer set
+// enables per-tensor current scaling: "NVIDIA TransformerEngine JAX LayerNorm
+// Dense" (Description: the normalised output and the kernel are quantised,
+// then the GEMM runs) and "... LayerNorm MLP" (Description: the same for
+// GEMM1 and GEMM2).
 //
 // Both operands arrive K-contiguous: A codes [M, K] and B^T codes [n_b, K]
-// (the weight quantiser writes the kernel transposed). A BK-deep k stage of
-// each operand (256 rows x BK bytes) moves to LDS with buffer_load ... lds,
-// 16-byte chunks XOR-swizzled per row; each lane then reads its 32
-// consecutive k bytes per operand with two ds_read_b128 and issues
+// (the weight quantiser writes the kernel transposed). Each k stage holds 64
+// codes of every tile row for 256 rows of each operand; both tiles move HBM ->
+// LDS with buffer_load ... lds (16 bytes per lane, no register staging),
+// 16-byte chunks XOR-swizzled per row, and come back with conflict-free
+// ds_read_b128, two per lane and operand for one
 // v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 for both operands, unit block
-// scales). STAGES LDS stages (128 KiB in all), one barrier per stage.
+// scales). The accumulator is multiplied by scale_inv(A) * scale_inv(B),
+// which the kernel derives from the two amax values exactly as the
+// quantisers did.
 //
-// The accumulator is multiplied by scale_inv(A) * scale_inv(B), which the
-// kernel derives from the two amax values exactly as the quantisers did.
+// 256 x 256 output tile per workgroup, 8 waves of 128 x 64, 4 LDS stages
+// (128 KiB). Ping-pong schedule: waves 0-3 and 4-7 hold one wave per SIMD
+// each and alternate, one phase apart, between a memory phase (their share
+// of the DMA three stages ahead, all fragment reads of the current stage)
+// and a compute phase (the stage's MFMAs), so each SIMD's matrix core is fed
+// by one wave while the other loads.
 #include "gemm_common.hpp"
 #include "gemm_lds.hpp"
 #include "te_kernels.hpp"
@@ -21,31 +29,44 @@
 namespace te {
 namespace {
 
-struct GemmArgs {
+constexpr int kWaves = 8;
+constexpr int kRowBytes = 64;              // bytes of one tile row per k stage
+constexpr int kStages = 4;
+constexpr int kCpr = kRowBytes / 16;       // 16-byte chunks per tile row
+constexpr int kOpBytes = kTileM * kRowBytes;
+constexpr int kStageBytes = 2 * kOpBytes;
+constexpr int kNJ = 2;                     // 32-column blocks per wave
+constexpr int kRowsPerWave = kTileM / kWaves;
+constexpr int kLJ = kRowsPerWave * kRowBytes / 1024;   // 1 KiB loads per wave, operand and stage
+constexpr int kLoads = 2 * kLJ;                        // per wave and stage
+
+struct FpArgs {
   const uint8_t* A;
   const uint8_t* Bt;
   int K;
-  const float* amax_a;
+  const float* amax_a;      // amaxes of the two quantised operands
   const float* amax_b;
   EpiArgs ep;
 };
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES>
-__global__ void __launch_bounds__(64 * WAVES, 1) gemm_fp8_kernel(GemmArgs a) {
-  constexpr int CPR = BK / 16;                  // 16-byte chunks per tile row
-  constexpr int OP_BYTES = kTileM * BK;         // one operand of one stage
-  constexpr int BYTES = 2 * OP_BYTES;
-  constexpr int NJ = 16 / WAVES;                // 32-column blocks per wave
-  constexpr int RW = kTileM / WAVES;            // tile rows loaded per wave and operand
-  constexpr int LJ = RW * BK / 1024;            // 1 KiB loads per wave, operand and stage
-  constexpr int KS = BK / 64;                   // MFMA k-steps per stage
-  static_assert(LJ >= 1 && KS >= 1, "tile too small for the wave count");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 stages");
-  // one array per stage (see the bf16 GEMM): no false LDS-DMA dependencies
-  __shared__ __attribute__((aligned(1024))) uint8_t sm0[BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm1[BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm2[STAGES > 2 ? BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sm3[STAGES > 3 ? BYTES : 16];
+struct Frags {
+  i32x8_t a[4];             // row blocks
+  i32x8_t b[kNJ];           // column blocks
+};
+
+__device__ __forceinline__ i32x8_t join16x2(const uint4& lo, const uint4& hi) {
+  return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
+__global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
+  constexpr int KE = kRowBytes;            // codes (k values) per stage
+  // one array per stage: distinct objects let the compiler see that the
+  // LDS-DMA of a later stage cannot alias the reads of the current one
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[kStageBytes];
   auto stage_ptr = [&](int s) -> uint8_t* { return s == 0 ? sm0 : s == 1 ? sm1 : s == 2 ? sm2 : sm3; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -57,140 +78,154 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_fp8_kernel(GemmArgs a) {
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
+  const uint32_t pitch = (uint32_t)K;      // bytes per operand row (< 2^31, checked by the caller)
 
-  // ---- loaders: wave w fills rows [w RW, (w + 1) RW) of both tiles
+  // ---- loaders: wave w fills tile rows [w R, (w + 1) R) of both operands
   const int rows_a = min(M - m0, kTileM);
-  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * pitch, (uint32_t)rows_a * pitch);
   // B^T rows of this tile: [n0, n0 + 256), or for gated the first-half rows
-  // [n0, n0 + 128) (first half of the waves) and the second-half rows
-  // [F + n0, F + n0 + 128) (second half of the waves)
+  // [n0, n0 + 128) (waves 0-3) and the second-half rows [F + n0, F + n0 + 128) (waves 4-7)
   int b_row0, b_rows;
   if constexpr (GATED) {
-    b_row0 = (wave < WAVES / 2 ? 0 : F) + n0;
+    b_row0 = (wave < kWaves / 2 ? 0 : F) + n0;
     b_rows = min(F - n0, 128);
   } else {
     b_row0 = n0;
     b_rows = min(NB - n0, kTileN);
   }
-  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.Bt + (int64_t)b_row0 * K, (uint32_t)b_rows * K);
-  const int b_first = GATED ? (wave % (WAVES / 2)) * RW : wave * RW;   // first row inside its part
-  uint32_t off_a[LJ], off_b[LJ];
-  int kc[LJ];
+  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.Bt + (int64_t)b_row0 * pitch, (uint32_t)b_rows * pitch);
+  const int b_first = GATED ? (wave % (kWaves / 2)) * kRowsPerWave : wave * kRowsPerWave;
+  uint32_t off_a[kLJ], off_b[kLJ];
+  int kc[kLJ];
 #pragma unroll
-  for (int j = 0; j < LJ; ++j) {
-    const int r = wave * RW + j * (64 / CPR) + lane / CPR;    // row inside the LDS tile
-    const int c = (lane % CPR) ^ chunk_swizzle<CPR>(r);
-    off_a[j] = (uint32_t)r * K + c * 16;
-    off_b[j] = (uint32_t)(b_first + j * (64 / CPR) + lane / CPR) * K + c * 16;
+  for (int j = 0; j < kLJ; ++j) {
+    const int r = wave * kRowsPerWave + j * (64 / kCpr) + lane / kCpr;   // row inside the LDS tile
+    const int c = (lane % kCpr) ^ chunk_swizzle<kCpr>(r);
+    off_a[j] = (uint32_t)r * pitch + c * 16;
+    off_b[j] = (uint32_t)(b_first + j * (64 / kCpr) + lane / kCpr) * pitch + c * 16;
     kc[j] = c * 16;
   }
   auto issue_stage = [&](int kt, int s) {
-    const int k0 = kt * BK;
+    const int k0 = kt * KE;
     uint8_t* As = stage_ptr(s);
-    uint8_t* Bs = As + OP_BYTES;
+    uint8_t* Bs = As + kOpBytes;
     // chunks at or past K (including whole stages past the end) read as zero
 #pragma unroll
-    for (int j = 0; j < LJ; ++j) {
+    for (int j = 0; j < kLJ; ++j) {
       const bool out = k0 + kc[j] >= K;
-      load_lds16(rsrc_a, As + wave * RW * BK + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0);
-      load_lds16(rsrc_b, Bs + wave * RW * BK + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0);
+      load_lds16(rsrc_a, As + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0);
+      load_lds16(rsrc_b, Bs + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0);
     }
   };
 
-  // ---- fragment addresses: 32 k bytes = logical chunks 4 ks + 2 h and + 1
+  // ---- fragment addresses. Lane l reads row l % 32 of its 32-row block; the
+  // chunk swizzle of every such row is that of row l % 32.
   const int lr = lane & 31, lh = lane >> 5;
-  int a_lo[KS], a_hi[KS], b_lo[NJ][KS], b_hi[NJ][KS];
+  const int sw = chunk_swizzle<kCpr>(lr);
+  int a_off[2], b_off[kNJ][2];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = 4 * ks + 2 * lh;
-    const int sw = chunk_swizzle<CPR>(lr);
-    a_lo[ks] = (wm * 128 + lr) * BK + 16 * (c ^ sw);
-    a_hi[ks] = (wm * 128 + lr) * BK + 16 * ((c + 1) ^ sw);
+  for (int h = 0; h < 2; ++h) {
+    // the lane's 32 k bytes are chunks 2 lh and 2 lh + 1
+    const int c = 2 * lh + h;
+    a_off[h] = (wm * 128 + lr) * kRowBytes + 16 * (c ^ sw);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int row = b_block_row<GATED, NJ>(wn, j) + lr;
-      b_lo[j][ks] = OP_BYTES + row * BK + 16 * (c ^ sw);
-      b_hi[j][ks] = OP_BYTES + row * BK + 16 * ((c + 1) ^ sw);
-    }
+    for (int j = 0; j < kNJ; ++j)
+      b_off[j][h] = kOpBytes + (b_block_row<GATED, kNJ>(wn, j) + lr) * kRowBytes + 16 * (c ^ sw);
   }
 
-  f32x16_t acc[4][NJ];
+  uint2 bv[kNJ][4];   // the epilogue's bias values, loaded while the main loop runs
+  load_bias_frag<GATED, kNJ>(a.ep, n0, wn, lane, bv);
+
+  f32x16_t acc[4][kNJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < kNJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute_stage = [&](int s) {
+  Frags f;
+  auto read_frags = [&](int s) {
     const uint8_t* S = stage_ptr(s);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x8_t af[4], bfr[NJ];
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = join16x2(*reinterpret_cast<const uint4*>(S + a_off[0] + i * 32 * kRowBytes),
+                        *reinterpret_cast<const uint4*>(S + a_off[1] + i * 32 * kRowBytes));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(S + a_lo[ks] + i * 32 * BK);
-        const uint4 hi = *reinterpret_cast<const uint4*>(S + a_hi[ks] + i * 32 * BK);
-        af[i] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    for (int j = 0; j < kNJ; ++j)
+      f.b[j] = join16x2(*reinterpret_cast<const uint4*>(S + b_off[j][0]),
+                        *reinterpret_cast<const uint4*>(S + b_off[j][1]));
+  };
+  // B fragment first: each lane then holds 4 consecutive output columns
+  auto mfmas = [&]() {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(S + b_lo[j][ks]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(S + b_hi[j][ks]);
-        bfr[j] = i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          // cbsz/blgp = 0: both operands E4M3; scales 127 = 2^0 (no block scaling)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[j], af[i], acc[i][j], 0, 0,
-                                                                       0, 127, 0, 127);
-    }
+      for (int j = 0; j < kNJ; ++j)
+        // cbsz/blgp = 0: both operands E4M3; scales 127 = 2^0 (no block scaling)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, 127, 0, 127);
   };
 
-  // ---- pipeline (as in the bf16 GEMM): one stage issued per step, the
-  // newest STAGES - 2 stages stay in flight across the barrier
+  // ---- ping-pong pipeline.
+  //   phase 2t:   group 0 memory M(t),  group 1 compute C(t-1)
+  //   phase 2t+1: group 0 compute C(t), group 1 memory M(t)
+  // M(t): DMA of the wave's share of stage t+3 into the buffer of stage t-1,
+  // fragment reads of stage t, then wait for those reads and for the wave's
+  // share of stage t+1 (two newer stages stay in flight); barrier.
+  // C(t): the stage's MFMAs; barrier.
+  // The buffer of stage t-1 was last read by group 1 in phase 2t-1 and those
+  // reads completed before that phase's barrier; both groups' shares of stage
+  // t+1 are complete before phase 2t+2, where it is first read. Every step
+  // issues exactly one stage (past K it reads nothing), so the vmcnt budget is
+  // the same in every step, and both groups pass the same number of barriers.
+  const bool late = wave >= kWaves / 2;
+  const int nk = (K + KE - 1) / KE;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_stage(s, s);
+  wait_vmcnt<(kStages - 2) * kLoads>();
+  block_barrier();
+  if (late) block_barrier();
   auto step = [&](int kt, int s) {
-    wait_vmcnt<(STAGES - 2) * 2 * LJ>();
+    issue_stage(kt + kStages - 1, (s + kStages - 1) % kStages);
+    read_frags(s);
+    wait_vmcnt_lgkm0<(kStages - 2) * kLoads>();
     block_barrier();
-    issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-    compute_stage(s);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    mfmas();
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
   };
-  const int nk = (K + BK - 1) / BK;
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
   int kb = 0;
-  for (; kb + STAGES <= nk; kb += STAGES) {
+  for (; kb + kStages <= nk; kb += kStages) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) step(kb + s, s);
+    for (int s = 0; s < kStages; ++s) step(kb + s, s);
   }
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < kStages - 1; ++s)
     if (kb + s < nk) step(kb + s, s);
-  wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
+  if (!late) block_barrier();
+  wait_vmcnt<0>();   // no LDS-DMA may still be writing when the epilogue reuses the LDS
 
   const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
   const float scale = (1.0f / sa) * (1.0f / sb);
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, a.ep, m0, n0, wm, wn, lane, tid, scale, stage_ptr);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, kNJ, 64 * kWaves>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
+                                                                       scale, stage_ptr);
 }
 
-constexpr int kWaves = TE_GEMM_WAVES;
-constexpr int kBK = TE_GEMM_FP8_BK;
-constexpr int kStages = TE_GEMM_FP8_STAGES;
-
 template <int ACT, bool GATED>
-hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
+hipError_t launch_flags(const FpArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_fp8_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    if (h) gemm_fp8_kernel<ACT, GATED, false, true, true><<<grid, T, 0, s>>>(a);
+    else gemm_fp8_kernel<ACT, GATED, false, false, true><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_fp8_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    if (out) gemm_fp8_kernel<ACT, GATED, true, true, false><<<grid, T, 0, s>>>(a);
+    else gemm_fp8_kernel<ACT, GATED, false, true, false><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_fp8_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages><<<grid, T, 0, s>>>(a);
+    gemm_fp8_kernel<ACT, GATED, true, false, false><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -198,18 +233,17 @@ hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b, int64_t K,
-                           const float* amax_a, const float* amax_b, const Epilogue& e,
-                           hipStream_t s) {
+                           const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s) {
   LaunchScope scope(e.amax != nullptr ? "gemm_fp8_h_amax" : "gemm_fp8", s);
-  GemmArgs a;
+  FpArgs a;
   a.A = A;
   a.Bt = Bt;
   a.K = (int)K;
   a.amax_a = amax_a;
   a.amax_b = amax_b;
-  a.ep.bias = reinterpret_cast<const uint16_t*>(e.bias);
-  a.ep.out = reinterpret_cast<uint16_t*>(e.out);
-  a.ep.h_out = reinterpret_cast<uint16_t*>(e.h_out);
+  a.ep.bias = static_cast<const uint16_t*>(e.bias);
+  a.ep.out = static_cast<uint16_t*>(e.out);
+  a.ep.h_out = static_cast<uint16_t*>(e.h_out);
   a.ep.amax = e.amax;
   a.ep.M = (int)M;
   a.ep.n_b = (int)n_b;

@@ -21,7 +21,8 @@ def _dense_case(rows, hidden, out, dtype, quant, norm="layernorm", seed=0, bias=
 
 
 @pytest.mark.parametrize("rows,hidden,out", [(1, 16, 16), (300, 272, 400), (257, 80, 528),
-                                             (512, 1024, 768), (64, 4096, 256)])
+                                             (512, 1024, 768), (64, 4096, 256), (2100, 272, 400),
+                                             (2048, 1040, 784), (2305, 80, 16)])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_layernorm_dense(rows, hidden, out, dtype):
     print(f"layernorm_dense {dtype} {rows}x{hidden}->{out}", flush=True)
@@ -91,10 +92,10 @@ def test_mlp_tiny_fp32_workload():
 
 
 @pytest.mark.parametrize("act", MLP_ACTS, ids=["-".join(a) for a in MLP_ACTS])
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_mlp_activations(act, dtype):
-    w = W.Workload("mlp", "mlp", 300, 272, 400, dtype, "none", "layernorm", False, 1e-6, act, True)
-    print(f"layernorm_mlp {dtype} {act} 300x272x400", flush=True)
+@pytest.mark.parametrize("dtype,rows", [("fp32", 300), ("bf16", 300), ("bf16", 2100)])
+def test_mlp_activations(act, dtype, rows):
+    w = W.Workload("mlp", "mlp", rows, 272, 400, dtype, "none", "layernorm", False, 1e-6, act, True)
+    print(f"layernorm_mlp {dtype} {act} {rows}x272x400", flush=True)
     t = W.make_inputs(w, seed=11)
     y, saved = _mlp_gpu(w, to_dev(t), return_saved=True)
     torch.cuda.synchronize()
@@ -108,6 +109,8 @@ def test_mlp_activations(act, dtype):
     ("ln_mlp_gelu_bf16", 513, 512, 1024),
     ("rms_swiglu_bf16", 257, 256, 288),
     ("rms_swiglu_bf16", 512, 1024, 1536),
+    ("ln_mlp_gelu_bf16", 2300, 512, 1040),
+    ("rms_swiglu_bf16", 2049, 256, 288),
 ])
 def test_mlp_bf16_workload_recipes(name, rows, hidden, ffn):
     w = W.WORKLOADS[name].scaled(rows, hidden, ffn)
