@@ -261,19 +261,23 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 }
 
 // ------------------------------------------------------------------ dact + dbias
-// Block = 4 waves over one strip of 512 output columns (8 per lane) and one
-// chunk of rows; wave w takes rows w, w+4, ... of the chunk. Each lane keeps
-// fp32 column sums in registers; the 4 waves are combined in LDS and every
-// block writes one row of fp32 partials, which dbias_finalize sums in a fixed
-// order (bitwise reproducible).
+// Block = 8 waves over one strip of 512 output columns (8 per lane) and one
+// chunk of rows; wave w takes rows w, w+8, ... of the chunk, 4 rows per
+// iteration so that each lane has 8 (gated 12) 16-byte loads in flight. Each
+// lane keeps fp32 column sums in registers; the 8 waves are combined in LDS
+// in a fixed order and every block writes one row of fp32 partials, which
+// dbias_finalize sums in a fixed order (bitwise reproducible).
 constexpr int kDactStrip = 512;
+constexpr int kDactWaves = 8;
+constexpr int kDactUnroll = 4;
 
 template <bool BF16, int ACT, bool GATED>
-__global__ void __launch_bounds__(kThreads) dact_kernel(const void* grad, const void* x, int64_t rows,
-                                                        int64_t cols, int64_t rows_per_chunk,
-                                                        void* dx, float* partials) {
+__global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad, const void* x, int64_t rows,
+                                                               int64_t cols, int64_t rows_per_chunk,
+                                                               void* dx, float* partials) {
   constexpr int G = GATED ? 2 : 1;
-  __shared__ float red[4][G][kDactStrip];
+  constexpr int W = kDactWaves, U = kDactUnroll;
+  __shared__ float red[W][G][kDactStrip];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t col = (int64_t)blockIdx.x * kDactStrip + lane * 8;
   const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
@@ -284,31 +288,42 @@ __global__ void __launch_bounds__(kThreads) dact_kernel(const void* grad, const 
 #pragma unroll
   for (int i = 0; i < 8; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
   if (col < cols) {
-    int64_t r = r_begin + w;
-#pragma unroll 2
-    for (; r < r_end; r += 4) {
-      float g[8], a[8], d[8];
-      load8<BF16>(grad, r * cols + col, g);
-      load8<BF16>(x, r * xcols + col, a);
-      if constexpr (GATED) {
-        float b[8], db[8];
-        load8<BF16>(x, r * xcols + cols + col, b);
+    for (int64_t r0 = r_begin + w; r0 < r_end; r0 += W * U) {
+      float g[U][8], a[U][8], b[U][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          d[i] = g[i] * b[i] * act_bwd<ACT>(a[i]);
-          db[i] = g[i] * act_fwd<ACT>(a[i]);
-          sa[i] += d[i];
-          sb[i] += db[i];
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = r0 + (int64_t)u * W;
+        if (r < r_end) {
+          load8<BF16>(grad, r * cols + col, g[u]);
+          load8<BF16>(x, r * xcols + col, a[u]);
+          if constexpr (GATED) load8<BF16>(x, r * xcols + cols + col, b[u]);
         }
-        store8<BF16>(dx, r * xcols + col, d);
-        store8<BF16>(dx, r * xcols + cols + col, db);
-      } else {
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          d[i] = g[i] * act_bwd<ACT>(a[i]);
-          sa[i] += d[i];
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = r0 + (int64_t)u * W;
+        if (r < r_end) {
+          float d[8];
+          if constexpr (GATED) {
+            float db[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              d[i] = g[u][i] * b[u][i] * act_bwd<ACT>(a[u][i]);
+              db[i] = g[u][i] * act_fwd<ACT>(a[u][i]);
+              sa[i] += d[i];
+              sb[i] += db[i];
+            }
+            store8<BF16>(dx, r * xcols + col, d);
+            store8<BF16>(dx, r * xcols + cols + col, db);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              d[i] = g[u][i] * act_bwd<ACT>(a[u][i]);
+              sa[i] += d[i];
+            }
+            store8<BF16>(dx, r * xcols + col, d);
+          }
         }
-        store8<BF16>(dx, r * xcols + col, d);
       }
     }
   }
@@ -319,12 +334,14 @@ __global__ void __launch_bounds__(kThreads) dact_kernel(const void* grad, const 
     if constexpr (GATED) red[w][G - 1][lane * 8 + i] = sb[i];
   }
   __syncthreads();
-  // 256 threads finalise G*512 columns: fixed order w = 0..3
-  for (int idx = threadIdx.x; idx < G * kDactStrip; idx += kThreads) {
+  // the block's threads finalise G*512 columns: fixed order w = 0..W-1
+  for (int idx = threadIdx.x; idx < G * kDactStrip; idx += 64 * W) {
     const int h = idx / kDactStrip, cl = idx % kDactStrip;
     const int64_t c = (int64_t)blockIdx.x * kDactStrip + cl;
     if (c < cols) {
-      const float s = ((red[0][h][cl] + red[1][h][cl]) + red[2][h][cl]) + red[3][h][cl];
+      float s = red[0][h][cl];
+#pragma unroll
+      for (int k = 1; k < W; ++k) s += red[k][h][cl];
       partials[(int64_t)blockIdx.y * xcols + h * cols + c] = s;
     }
   }
@@ -388,7 +405,8 @@ hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStr
 
 hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s) {
   LaunchScope scope("amax", s);
-  const unsigned grid = min(grid_for(n / 8, kUnroll), 4096u);
+  // one atomic per workgroup on a single address: few workgroups, each looping
+  const unsigned grid = min(grid_for(n / 8, kUnroll), 1024u);
   if (x_dtype == kBF16) amax_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
   else amax_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
   return hipGetLastError();
@@ -454,7 +472,7 @@ hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int6
   const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
   {
     LaunchScope scope("dact_dbias", s);
-#define TE_DACT(B, A, G) dact_kernel<B, A, G><<<grid, kThreads, 0, s>>>(grad, x, rows, cols, rpc, dx, partials)
+#define TE_DACT(B, A, G) dact_kernel<B, A, G><<<grid, 64 * kDactWaves, 0, s>>>(grad, x, rows, cols, rpc, dx, partials)
 #define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);
 #define TE_DACT_A(B)                                   \
   switch (act) {                                       \

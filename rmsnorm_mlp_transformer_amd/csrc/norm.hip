@@ -199,7 +199,10 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
 
 template <bool BF16, int NCH, bool RMS>
 hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s) {
-  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  // one row per wave; the amax pass caps the grid (one atomic per workgroup on
+  // a single address serialises in the L2) and its waves loop over rows
+  const int64_t blocks = (a.rows + 3) / 4;
+  const dim3 grid((unsigned)(mode == kNormAmax && blocks > 1024 ? 1024 : blocks)), block(256);
   if (mode == kNormAmax) {
     norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32><<<grid, block, 0, s>>>(a);
   } else if (mode == kNormQuant) {

@@ -14,6 +14,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4_t;
 
 constexpr int kWave = 64;
 
