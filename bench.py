@@ -105,16 +105,18 @@ class Case:
 
 
 class DactCase:
-    """dact + dbias on grad [M, F] ~ N(0, 1) and a pre-activation h1 [M, F]
-    with the spread of GEMM1's output (N(0, 1.3^2)), both bf16."""
+    """dact + dbias on grad [M, F] ~ N(0, 1) and a pre-activation h1 [M, G*F]
+    with the spread of GEMM1's output (N(0, 1.3^2)), both bf16 (G = 2 for a
+    gated activation)."""
 
     def __init__(self, w: W.Workload, te, dev):
         self.w = w
-        a = W.make_act_inputs(w.rows, w.ffn, gated=False, dtype="bf16", seed=0, std=1.3)
+        g = 2 if w.gated else 1
+        a = W.make_act_inputs(w.rows, w.ffn, gated=w.gated, dtype="bf16", seed=0, std=1.3)
         self.grad = a["grad"].to(dev)
         self.h1 = a["x"].to(dev)
         self.dx = torch.empty_like(self.h1)
-        self.dbias = torch.empty(w.ffn, dtype=torch.float32, device=dev)
+        self.dbias = torch.empty(g * w.ffn, dtype=torch.float32, device=dev)
         act = te.act_type_of(w.activation_type)
         n = te.te_dact_dbias_workspace_size(w.rows, w.ffn, act)
         self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
@@ -127,7 +129,33 @@ class DactCase:
 
     def bytes(self):
         # grad + h1 read, dx written (bf16), dbias written (fp32)
-        return 3 * self.w.rows * self.w.ffn * 2 + self.w.ffn * 4
+        g = 2 if self.w.gated else 1
+        return (1 + 2 * g) * self.w.rows * self.w.ffn * 2 + g * self.w.ffn * 4
+
+
+class DactQuantCase(DactCase):
+    """dact + dbias with dx quantised to E4M3 (current scaling): two passes over
+    grad and h1 (amax, then codes)."""
+
+    def __init__(self, w: W.Workload, te, dev):
+        super().__init__(w, te, dev)
+        g = 2 if w.gated else 1
+        self.codes = torch.empty(w.rows, g * w.ffn, dtype=torch.uint8, device=dev)
+        self.meta = te.Fp8Meta()
+        act = te.act_type_of(w.activation_type)
+        n = te.te_dact_dbias_quantize_workspace_size(w.rows, w.ffn, act)
+        self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        B = te._binding
+
+        def fn():
+            B.te_dact_dbias_quantize(self.grad, self.h1, w.rows, w.ffn, B.TE_BF16, act, self.codes, self.meta,
+                                     self.dbias, B.TE_F32, self.ws, self.ws.numel())
+        self.fn = fn
+
+    def bytes(self):
+        # grad + h1 read in each of the two passes, codes written once, dbias written
+        g = 2 if self.w.gated else 1
+        return 2 * (1 + g) * self.w.rows * self.w.ffn * 2 + g * self.w.rows * self.w.ffn + g * self.w.ffn * 4
 
 
 def time_steps(fn, steps, warmup, te=None):
@@ -163,8 +191,12 @@ def kernel_work(w: W.Workload, name: str):
         if name in ("gemm_bf16_act", "gemm_bf16_gated", "gemm_fp8_h_amax"):
             return 2 * M * H * g * F, "flop", "mfma"
         return 2 * M * F * H, "flop", "mfma"
-    if name == "dact_dbias":
-        return 3 * M * F * 2, "byte", "hbm"
+    if name == "dact_dbias":   # grad [M, F], h1 and dx [M, G*F], bf16
+        return (1 + 2 * g) * M * F * 2, "byte", "hbm"
+    if name == "dact_dbias_amax":   # grad and h1 read
+        return (1 + g) * M * F * 2, "byte", "hbm"
+    if name == "dact_quant":   # grad and h1 read, E4M3 codes [M, G*F] written
+        return (1 + g) * M * F * 2 + g * M * F, "byte", "hbm"
     if name == "norm_fwd":
         return 2 * M * H * 2 + 2 * H * 2, "byte", "hbm"
     return None
@@ -291,17 +323,36 @@ def main():
             log(f"bench part {name}: {pms:.4f} ms, {pv:.1f} TFLOP/s")
             del c
             torch.cuda.empty_cache()
+        # activation backward at the GELU workload's shape and (gated) at the SwiGLU one
+        for pname, wname in (("dact_dbias_gelu_bf16", "ln_mlp_gelu_fp8"), ("dact_dbias_swiglu_bf16", "rms_swiglu_bf16")):
+            dw = W.WORKLOADS[wname]
+            d = DactCase(dw, te, dev)
+            dms, dk = time_steps(d.fn, max(10, args.steps), 3, te)
+            gbs = d.bytes() / (dms / 1e3) / 1e9
+            parts[pname] = {"shape": [dw.rows, (2 if dw.gated else 1) * dw.ffn],
+                            "activation": list(dw.activation_type),
+                            "ms_per_step": round(dms, 4), "GB/s": round(gbs, 1),
+                            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                            "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
+                            "roofline": roofline(dw, {k: v for k, v in dk.items() if k == "dact_dbias"}, "bf16",
+                                                 pname)}
+            log(f"bench part {pname}: {dms:.4f} ms, {gbs:.0f} GB/s")
+            del d
+            torch.cuda.empty_cache()
+        # the quantising variant (fp8 backward), GELU shape
         dw = W.WORKLOADS["ln_mlp_gelu_fp8"]
-        d = DactCase(dw, te, dev)
+        d = DactQuantCase(dw, te, dev)
         dms, dk = time_steps(d.fn, max(10, args.steps), 3, te)
         gbs = d.bytes() / (dms / 1e3) / 1e9
-        parts["dact_dbias_gelu_bf16"] = {"ms_per_step": round(dms, 4), "GB/s": round(gbs, 1),
-                                         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                         "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
-                                         "roofline": roofline(dw, {k: v for k, v in dk.items()
-                                                                   if k == "dact_dbias"}, "bf16",
-                                                              "dact_dbias_gelu_bf16")}
-        log(f"bench part dact_dbias: {dms:.4f} ms, {gbs:.0f} GB/s")
+        parts["dact_dbias_quantize_gelu_bf16"] = {
+            "shape": [dw.rows, dw.ffn], "activation": list(dw.activation_type), "ms_per_step": round(dms, 4),
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
+            "roofline": roofline(dw, {k: v for k, v in dk.items() if k in ("dact_dbias_amax", "dact_quant")},
+                                 "bf16", "dact_dbias_quantize_gelu_bf16")}
+        log(f"bench part dact_dbias_quantize: {dms:.4f} ms, {gbs:.0f} GB/s")
+        del d
+        torch.cuda.empty_cache()
         result["parts"] = parts
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -167,6 +167,25 @@ te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t c
                         void* workspace, size_t workspace_bytes, void* stream);
 size_t te_dact_dbias_workspace_size(int64_t rows, int64_t cols, te_act_type act_type);
 
+/* te_dact_dbias_quantize - the activation backward with the bias reduction
+ * and the activation gradient quantised for the fp8 backward GEMMs ([MLP]
+ * Description: the fused backward's quantize_dact_dbias step returns the
+ * quantised activation gradient together with the bias gradient).
+ * dx is computed in fp32 exactly as in te_dact_dbias; with per-tensor current
+ * scaling amax = max |dx| over the whole tensor (before any rounding), scale
+ * = 448 / amax (1 if amax is 0), dx_codes [rows, G*cols] = E4M3(dx * scale),
+ * and dx_meta (required) receives amax, scale and scale_inv. dbias
+ * (optional, [G*cols] of dbias_dtype) as in te_dact_dbias. grad and x as in
+ * te_dact_dbias. Two passes over grad and x: the scale needs the whole
+ * tensor's amax before the first code is written. rows = 0 zeroes dbias and
+ * sets dx_meta to amax 0, scale 1, scale_inv 1. Workspace:
+ * te_dact_dbias_quantize_workspace_size(). */
+te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols,
+                                 te_dtype dtype, te_act_type act_type, uint8_t* dx_codes,
+                                 const te_fp8_meta* dx_meta, void* dbias, te_dtype dbias_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+size_t te_dact_dbias_quantize_workspace_size(int64_t rows, int64_t cols, te_act_type act_type);
+
 /* te_layernorm_dense_fwd - normalisation followed by a dense layer ([DENSE]
  * Description; Outputs: LayerNorm(x) @ kernel + bias). With
  * TE_QUANT_FP8_E4M3_CURRENT the normalised input and the kernel are both

@@ -79,6 +79,8 @@ _SIGS = {
     "te_act_lu": (_int, [_vp, _i64, _i64, _int, _int, _vp, _int, _meta_p, _vp]),
     "te_dact_dbias": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_workspace_size": (_sz, [_i64, _i64, _int]),
+    "te_dact_dbias_quantize": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _meta_p, _vp, _int, _vp, _sz, _vp]),
+    "te_dact_dbias_quantize_workspace_size": (_sz, [_i64, _i64, _int]),
     "te_layernorm_dense_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f,
                                       _int, _vp, _vp, _sz, _vp]),
     "te_layernorm_dense_fwd_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int]),
@@ -204,6 +206,17 @@ def te_dact_dbias(grad, x, rows, cols, dtype, act_type, dx, dbias, dbias_dtype, 
                   workspace_bytes, stream=None):
     _check(_lib.te_dact_dbias(_ptr(grad), _ptr(x), rows, cols, dtype, act_type, _ptr(dx), _ptr(dbias),
                               dbias_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def te_dact_dbias_quantize_workspace_size(rows, cols, act_type) -> int:
+    return _lib.te_dact_dbias_quantize_workspace_size(rows, cols, act_type)
+
+
+def te_dact_dbias_quantize(grad, x, rows, cols, dtype, act_type, dx_codes, dx_meta: "Fp8Meta", dbias,
+                           dbias_dtype, workspace, workspace_bytes, stream=None):
+    _check(_lib.te_dact_dbias_quantize(_ptr(grad), _ptr(x), rows, cols, dtype, act_type, _ptr(dx_codes),
+                                       ctypes.byref(dx_meta.c()), _ptr(dbias), dbias_dtype, _ptr(workspace),
+                                       workspace_bytes, _stream(stream)))
 
 
 def te_layernorm_dense_fwd_workspace_size(rows, hidden, out_features, dtype, quant) -> int:
@@ -346,6 +359,23 @@ def dact_dbias(grad, x, activation_type, dbias_dtype=torch.float32, with_dbias=T
     te_dact_dbias(g2, x2, rows, cols, _dtype(x2), act, dx, dbias,
                   _dtype(dbias) if dbias is not None else TE_F32, ws, ws.numel())
     return dx.reshape(x.shape), dbias
+
+
+def dact_dbias_quantize(grad, x, activation_type, quantizer: "Fp8Meta", dbias_dtype=torch.float32,
+                        with_dbias=True):
+    """Activation backward with the bias reduction and the activation gradient
+    quantised to E4M3 with current scaling (the quantizer receives amax, scale
+    and scale_inv): returns (dx codes as uint8, dbias)."""
+    act = act_type_of(activation_type)
+    g2, x2 = _flat(grad), _flat(x)
+    rows, cols = g2.shape
+    codes = torch.empty(x2.shape, dtype=torch.uint8, device=x.device)
+    dbias = torch.empty(x2.shape[1], dtype=dbias_dtype, device=x.device) if with_dbias else None
+    nbytes = te_dact_dbias_quantize_workspace_size(rows, cols, act)
+    ws = _workspace(nbytes, x.device)
+    te_dact_dbias_quantize(g2, x2, rows, cols, _dtype(x2), act, codes, quantizer, dbias,
+                           _dtype(dbias) if dbias is not None else TE_F32, ws, ws.numel())
+    return codes.reshape(x.shape), dbias
 
 
 def layernorm_dense(x, kernel, gamma, beta, bias=None, norm_type="layernorm", zero_centered_gamma=False,

@@ -267,14 +267,19 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 // lane keeps fp32 column sums in registers; the 8 waves are combined in LDS
 // in a fixed order and every block writes one row of fp32 partials, which
 // dbias_finalize sums in a fixed order (bitwise reproducible).
+// MODE kDactStore writes dx; kDactAmax writes no dx but the block's max |dx|
+// (fp32, before any rounding) to amax_part[block]; kDactQuant writes the E4M3
+// codes of dx * scale, the scale coming from the finished amax.
 constexpr int kDactStrip = 512;
 constexpr int kDactWaves = 8;
 constexpr int kDactUnroll = 4;
+enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2 };
 
-template <bool BF16, int ACT, bool GATED>
+template <bool BF16, int ACT, bool GATED, int MODE>
 __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad, const void* x, int64_t rows,
                                                                int64_t cols, int64_t rows_per_chunk,
-                                                               void* dx, float* partials) {
+                                                               void* dx, float* partials, float* amax_part,
+                                                               const float* amax) {
   constexpr int G = GATED ? 2 : 1;
   constexpr int W = kDactWaves, U = kDactUnroll;
   __shared__ float red[W][G][kDactStrip];
@@ -284,9 +289,22 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
   int64_t r_end = r_begin + rows_per_chunk;
   if (r_end > rows) r_end = rows;
   const int64_t xcols = G * cols;
-  float sa[8], sb[8];
+  float qscale = 1.0f;
+  if constexpr (MODE == kDactQuant) qscale = fp8_scale_from_amax(*amax);
+  float sa[8], sb[8], m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
+  // one output chunk of 8 values at element offset e: bf16/fp32 dx, or codes
+  auto emit = [&](int64_t e, const float* d) {
+    if constexpr (MODE == kDactStore) {
+      store8<BF16>(dx, e, d);
+    } else if constexpr (MODE == kDactAmax) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(d[i]));
+    } else {
+      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(dx) + e) = encode8(d, qscale);
+    }
+  };
   if (col < cols) {
     for (int64_t r0 = r_begin + w; r0 < r_end; r0 += W * U) {
       float g[U][8], a[U][8], b[U][8];
@@ -313,21 +331,33 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
               sa[i] += d[i];
               sb[i] += db[i];
             }
-            store8<BF16>(dx, r * xcols + col, d);
-            store8<BF16>(dx, r * xcols + cols + col, db);
+            emit(r * xcols + col, d);
+            emit(r * xcols + cols + col, db);
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               d[i] = g[u][i] * act_bwd<ACT>(a[u][i]);
               sa[i] += d[i];
             }
-            store8<BF16>(dx, r * xcols + col, d);
+            emit(r * xcols + col, d);
           }
         }
       }
     }
   }
-  if (partials == nullptr) return;   // no dbias requested (uniform across the block)
+  if constexpr (MODE == kDactAmax) {
+    __shared__ float mred[W];
+    m = wave_max(m);
+    if (lane == 0) mred[w] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float bm = mred[0];
+#pragma unroll
+      for (int k = 1; k < W; ++k) bm = fmaxf(bm, mred[k]);
+      amax_part[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = bm;
+    }
+  }
+  if (MODE == kDactQuant || partials == nullptr) return;   // no dbias (uniform across the block)
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     red[w][0][lane * 8 + i] = sa[i];
@@ -344,6 +374,26 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
       for (int k = 1; k < W; ++k) s += red[k][h][cl];
       partials[(int64_t)blockIdx.y * xcols + h * cols + c] = s;
     }
+  }
+}
+
+// Max over the per-block partial amaxes; writes amax, scale, scale_inv.
+__global__ void __launch_bounds__(kThreads) amax_finalize_kernel(const float* part, int64_t n, float* amax,
+                                                                  float* scale, float* scale_inv) {
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, part[i]);
+  __shared__ float red[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) r = fmaxf(r, red[k]);
+    const float sc = fp8_scale_from_amax(r);
+    *amax = r;
+    *scale = sc;
+    *scale_inv = 1.0f / sc;
   }
 }
 
@@ -464,15 +514,18 @@ int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated) {
   return chunks;
 }
 
-hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
-                             int act, bool gated, void* dx, void* dbias, int dbias_dtype,
-                             float* partials, hipStream_t s) {
+int64_t dact_blocks(int64_t rows, int64_t cols, bool gated) {
+  return ((cols + kDactStrip - 1) / kDactStrip) * dact_row_chunks(rows, cols, gated);
+}
+
+namespace {
+template <int MODE>
+hipError_t dact_dispatch(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype, int act, bool gated,
+                         void* dx, float* partials, float* amax_part, const float* amax, hipStream_t s) {
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
   const int64_t rpc = (rows + chunks - 1) / chunks;
   const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
-  {
-    LaunchScope scope("dact_dbias", s);
-#define TE_DACT(B, A, G) dact_kernel<B, A, G><<<grid, 64 * kDactWaves, 0, s>>>(grad, x, rows, cols, rpc, dx, partials)
+#define TE_DACT(B, A, G) dact_kernel<B, A, G, MODE><<<grid, 64 * kDactWaves, 0, s>>>(grad, x, rows, cols, rpc, dx, partials, amax_part, amax)
 #define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);
 #define TE_DACT_A(B)                                   \
   switch (act) {                                       \
@@ -482,22 +535,60 @@ hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int6
     case kSilu: TE_DACT_G(B, kSilu) break;             \
     default: TE_DACT_G(B, kLinear) break;              \
   }
-    if (dtype == kBF16) { TE_DACT_A(true) } else { TE_DACT_A(false) }
+  if (dtype == kBF16) { TE_DACT_A(true) } else { TE_DACT_A(false) }
 #undef TE_DACT_A
 #undef TE_DACT_G
 #undef TE_DACT
-    const hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t dbias_finalize(const float* partials, int64_t rows, int64_t cols, bool gated, void* dbias,
+                          int dbias_dtype, hipStream_t s) {
+  LaunchScope scope("dbias_finalize", s);
+  const int64_t chunks = dact_row_chunks(rows, cols, gated);
+  const int64_t n = (gated ? 2 : 1) * cols;
+  const unsigned g2 = (unsigned)((n + kThreads - 1) / kThreads);
+  if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
+  else dbias_finalize_kernel<kF32><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                             int act, bool gated, void* dx, void* dbias, int dbias_dtype,
+                             float* partials, hipStream_t s) {
+  {
+    LaunchScope scope("dact_dbias", s);
+    const hipError_t e = dact_dispatch<kDactStore>(grad, x, rows, cols, dtype, act, gated, dx,
+                                                   dbias != nullptr ? partials : nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  if (dbias != nullptr) return dbias_finalize(partials, rows, cols, gated, dbias, dbias_dtype, s);
+  return hipSuccess;
+}
+
+hipError_t launch_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                                      int act, bool gated, uint8_t* codes, float* amax, float* scale,
+                                      float* scale_inv, void* dbias, int dbias_dtype, float* partials,
+                                      float* amax_part, hipStream_t s) {
+  {
+    LaunchScope scope("dact_dbias_amax", s);
+    const hipError_t e = dact_dispatch<kDactAmax>(grad, x, rows, cols, dtype, act, gated, nullptr,
+                                                  dbias != nullptr ? partials : nullptr, amax_part, nullptr, s);
     if (e != hipSuccess) return e;
   }
   if (dbias != nullptr) {
-    LaunchScope scope("dbias_finalize", s);
-    const int64_t n = (gated ? 2 : 1) * cols;
-    const unsigned g2 = (unsigned)((n + kThreads - 1) / kThreads);
-    if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
-    else dbias_finalize_kernel<kF32><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
-    return hipGetLastError();
+    const hipError_t e = dbias_finalize(partials, rows, cols, gated, dbias, dbias_dtype, s);
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  {
+    LaunchScope scope("amax_finalize", s);
+    amax_finalize_kernel<<<1, kThreads, 0, s>>>(amax_part, dact_blocks(rows, cols, gated), amax, scale, scale_inv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  LaunchScope scope("dact_quant", s);
+  return dact_dispatch<kDactQuant>(grad, x, rows, cols, dtype, act, gated, codes, nullptr, nullptr, amax, s);
 }
 
 }  // namespace te

@@ -360,6 +360,47 @@ te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t c
   return ok();
 }
 
+size_t te_dact_dbias_quantize_workspace_size(int64_t rows, int64_t cols, te_act_type act_type) {
+  if (rows <= 0 || cols <= 0) return 0;
+  const bool g = is_gated(act_type);
+  Carver c(nullptr);
+  c.floats((size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols);
+  c.floats((size_t)te::dact_blocks(rows, cols, g));
+  return c.off;
+}
+
+te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
+                                 te_act_type act_type, uint8_t* dx_codes, const te_fp8_meta* dx_meta, void* dbias,
+                                 te_dtype dbias_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
+  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(meta_ok(dx_meta), "dx_meta with amax, scale and scale_inv is required");
+  TE_ARG((grad != nullptr && x != nullptr && dx_codes != nullptr) || rows == 0, "grad, x and dx_codes are required");
+  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx_codes) && (dbias == nullptr || aligned16(dbias)),
+         "pointers must be 16-byte aligned");
+  const size_t need = te_dact_dbias_quantize_workspace_size(rows, cols, act_type);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
+  hipStream_t s = as_stream(stream);
+  const bool g = is_gated(act_type);
+  if (rows == 0) {   // empty: zero bias gradient, meta of an empty tensor
+    if (dbias != nullptr) TE_HIP(te::launch_fill_zero_bytes(dbias, (g ? 2 : 1) * cols * (int64_t)esize(dbias_dtype), s), "fill");
+    TE_HIP(te::launch_empty_meta(dx_meta->amax, dx_meta->scale, dx_meta->scale_inv, s), "meta");
+    return ok();
+  }
+  Carver c(workspace);
+  float* partials = c.floats((size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols);
+  float* amax_part = c.floats((size_t)te::dact_blocks(rows, cols, g));
+  TE_HIP(te::launch_dact_dbias_quantize(grad, x, rows, cols, dtype, act_kind(act_type), g, dx_codes, dx_meta->amax,
+                                        dx_meta->scale, dx_meta->scale_inv, dbias, dbias_dtype, partials, amax_part, s),
+         "dact_dbias_quantize");
+  return ok();
+}
+
 // ---------------------------------------------------------------- quantiser
 te_status te_quantize(const void* x, int64_t n, te_dtype x_dtype, uint8_t* codes, const te_fp8_meta* meta,
                       void* stream) {

@@ -65,9 +65,19 @@ hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, in
 
 // dact + dbias. partials: fp32 workspace of dact_partials_floats() floats.
 int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated);
+// Number of dact workgroups (one partial amax each in the quantising variant).
+int64_t dact_blocks(int64_t rows, int64_t cols, bool gated);
 hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,
                              int dtype, int act, bool gated, void* dx, void* dbias,
                              int dbias_dtype, float* partials, hipStream_t s);
+// dact + dbias with the activation gradient quantised to E4M3 (current
+// scaling): pass 1 computes dx for the bias partials and per-workgroup amax
+// partials (amax_part: dact_blocks() floats), a one-workgroup kernel reduces
+// them into amax / scale / scale_inv, pass 2 recomputes dx and writes codes.
+hipError_t launch_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                                      int act, bool gated, uint8_t* codes, float* amax, float* scale,
+                                      float* scale_inv, void* dbias, int dbias_dtype, float* partials,
+                                      float* amax_part, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMMs
 // Epilogue applied to h = acc * scale + bias (scale = 1 unless fp8):

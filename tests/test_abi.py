@@ -154,6 +154,17 @@ def test_norm_act_dact_quant_validation():
         == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_dact_dbias(P, P, 0, 32, B.TE_BF16, B.TE_ACT_SWIGLU, P, None, B.TE_F32, None, 0, None) \
         == B.TE_SUCCESS
+    # quantised dact
+    needq = lib.te_dact_dbias_quantize_workspace_size(64, 32, B.TE_ACT_GELU)
+    assert needq > need
+    assert lib.te_dact_dbias_quantize(P, P, 64, 32, B.TE_BF16, B.TE_ACT_GELU, P, ctypes.byref(m), P, B.TE_F32, P,
+                                      needq - 1, None) == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.te_dact_dbias_quantize(P, P, 64, 32, B.TE_BF16, B.TE_ACT_GELU, P, None, P, B.TE_F32, P, needq,
+                                      None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_dact_dbias_quantize(P, P, 64, 24, B.TE_BF16, B.TE_ACT_GELU, P, ctypes.byref(m), P, B.TE_F32, P,
+                                      needq, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_dact_dbias_quantize(P, P, 64, 32, B.TE_E4M3, B.TE_ACT_GELU, P, ctypes.byref(m), P, B.TE_F32, P,
+                                      needq, None) == B.TE_ERR_INVALID_ARGUMENT
     # quantiser
     assert lib.te_quantize(P, 24, B.TE_BF16, P, ctypes.byref(m), None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_quantize(P, 32, B.TE_BF16, P, None, None) == B.TE_ERR_INVALID_ARGUMENT

@@ -11,8 +11,8 @@ import torch
 import oracle as O
 import rmsnorm_mlp_transformer_amd as te
 import workloads as W
-from gpu_util import (ACT_CODE_ONE_STEP_MAX, CODE_ONE_STEP_MAX, TOL, assert_rel, check_codes_combined,
-                      codes_np, dev, f64, to_dev)
+from gpu_util import (ACT_CODE_ONE_STEP_MAX, CODE_ONE_STEP_MAX, TOL, assert_rel, check_codes,
+                      check_codes_combined, codes_np, dev, f64, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,4 +107,48 @@ def test_full_dact_dbias():
     rows = sample_rows(w.rows)
     rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), ("gelu",))
     assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx[rows], TOL["bf16"], "dx")
+    assert_rel(f64(db), rdb, 1e-5, "dbias")
+
+
+def test_full_dact_dbias_swiglu():
+    """Gated (silu, linear) at the RMSNorm-SwiGLU shape: grad [8192, 14336],
+    pre-activation [8192, 2 x 14336]."""
+    w = W.WORKLOADS["rms_swiglu_bf16"]
+    print("full dact_dbias 8192x2x14336 swiglu", flush=True)
+    a = W.make_act_inputs(w.rows, w.ffn, gated=True, dtype="bf16", seed=0, std=1.3)
+    gd, xd = a["grad"].to(dev()), a["x"].to(dev())
+    dx, db = te.dact_dbias(gd, xd, ("silu", "linear"))
+    torch.cuda.synchronize()
+    rows = sample_rows(w.rows)
+    rdx, rdb = O.dact_dbias(_f64_rows(a["grad"], rows), _f64_rows(a["x"], rows), ("silu", "linear"))
+    assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx, TOL["bf16"], "dx")
+    # dbias over all rows, in column blocks (the same columns of both halves)
+    # to bound the oracle's memory
+    F = w.ffn
+    for c0 in range(0, F, 2048):
+        c1 = min(c0 + 2048, F)
+        n = c1 - c0
+        xab = np.concatenate([f64(a["x"][:, c0:c1]), f64(a["x"][:, F + c0:F + c1])], axis=1)
+        ref = O.dact_dbias(f64(a["grad"][:, c0:c1]), xab, ("silu", "linear"))[1]
+        assert_rel(f64(db[c0:c1]), ref[:n], 1e-5, f"dbias a[{c0}:{c1}]")
+        assert_rel(f64(db[F + c0:F + c1]), ref[n:], 1e-5, f"dbias b[{c0}:{c1}]")
+
+
+def test_full_dact_dbias_quantize():
+    """quantize_dact_dbias at 8192 x 16384 (GELU): amax over the whole dx, codes
+    of sampled rows, dbias over all rows."""
+    w = W.WORKLOADS["ln_mlp_gelu_fp8"]
+    print("full dact_dbias_quantize 8192x16384 gelu", flush=True)
+    a = W.make_act_inputs(w.rows, w.ffn, gated=False, dtype="bf16", seed=0, std=1.3)
+    gd, xd = a["grad"].to(dev()), a["x"].to(dev())
+    q = te.Fp8Meta()
+    codes, db = te.dact_dbias_quantize(gd, xd, ("gelu",), q)
+    torch.cuda.synchronize()
+    rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), ("gelu",))
+    meta = O.current_scaling(rdx)
+    m = q.values()
+    assert abs(m["amax"] - meta["amax"]) <= 1e-5 * meta["amax"]
+    rows = sample_rows(w.rows)
+    rq, _ = O.quantize(rdx[rows], meta)
+    check_codes(codes_np(codes[torch.as_tensor(rows, device=dev())]), rq, "dx codes (sampled rows)")
     assert_rel(f64(db), rdb, 1e-5, "dbias")

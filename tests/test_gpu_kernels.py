@@ -172,6 +172,44 @@ def test_dact_dbias_matches_oracle(act, rows, cols, dtype):
     assert torch.equal(dx, dx2) and torch.equal(db, db2), "not bitwise reproducible"
 
 
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (37, 272), (1000, 1536)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dact_dbias_quantize_matches_oracle(act, rows, cols, dtype):
+    """quantize_dact_dbias: E4M3 codes of dx under current scaling, its meta, and dbias."""
+    print(f"dact_dbias_quantize {act} {dtype} {rows}x{cols}", flush=True)
+    a = W.make_act_inputs(rows, cols, len(act) == 2, dtype, seed=cols + 1)
+    g, x = a["grad"].to(dev()), a["x"].to(dev())
+    q = te.Fp8Meta()
+    codes, db = te.dact_dbias_quantize(g, x, act, q)
+    codes2, db2 = te.dact_dbias_quantize(g, x, act, q)
+    dx_ref, _ = te.dact_dbias(g, x, act, with_dbias=False)
+    torch.cuda.synchronize()
+    rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), act)
+    rq, rm = O.quantize(rdx)
+    m = q.values()
+    assert abs(m["amax"] - rm["amax"]) <= 1e-5 * rm["amax"], (m, rm)
+    assert m["scale"] == float(np.float32(448.0) / np.float32(m["amax"]))
+    assert m["scale_inv"] == float(np.float32(1.0) / np.float32(m["scale"]))
+    check_codes(codes_np(codes), rq, "dx codes")
+    assert_rel(f64(db), rdb, 1e-5, "dbias fp32")
+    assert torch.equal(codes, codes2) and torch.equal(db, db2), "not bitwise reproducible"
+    # the unquantised pass and the quantising passes agree on dbias bit for bit
+    assert torch.equal(db, te.dact_dbias(g, x, act)[1])
+    assert dx_ref.shape == codes.shape
+
+
+def test_dact_dbias_quantize_zero_rows():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev())
+    q = te.Fp8Meta()
+    q.buf.fill_(7.0)
+    codes, db = te.dact_dbias_quantize(torch.empty(0, 32, dtype=torch.bfloat16, device=dev()), x,
+                                       ("silu", "linear"), q)
+    torch.cuda.synchronize()
+    assert codes.shape == (0, 64) and db.shape == (64,) and not db.any()
+    assert q.values() == {"amax": 0.0, "scale": 1.0, "scale_inv": 1.0}
+
+
 def test_empty_rows_is_a_no_op():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev())
     y = te.activation(x, ("gelu",))
