@@ -186,6 +186,40 @@ def normalize(x, gamma, beta, norm_type: str, epsilon: float, zero_centered_gamm
     raise ValueError(f"unknown norm_type {norm_type!r}")
 
 
+def norm_bwd(dy, x, gamma, norm_type: str, epsilon: float, zero_centered_gamma: bool = False):
+    """Gradients of the normalization ([DENSE] Description: the backward pass
+    gives the gradients of every input, x, gamma and beta among them, from the
+    saved forward context). With xhat the normalized input (before g and
+    beta), rs = 1 / sqrt(var + eps) (LayerNorm) or 1 / sqrt(mean(x^2) + eps)
+    (RMSNorm) and dxhat = dy * g:
+      LayerNorm: dx = rs * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat))
+      RMSNorm:   dx = rs * (dxhat - xhat * mean(dxhat * xhat))
+      dgamma = sum over rows of dy * xhat (also for a zero-centred gamma, whose
+      scale 1 + gamma has the same derivative); dbeta = sum over rows of dy
+      (LayerNorm only). The statistics are recomputed here from x.
+    Returns (dx, dgamma, dbeta); dbeta is None for RMSNorm."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    g = effective_gamma(gamma, zero_centered_gamma)
+    if norm_type == "layernorm":
+        mu = x.mean(axis=-1, keepdims=True)
+        rs = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + epsilon)
+        xhat = (x - mu) * rs
+    elif norm_type == "rmsnorm":
+        rs = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + epsilon)
+        xhat = x * rs
+    else:
+        raise ValueError(f"unknown norm_type {norm_type!r}")
+    dxhat = dy * g
+    inner = dxhat - xhat * (dxhat * xhat).mean(axis=-1, keepdims=True)
+    if norm_type == "layernorm":
+        inner = inner - dxhat.mean(axis=-1, keepdims=True)
+    dx = rs * inner
+    dgamma = (dy * xhat).reshape(-1, x.shape[-1]).sum(axis=0)
+    dbeta = dy.reshape(-1, x.shape[-1]).sum(axis=0) if norm_type == "layernorm" else None
+    return dx, dgamma, dbeta
+
+
 # --------------------------------------------------------------------------
 # Activations ([ACT] Overview: GELU, SiLU, ReLU; Inputs: activation_type such
 # as ("gelu",) or the gated pair ("silu", "linear"))

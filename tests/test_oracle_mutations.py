@@ -136,6 +136,27 @@ def _bf16_truncate(a):
     return np.where(a == 0, a, np.trunc(a / q) * q)
 
 
+_orig_norm_bwd = T.norm_bwd
+
+
+def _norm_bwd_dropped_mean(dy, x, gamma, norm_type, epsilon, zero_centered_gamma=False):
+    dy = np.asarray(dy, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    if norm_type != "layernorm":
+        return _orig_norm_bwd(dy, x, gamma, norm_type, epsilon, zero_centered_gamma)
+    mu = x.mean(axis=-1, keepdims=True)
+    rs = 1.0 / np.sqrt(((x - mu) ** 2).mean(axis=-1, keepdims=True) + epsilon)
+    xhat = (x - mu) * rs
+    dxhat = dy * T.effective_gamma(gamma, zero_centered_gamma)
+    dx = rs * (dxhat - xhat * (dxhat * xhat).mean(axis=-1, keepdims=True))
+    return dx, (dy * xhat).sum(axis=0), dy.sum(axis=0)
+
+
+def _norm_bwd_dgamma_from_x(dy, x, gamma, norm_type, epsilon, zero_centered_gamma=False):
+    dx, _, dbeta = _orig_norm_bwd(dy, x, gamma, norm_type, epsilon, zero_centered_gamma)
+    return dx, (np.asarray(dy) * np.asarray(x)).sum(axis=0), dbeta
+
+
 MUTANTS = [
     ("layernorm", _ln_unbiased, [P.test_layernorm_invariants_closed_form_variance, P.test_layernorm_brute_force]),
     ("layernorm", _ln_eps_outside, [P.test_layernorm_brute_force]),
@@ -152,6 +173,9 @@ MUTANTS = [
     ("dact_dbias", _dact_no_gate, [lambda: P.test_gated_dact_central_differences(("silu", "linear"))]),
     ("effective_gamma", _zcg_ignored, [P.test_zero_centered_gamma_equivalence]),
     ("bf16_round", _bf16_truncate, [P.test_bf16_round_matches_torch_cast]),
+    ("norm_bwd", _norm_bwd_dropped_mean, [P.test_layernorm_bwd_dx_sums_to_zero_per_row,
+                                          lambda: P.test_norm_bwd_central_differences("layernorm", False)]),
+    ("norm_bwd", _norm_bwd_dgamma_from_x, [lambda: P.test_norm_bwd_central_differences("rmsnorm", True)]),
 ]
 
 

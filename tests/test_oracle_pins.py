@@ -394,3 +394,67 @@ def test_round_intermediates_is_close_to_exact():
 def test_rel_l2():
     assert O.rel_l2([3.0, 4.0], [3.0, 4.0]) == 0.0
     assert abs(O.rel_l2([3.0, 5.0], [3.0, 4.0]) - 0.2) < 1e-15
+
+
+# ---- norm backward: finite differences of the (pinned) forward, invariants
+
+def _norm_fwd_sum(dy, x, gamma, beta, norm_type, eps, zcg):
+    y = O.normalize(x, gamma, beta, norm_type, eps, zcg)[0]
+    return float(np.sum(dy * y))
+
+
+@pytest.mark.parametrize("norm_type", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("zcg", [False, True])
+def test_norm_bwd_central_differences(norm_type, zcg):
+    rows, h, eps = 3, 8, 1e-3
+    x = RNG.standard_normal((rows, h)) * 1.5 + 0.3
+    gamma = RNG.standard_normal(h) * 0.3 + (0.0 if zcg else 1.0)
+    beta = RNG.standard_normal(h) * 0.1
+    dy = RNG.standard_normal((rows, h))
+    dx, dgamma, dbeta = O.norm_bwd(dy, x, gamma, norm_type, eps, zcg)
+    d = 1e-6
+
+    def fd(arr, idx):
+        ap, am = arr.copy(), arr.copy()
+        ap[idx] += d
+        am[idx] -= d
+        return ap, am
+
+    for i, j in itertools.product(range(rows), range(h)):
+        xp, xm = fd(x, (i, j))
+        g = (_norm_fwd_sum(dy, xp, gamma, beta, norm_type, eps, zcg)
+             - _norm_fwd_sum(dy, xm, gamma, beta, norm_type, eps, zcg)) / (2 * d)
+        assert abs(dx[i, j] - g) <= 1e-6 * max(1.0, abs(g)), (i, j, dx[i, j], g)
+    for j in range(h):
+        gp, gm = fd(gamma, j)
+        g = (_norm_fwd_sum(dy, x, gp, beta, norm_type, eps, zcg) - _norm_fwd_sum(dy, x, gm, beta, norm_type, eps, zcg)) / (2 * d)
+        assert abs(dgamma[j] - g) <= 1e-6 * max(1.0, abs(g))
+        if norm_type == "layernorm":
+            bp, bm = fd(beta, j)
+            g = (_norm_fwd_sum(dy, x, gamma, bp, norm_type, eps, zcg)
+                 - _norm_fwd_sum(dy, x, gamma, bm, norm_type, eps, zcg)) / (2 * d)
+            assert abs(dbeta[j] - g) <= 1e-6 * max(1.0, abs(g))
+    if norm_type == "rmsnorm":
+        assert dbeta is None
+
+
+def test_layernorm_bwd_dx_sums_to_zero_per_row():
+    # shifting a row by a constant leaves LayerNorm unchanged, so dx has zero row sums
+    x = RNG.standard_normal((5, 64)) * 2.0 + 1.0
+    dx = O.norm_bwd(RNG.standard_normal((5, 64)), x, RNG.standard_normal(64), "layernorm", 1e-5)[0]
+    assert np.max(np.abs(dx.sum(axis=-1))) <= 1e-12 * np.max(np.abs(dx)) * 64
+
+
+def test_rmsnorm_bwd_dx_orthogonal_to_x_when_eps_is_zero():
+    # with eps = 0 RMSNorm is invariant to scaling the row, so dx . x = 0
+    x = RNG.standard_normal((4, 32))
+    dx = O.norm_bwd(RNG.standard_normal((4, 32)), x, RNG.standard_normal(32), "rmsnorm", 0.0)[0]
+    assert np.max(np.abs((dx * x).sum(axis=-1))) <= 1e-12 * np.max(np.abs(dx)) * 32
+
+
+def test_norm_bwd_zero_centered_gamma_equivalence():
+    x, dy, gamma = RNG.standard_normal((3, 16)), RNG.standard_normal((3, 16)), RNG.standard_normal(16) * 0.1
+    for nt in ("layernorm", "rmsnorm"):
+        a = O.norm_bwd(dy, x, gamma, nt, 1e-6, True)
+        b = O.norm_bwd(dy, x, 1.0 + gamma, nt, 1e-6, False)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
