@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "gemm_bf16_act": _GEMM, "gemm_bf16": _GEMM, "gemm_bf16_gated": _GEMM, "gemm_fp8_h_amax": _GEMM,
     "gemm_fp8": _GEMM,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
+    "norm_bwd": ["norm_bwd.hip", "te_common.hpp"],
 }
 # Counter-measured HBM bytes per launch: {(workload, kernel): (bytes, source hash)}.
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summaries are
@@ -158,6 +159,36 @@ class DactQuantCase(DactCase):
         return 2 * (1 + g) * self.w.rows * self.w.ffn * 2 + g * self.w.rows * self.w.ffn + g * self.w.ffn * 4
 
 
+class NormBwdCase:
+    """LayerNorm backward at the bench workload's normalisation shape: dy, x
+    (bf16) and the forward's saved mu / rsigma -> dx, dgamma, dbeta (fp32)."""
+
+    def __init__(self, w: W.Workload, te, dev):
+        self.w = w
+        t = W.make_inputs(w)
+        gen = torch.Generator(device="cpu").manual_seed(5)
+        self.dy = torch.randn(w.rows, w.hidden, generator=gen).to(torch.bfloat16).to(dev)
+        self.x, self.gamma = t["x"].to(dev), t["gamma"].to(dev)
+        beta = t["beta"].to(dev)
+        _, self.mu, self.rs = te.layernorm(self.x, self.gamma, beta, "layernorm", False, w.epsilon, return_stats=True)
+        self.dx = torch.empty_like(self.x)
+        self.dg = torch.empty(w.hidden, dtype=torch.float32, device=dev)
+        self.db = torch.empty(w.hidden, dtype=torch.float32, device=dev)
+        B = te._binding
+        n = B.te_layernorm_bwd_workspace_size(w.rows, w.hidden, B.TE_BF16)
+        self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+
+        def fn():
+            B.te_layernorm_bwd(self.dy, self.x, self.mu, self.rs, self.gamma, w.rows, w.hidden, B.TE_BF16,
+                               B.TE_LAYERNORM, 0, self.dx, self.dg, self.db, B.TE_F32, self.ws, self.ws.numel())
+        self.fn = fn
+
+    def bytes(self):
+        # dy and x read, dx written (bf16); mu, rsigma read; dgamma, dbeta written
+        M, H = self.w.rows, self.w.hidden
+        return 3 * M * H * 2 + 2 * M * 4 + 2 * H * 4
+
+
 def time_steps(fn, steps, warmup, te=None):
     for _ in range(warmup):
         fn()
@@ -193,6 +224,8 @@ def kernel_work(w: W.Workload, name: str):
         return 2 * M * F * H, "flop", "mfma"
     if name == "dact_dbias":   # grad [M, F], h1 and dx [M, G*F], bf16
         return (1 + 2 * g) * M * F * 2, "byte", "hbm"
+    if name == "norm_bwd":   # dy, x read and dx written (bf16), mu and rsigma read
+        return 3 * M * H * 2 + 2 * M * 4, "byte", "hbm"
     if name == "dact_dbias_amax":   # grad and h1 read
         return (1 + g) * M * F * 2, "byte", "hbm"
     if name == "dact_quant":   # grad and h1 read, E4M3 codes [M, G*F] written
@@ -339,6 +372,19 @@ def main():
             log(f"bench part {pname}: {dms:.4f} ms, {gbs:.0f} GB/s")
             del d
             torch.cuda.empty_cache()
+        # normalisation backward at the bench workload's shape
+        nw = W.WORKLOADS["ln_mlp_gelu_bf16"]
+        nbc = NormBwdCase(nw, te, dev)
+        nms, nk = time_steps(nbc.fn, max(10, args.steps), 3, te)
+        gbs = nbc.bytes() / (nms / 1e3) / 1e9
+        parts["norm_bwd_ln_bf16"] = {
+            "shape": [nw.rows, nw.hidden], "ms_per_step": round(nms, 4), "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in nk.items()},
+            "roofline": roofline(nw, {k: v for k, v in nk.items() if k == "norm_bwd"}, "bf16", "norm_bwd_ln_bf16")}
+        log(f"bench part norm_bwd: {nms:.4f} ms, {gbs:.0f} GB/s")
+        del nbc
+        torch.cuda.empty_cache()
         # the quantising variant (fp8 backward), GELU shape
         dw = W.WORKLOADS["ln_mlp_gelu_fp8"]
         d = DactQuantCase(dw, te, dev)

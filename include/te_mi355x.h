@@ -137,6 +137,28 @@ te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta,
 size_t te_layernorm_fwd_workspace_size(int64_t rows, int64_t hidden, te_dtype x_dtype,
                                        te_dtype y_dtype);
 
+/* te_layernorm_bwd - gradients of the normalisation step ([DENSE]
+ * Description: the backward pass gives the gradients of every input, x,
+ * gamma and beta among them, from the saved forward context).
+ * With xhat = (x - mu) * rsigma (RMSNorm: x * rsigma), g = gamma (1 + gamma
+ * when zero_centered_gamma != 0) and dxhat = dy * g:
+ *   LayerNorm: dx = rsigma * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat))
+ *   RMSNorm:   dx = rsigma * (dxhat - xhat * mean(dxhat * xhat))
+ *   dgamma = sum over rows of dy * xhat; dbeta = sum over rows of dy
+ *   (LayerNorm only; ignored and not written for RMSNorm).
+ * dy, x, dx: [rows, hidden] of dtype (F32 or BF16); gamma: [hidden] of dtype;
+ * mu (LayerNorm) and rsigma: [rows] fp32 as te_layernorm_fwd saved them.
+ * dgamma, dbeta: optional [hidden] of dparam_dtype (F32 or BF16), summed in
+ * fp32 in a fixed order (bitwise reproducible). hidden is at most 16384 (bf16)
+ * / 8192 (fp32), else TE_ERR_UNSUPPORTED. rows = 0 zeroes dgamma and dbeta.
+ * Workspace (needed with dgamma or dbeta): te_layernorm_bwd_workspace_size(). */
+te_status te_layernorm_bwd(const void* dy, const void* x, const float* mu, const float* rsigma,
+                           const void* gamma, int64_t rows, int64_t hidden, te_dtype dtype,
+                           te_norm_type norm_type, int zero_centered_gamma, void* dx,
+                           void* dgamma, void* dbeta, te_dtype dparam_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+size_t te_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden, te_dtype dtype);
+
 /* te_act_lu - activation forward with optional fp8 output ([ACT]
  * Description: the forward applies the activation with optional
  * quantisation; Outputs: the activated tensor).

@@ -76,6 +76,9 @@ _SIGS = {
     "te_layernorm_fwd": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _f, _vp, _int, _meta_p,
                                 _vp, _vp, _vp, _sz, _vp]),
     "te_layernorm_fwd_workspace_size": (_sz, [_i64, _i64, _int, _int]),
+    "te_layernorm_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _int,
+                                _vp, _sz, _vp]),
+    "te_layernorm_bwd_workspace_size": (_sz, [_i64, _i64, _int]),
     "te_act_lu": (_int, [_vp, _i64, _i64, _int, _int, _vp, _int, _meta_p, _vp]),
     "te_dact_dbias": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_workspace_size": (_sz, [_i64, _i64, _int]),
@@ -191,6 +194,17 @@ def te_layernorm_fwd(x, gamma, beta, rows, hidden, x_dtype, norm_type, zero_cent
                                  int(zero_centered_gamma), float(epsilon), _ptr(y), y_dtype,
                                  ctypes.byref(y_meta.c()) if y_meta is not None else None,
                                  _ptr(mu), _ptr(rsigma), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def te_layernorm_bwd_workspace_size(rows, hidden, dtype) -> int:
+    return _lib.te_layernorm_bwd_workspace_size(rows, hidden, dtype)
+
+
+def te_layernorm_bwd(dy, x, mu, rsigma, gamma, rows, hidden, dtype, norm_type, zero_centered_gamma, dx, dgamma,
+                     dbeta, dparam_dtype, workspace, workspace_bytes, stream=None):
+    _check(_lib.te_layernorm_bwd(_ptr(dy), _ptr(x), _ptr(mu), _ptr(rsigma), _ptr(gamma), rows, hidden, dtype,
+                                 norm_type, int(zero_centered_gamma), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                 dparam_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def te_act_lu(x, rows, cols, x_dtype, act_type, y, y_dtype, y_meta=None, stream=None):
@@ -313,6 +327,23 @@ def layernorm(x, gamma, beta=None, norm_type="layernorm", zero_centered_gamma=Fa
                      epsilon, y, yd, quantizer, mu, rs)
     y = y.reshape(x.shape)
     return (y, mu, rs) if return_stats else y
+
+
+def layernorm_bwd(dy, x, mu, rsigma, gamma, norm_type="layernorm", zero_centered_gamma=False,
+                  dparam_dtype=torch.float32, with_params=True):
+    """Gradients of the normalisation from the forward's saved mu / rsigma:
+    returns (dx, dgamma, dbeta); dbeta is None for RMSNorm."""
+    dy2, x2 = _flat(dy), _flat(x)
+    rows, hidden = x2.shape
+    dx = torch.empty_like(x2)
+    dgamma = torch.empty(hidden, dtype=dparam_dtype, device=x.device) if with_params else None
+    dbeta = (torch.empty(hidden, dtype=dparam_dtype, device=x.device)
+             if with_params and norm_type == "layernorm" else None)
+    nbytes = te_layernorm_bwd_workspace_size(rows, hidden, _dtype(x2))
+    ws = _workspace(nbytes, x.device)
+    te_layernorm_bwd(dy2, x2, mu, rsigma, gamma, rows, hidden, _dtype(x2), _NORM[norm_type], zero_centered_gamma,
+                     dx, dgamma, dbeta, _dtype(dgamma) if dgamma is not None else TE_F32, ws, ws.numel())
+    return dx.reshape(x.shape), dgamma, dbeta
 
 
 def activation(x, activation_type, quantizer: Optional[Fp8Meta] = None, act_params=None):

@@ -402,8 +402,18 @@ __global__ void __launch_bounds__(kThreads) dbias_finalize_kernel(const float* p
                                                                   int64_t n, void* dbias) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= n) return;
+  // 8 loads in flight per lane; the sum still runs over k = 0, 1, 2, ... in order
+  constexpr int U = 8;
   float s = 0.0f;
-  for (int64_t k = 0; k < chunks; ++k) s += partials[k * n + c];
+  int64_t k = 0;
+  for (; k + U <= chunks; k += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = partials[(k + u) * n + c];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  for (; k < chunks; ++k) s += partials[k * n + c];
   if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(dbias)[c] = f32_to_bf16(s);
   else reinterpret_cast<float*>(dbias)[c] = s;
 }

@@ -1,0 +1,265 @@
+// Row-wise LayerNorm / RMSNorm backward for gfx950: dx, dgamma and dbeta from
+// dy, x and the forward's saved statistics ("NVIDIA TransformerEngine JAX
+// LayerNorm Dense", Description: the backward pass gives the gradients of
+// every input, x, gamma and beta among them, from the saved forward context).
+//
+// With xhat = (x - mean) * rsigma (RMSNorm: x * rsigma), g = gamma or
+// 1 + gamma, and dxhat = dy * g:
+//   LayerNorm: dx = rsigma * (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat))
+//   RMSNorm:   dx = rsigma * (dxhat - xhat * mean(dxhat * xhat))
+//   dgamma = sum over rows of dy * xhat, dbeta = sum over rows of dy.
+//
+// A workgroup of 16 waves is split into teams of TW waves; a team owns one
+// row at a time, each lane holding two 16-byte chunks of it (so a row of
+// up to 2 * 64 * TW chunks). The two row means are reduced across the team
+// through LDS (one barrier per row, double-buffered). The column sums for
+// dgamma and dbeta stay in registers across the workgroup's rows; at the end
+// the teams add theirs in a fixed order through LDS and the workgroup writes
+// one row of fp32 partials, which a second kernel sums over the workgroups
+// in a fixed order (bitwise reproducible).
+#include "te_common.hpp"
+#include "te_kernels.hpp"
+
+namespace te {
+namespace {
+
+constexpr int kBwdWaves = 16;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdColFloats = 30720;          // LDS for the teams' column sums (120 KiB)
+
+template <bool BF16>
+struct Chunk {
+  static constexpr int VEC = BF16 ? 8 : 4;    // elements per 16-byte chunk
+  static __device__ __forceinline__ void unpack(const uint4& c, float* f) {
+    if constexpr (BF16) {
+      f[0] = bf16_lo(c.x); f[1] = bf16_hi(c.x); f[2] = bf16_lo(c.y); f[3] = bf16_hi(c.y);
+      f[4] = bf16_lo(c.z); f[5] = bf16_hi(c.z); f[6] = bf16_lo(c.w); f[7] = bf16_hi(c.w);
+    } else {
+      f[0] = __uint_as_float(c.x); f[1] = __uint_as_float(c.y);
+      f[2] = __uint_as_float(c.z); f[3] = __uint_as_float(c.w);
+    }
+  }
+  static __device__ __forceinline__ uint4 pack(const float* f) {
+    if constexpr (BF16) {
+      return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                        pack_bf16x2(f[6], f[7]));
+    } else {
+      return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+  }
+};
+
+struct BwdArgs {
+  const void* dy; const void* x; const float* mu; const float* rsigma; const void* gamma;
+  int64_t rows, hidden; int zcg; int tw;      // waves per team (1, 2, 4, 8 or 16)
+  int64_t rows_per_block;
+  void* dx; float* part_g; float* part_b;     // partials [gridDim.x, hidden] (nullable)
+};
+
+template <bool BF16, bool RMS>
+__global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
+  using C = Chunk<BF16>;
+  constexpr int VEC = C::VEC;
+  __shared__ float red[2][kBwdWaves][2];
+  __shared__ float colbuf[kBwdColFloats];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tw = a.tw, teams = kBwdWaves / tw;
+  const int team = wave / tw, wt = wave % tw;
+  const int64_t nch = a.hidden / VEC;
+  const float inv_h = 1.0f / (float)a.hidden;
+  // the lane's two chunks of a row
+  int64_t ch[2];
+  bool cv[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    ch[j] = (int64_t)j * tw * 64 + wt * 64 + lane;
+    cv[j] = ch[j] < nch;
+  }
+  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  float g[2][VEC];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    C::unpack(cv[j] ? reinterpret_cast<const uint4*>(a.gamma)[ch[j]] : zero, g[j]);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) g[j][i] = a.zcg ? 1.0f + g[j][i] : g[j][i];
+  }
+  float acc_g[2][VEC], acc_b[2][VEC];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) { acc_g[j][i] = 0.0f; acc_b[j][i] = 0.0f; }
+
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+  const int64_t r1 = min(r0 + a.rows_per_block, a.rows);
+  const int64_t iters = (a.rows_per_block + teams - 1) / teams;   // the same in every team
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t row = r0 + it * teams + team;
+    const bool rv = row < r1;
+    float dyv[2][VEC], xh[2][VEC];
+    float mu = 0.0f, rs = 0.0f;
+    if (rv) {
+      if constexpr (!RMS) mu = a.mu[row];
+      rs = a.rsigma[row];
+    }
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = rv && cv[j];
+      float xv[VEC];
+      C::unpack(ok ? reinterpret_cast<const uint4*>(a.dy)[row * nch + ch[j]] : zero, dyv[j]);
+      C::unpack(ok ? reinterpret_cast<const uint4*>(a.x)[row * nch + ch[j]] : zero, xv);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        xh[j][i] = ok ? (RMS ? xv[i] : xv[i] - mu) * rs : 0.0f;
+        const float dxh = dyv[j][i] * g[j][i];
+        s1 += dxh;
+        s2 += dxh * xh[j][i];
+      }
+    }
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    const int buf = (int)(it & 1);
+    if (lane == 0) {
+      red[buf][wave][0] = s1;
+      red[buf][wave][1] = s2;
+    }
+    __syncthreads();
+    float t1 = 0.0f, t2 = 0.0f;
+    for (int k = 0; k < tw; ++k) {              // fixed order over the team's waves
+      t1 += red[buf][team * tw + k][0];
+      t2 += red[buf][team * tw + k][1];
+    }
+    const float m1 = RMS ? 0.0f : t1 * inv_h, m2 = t2 * inv_h;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (rv && cv[j]) {
+        float d[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          d[i] = rs * (dyv[j][i] * g[j][i] - m1 - xh[j][i] * m2);
+          acc_g[j][i] += dyv[j][i] * xh[j][i];
+          acc_b[j][i] += dyv[j][i];
+        }
+        reinterpret_cast<uint4*>(a.dx)[row * nch + ch[j]] = C::pack(d);
+      }
+    }
+  }
+  if (a.part_g == nullptr) return;   // no parameter gradients requested (uniform)
+
+  // teams 1.. hand their column sums to team 0 through LDS; team 0 adds them in
+  // team order and writes the workgroup's partial row
+  const int nb = RMS ? 1 : 2;
+  __syncthreads();
+  if (team > 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (cv[j]) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const int64_t col = ch[j] * VEC + i;
+          colbuf[((team - 1) * nb + 0) * a.hidden + col] = acc_g[j][i];
+          if constexpr (!RMS) colbuf[((team - 1) * nb + 1) * a.hidden + col] = acc_b[j][i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (team == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (cv[j]) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const int64_t col = ch[j] * VEC + i;
+          float sg = acc_g[j][i], sb = acc_b[j][i];
+          for (int t = 1; t < teams; ++t) {
+            sg += colbuf[((t - 1) * nb + 0) * a.hidden + col];
+            if constexpr (!RMS) sb += colbuf[((t - 1) * nb + 1) * a.hidden + col];
+          }
+          a.part_g[(int64_t)blockIdx.x * a.hidden + col] = sg;
+          if constexpr (!RMS) a.part_b[(int64_t)blockIdx.x * a.hidden + col] = sb;
+        }
+      }
+    }
+  }
+}
+
+// Sum of the per-workgroup partial rows in workgroup order.
+template <int OUT>
+__global__ void __launch_bounds__(256) param_finalize_kernel(const float* part, int64_t blocks, int64_t n, void* out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  constexpr int U = 8;
+  float s = 0.0f;
+  int64_t k = 0;
+  for (; k + U <= blocks; k += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[(k + u) * n + c];
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += v[u];
+  }
+  for (; k < blocks; ++k) s += part[k * n + c];
+  if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(out)[c] = f32_to_bf16(s);
+  else reinterpret_cast<float*>(out)[c] = s;
+}
+
+}  // namespace
+
+int norm_bwd_team_waves(int64_t hidden, int dtype) {
+  const int64_t nch = hidden / (dtype == kBF16 ? 8 : 4);
+  int tw = 1;
+  while (tw < kBwdWaves && 2 * 64 * (int64_t)tw < nch) tw *= 2;
+  return 2 * 64 * (int64_t)tw >= nch ? tw : 0;
+}
+
+int64_t norm_bwd_blocks(int64_t rows, int64_t hidden, int dtype) {
+  const int tw = norm_bwd_team_waves(hidden, dtype);
+  if (tw == 0 || rows <= 0) return 0;
+  const int64_t teams = kBwdWaves / tw;
+  const int64_t want = (rows + teams - 1) / teams;   // at least one row per team
+  return want < 256 ? want : 256;                    // one 16-wave workgroup per CU
+}
+
+bool norm_bwd_fits(int64_t hidden, int dtype) {
+  const int tw = norm_bwd_team_waves(hidden, dtype);
+  if (tw == 0) return false;
+  const int64_t teams = kBwdWaves / tw;
+  return (teams - 1) * 2 * hidden <= kBwdColFloats;
+}
+
+hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const float* rsigma, const void* gamma,
+                           int64_t rows, int64_t hidden, int dtype, bool rms, bool zcg, void* dx, void* dgamma,
+                           void* dbeta, int dparam_dtype, float* part_g, float* part_b, hipStream_t s) {
+  const int tw = norm_bwd_team_waves(hidden, dtype);
+  const int64_t blocks = norm_bwd_blocks(rows, hidden, dtype);
+  if (tw == 0 || !norm_bwd_fits(hidden, dtype)) return hipErrorInvalidValue;
+  const bool params = dgamma != nullptr || dbeta != nullptr;
+  {
+    LaunchScope scope("norm_bwd", s);
+    BwdArgs a{dy, x, mu, rsigma, gamma, rows, hidden, zcg ? 1 : 0, tw, (rows + blocks - 1) / blocks, dx,
+              params ? part_g : nullptr, params ? part_b : nullptr};
+    if (dtype == kBF16) {
+      if (rms) norm_bwd_kernel<true, true><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+      else norm_bwd_kernel<true, false><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+    } else {
+      if (rms) norm_bwd_kernel<false, true><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+      else norm_bwd_kernel<false, false><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!params) return hipSuccess;
+  LaunchScope scope("norm_bwd_finalize", s);
+  const unsigned g = (unsigned)((hidden + 255) / 256);
+  for (int p = 0; p < 2; ++p) {
+    void* out = p == 0 ? dgamma : dbeta;
+    const float* part = p == 0 ? part_g : part_b;
+    if (out == nullptr || (p == 1 && rms)) continue;
+    if (dparam_dtype == kBF16) param_finalize_kernel<kBF16><<<g, 256, 0, s>>>(part, blocks, hidden, out);
+    else param_finalize_kernel<kF32><<<g, 256, 0, s>>>(part, blocks, hidden, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace te

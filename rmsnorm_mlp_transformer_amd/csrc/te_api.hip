@@ -401,6 +401,62 @@ te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, 
   return ok();
 }
 
+// ---------------------------------------------------------------- normalisation backward
+size_t te_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden, te_dtype dtype) {
+  if (rows <= 0 || hidden <= 0) return 0;
+  const int64_t blocks = te::norm_bwd_blocks(rows, hidden, dtype);
+  Carver c(nullptr);
+  c.floats((size_t)blocks * hidden);
+  c.floats((size_t)blocks * hidden);
+  return c.off;
+}
+
+te_status te_layernorm_bwd(const void* dy, const void* x, const float* mu, const float* rsigma, const void* gamma,
+                           int64_t rows, int64_t hidden, te_dtype dtype, te_norm_type norm_type,
+                           int zero_centered_gamma, void* dx, void* dgamma, void* dbeta, te_dtype dparam_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(hidden), "hidden must be a positive multiple of 16, got %lld", (long long)hidden);
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
+  TE_ARG(norm_type == TE_LAYERNORM || norm_type == TE_RMSNORM, "invalid norm_type %d", (int)norm_type);
+  TE_REQUIRE(te::norm_bwd_fits(hidden, dtype), TE_ERR_UNSUPPORTED,
+             "hidden %lld too wide for the normalisation backward (at most 16384 bf16 / 8192 fp32)", (long long)hidden);
+  const bool rms = norm_type == TE_RMSNORM;
+  if (rms) dbeta = nullptr;
+  TE_ARG((dgamma == nullptr && dbeta == nullptr) || dparam_dtype == TE_F32 || dparam_dtype == TE_BF16,
+         "dparam_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(gamma != nullptr && aligned16(gamma), "gamma is required (16-byte aligned)");
+  TE_ARG(rows == 0 || (dy != nullptr && x != nullptr && dx != nullptr && rsigma != nullptr && (rms || mu != nullptr)),
+         "dy, x, dx, rsigma and (LayerNorm) mu are required");
+  TE_ARG(aligned16(dy) && aligned16(x) && aligned16(dx) && (dgamma == nullptr || aligned16(dgamma)) &&
+             (dbeta == nullptr || aligned16(dbeta)),
+         "pointers must be 16-byte aligned");
+  const size_t need = te_layernorm_bwd_workspace_size(rows, hidden, dtype);
+  const bool params = dgamma != nullptr || dbeta != nullptr;
+  if (params) {
+    TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+               workspace_bytes, need);
+    TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
+  }
+  hipStream_t s = as_stream(stream);
+  if (rows == 0) {   // parameter gradients of an empty batch are zero
+    if (dgamma != nullptr) TE_HIP(te::launch_fill_zero_bytes(dgamma, hidden * (int64_t)esize(dparam_dtype), s), "fill");
+    if (dbeta != nullptr) TE_HIP(te::launch_fill_zero_bytes(dbeta, hidden * (int64_t)esize(dparam_dtype), s), "fill");
+    return ok();
+  }
+  float *part_g = nullptr, *part_b = nullptr;
+  if (params) {
+    Carver c(workspace);
+    const int64_t blocks = te::norm_bwd_blocks(rows, hidden, dtype);
+    part_g = c.floats((size_t)blocks * hidden);
+    part_b = c.floats((size_t)blocks * hidden);
+  }
+  TE_HIP(te::launch_norm_bwd(dy, x, mu, rsigma, gamma, rows, hidden, dtype, rms, zero_centered_gamma != 0, dx, dgamma,
+                             dbeta, dparam_dtype, part_g, part_b, s),
+         "norm backward");
+  return ok();
+}
+
 // ---------------------------------------------------------------- quantiser
 te_status te_quantize(const void* x, int64_t n, te_dtype x_dtype, uint8_t* codes, const te_fp8_meta* meta,
                       void* stream) {

@@ -65,6 +65,17 @@ hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, in
 
 // dact + dbias. partials: fp32 workspace of dact_partials_floats() floats.
 int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated);
+// Normalisation backward. norm_bwd_team_waves() is 0 when a row does not fit
+// one workgroup's registers (hidden above 16384 bf16 / 8192 fp32);
+// norm_bwd_fits() also checks the LDS of the column-sum combine. part_g and
+// part_b: fp32 workspace of norm_bwd_blocks() * hidden floats each.
+int norm_bwd_team_waves(int64_t hidden, int dtype);
+int64_t norm_bwd_blocks(int64_t rows, int64_t hidden, int dtype);
+bool norm_bwd_fits(int64_t hidden, int dtype);
+hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const float* rsigma, const void* gamma,
+                           int64_t rows, int64_t hidden, int dtype, bool rms, bool zcg, void* dx, void* dgamma,
+                           void* dbeta, int dparam_dtype, float* part_g, float* part_b, hipStream_t s);
+
 // Number of dact workgroups (one partial amax each in the quantising variant).
 int64_t dact_blocks(int64_t rows, int64_t cols, bool gated);
 hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,

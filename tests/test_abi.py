@@ -165,6 +165,19 @@ def test_norm_act_dact_quant_validation():
                                       needq, None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_dact_dbias_quantize(P, P, 64, 32, B.TE_E4M3, B.TE_ACT_GELU, P, ctypes.byref(m), P, B.TE_F32, P,
                                       needq, None) == B.TE_ERR_INVALID_ARGUMENT
+    # normalisation backward
+    nb = lib.te_layernorm_bwd_workspace_size(64, 4096, B.TE_BF16)
+    assert nb > 0
+    assert lib.te_layernorm_bwd(P, P, P, P, P, 64, 4096, B.TE_BF16, B.TE_LAYERNORM, 0, P, P, P, B.TE_F32, P, nb - 1,
+                                None) == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.te_layernorm_bwd(P, P, None, P, P, 64, 4096, B.TE_BF16, B.TE_LAYERNORM, 0, P, P, P, B.TE_F32, P, nb,
+                                None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_layernorm_bwd(P, P, P, P, P, 64, 32768, B.TE_BF16, B.TE_LAYERNORM, 0, P, P, P, B.TE_F32, P, 1 << 30,
+                                None) == B.TE_ERR_UNSUPPORTED
+    assert lib.te_layernorm_bwd(P, P, P, P, P, 64, 16384, B.TE_F32, B.TE_RMSNORM, 0, P, P, None, B.TE_F32, P, 1 << 30,
+                                None) == B.TE_ERR_UNSUPPORTED
+    assert lib.te_layernorm_bwd(P, P, P, P, P, 64, 40, B.TE_BF16, B.TE_LAYERNORM, 0, P, P, P, B.TE_F32, P, nb,
+                                None) == B.TE_ERR_INVALID_ARGUMENT
     # quantiser
     assert lib.te_quantize(P, 24, B.TE_BF16, P, ctypes.byref(m), None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_quantize(P, 32, B.TE_BF16, P, None, None) == B.TE_ERR_INVALID_ARGUMENT

@@ -152,3 +152,21 @@ def test_full_dact_dbias_quantize():
     rq, _ = O.quantize(rdx[rows], meta)
     check_codes(codes_np(codes[torch.as_tensor(rows, device=dev())]), rq, "dx codes (sampled rows)")
     assert_rel(f64(db), rdb, 1e-5, "dbias")
+
+
+def test_full_norm_bwd_ln_bf16():
+    """LayerNorm backward at 8192 x 4096 bf16 from the forward's saved statistics."""
+    w = W.WORKLOADS["ln_mlp_gelu_bf16"]
+    print("full norm_bwd 8192x4096 layernorm bf16", flush=True)
+    t = W.make_inputs(w)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    dy = torch.randn(w.rows, w.hidden, generator=gen).to(torch.bfloat16)
+    x, gamma, beta = t["x"].to(dev()), t["gamma"].to(dev()), t["beta"].to(dev())
+    _, mu, rs = te.layernorm(x, gamma, beta, "layernorm", False, w.epsilon, return_stats=True)
+    dx, dg, db = te.layernorm_bwd(dy.to(dev()), x, mu, rs, gamma, "layernorm")
+    torch.cuda.synchronize()
+    rdx, rdg, rdb = O.norm_bwd(f64(dy), f64(t["x"]), f64(t["gamma"]), "layernorm", w.epsilon)
+    rows = sample_rows(w.rows)
+    assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx[rows], TOL["bf16"], "dx")
+    assert_rel(f64(dg), rdg, 1e-5, "dgamma")
+    assert_rel(f64(db), rdb, 1e-5, "dbeta")

@@ -221,3 +221,52 @@ def test_empty_rows_is_a_no_op():
     assert y.shape == (0, 64) and dx.shape == (0, 64) and codes.shape == (0, 64)
     assert db.shape == (64,) and not db.any()
     assert q.values() == {"amax": 0.0, "scale": 1.0, "scale_inv": 1.0}
+
+
+# ---- normalisation backward
+
+def _norm_bwd_case(rows, hidden, dtype, norm_type, zcg, seed):
+    w = W.Workload("nb", "dense", rows, hidden, 16, dtype, "none", norm_type, zcg, 1e-5, (), False)
+    t = W.make_inputs(w, seed)
+    gen = torch.Generator(device="cpu").manual_seed(seed + 7)
+    dy = torch.randn(rows, hidden, generator=gen).to(W.TORCH_DTYPE[dtype])
+    return w, t, dy
+
+
+@pytest.mark.parametrize("norm_type", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("zcg", [False, True])
+@pytest.mark.parametrize("rows,hidden", [(1, 16), (37, 272), (300, 4096), (2049, 1040), (65, 16384)])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_norm_bwd_matches_oracle(norm_type, zcg, rows, hidden, dtype):
+    if dtype == "fp32" and hidden > 8192:
+        pytest.skip("fp32 rows wider than 8192 are rejected (covered by the ABI tests)")
+    print(f"norm_bwd {norm_type} zcg={zcg} {dtype} {rows}x{hidden}", flush=True)
+    w, t, dy = _norm_bwd_case(rows, hidden, dtype, norm_type, zcg, seed=hidden + rows)
+    x, gamma = t["x"].to(dev()), t["gamma"].to(dev())
+    beta = t["beta"].to(dev()) if norm_type == "layernorm" else None
+    _, mu, rs = te.layernorm(x, gamma, beta, norm_type, zcg, w.epsilon, return_stats=True)
+    dyd = dy.to(dev())
+    dx, dg, db = te.layernorm_bwd(dyd, x, mu, rs, gamma, norm_type, zcg)
+    dx2, dg2, db2 = te.layernorm_bwd(dyd, x, mu, rs, gamma, norm_type, zcg)
+    dgb = te.layernorm_bwd(dyd, x, mu, rs, gamma, norm_type, zcg, dparam_dtype=torch.bfloat16)[1]
+    dxn = te.layernorm_bwd(dyd, x, mu, rs, gamma, norm_type, zcg, with_params=False)[0]
+    torch.cuda.synchronize()
+    rdx, rdg, rdb = O.norm_bwd(f64(dy), f64(t["x"]), f64(t["gamma"]), norm_type, w.epsilon, zcg)
+    assert_rel(f64(dx), rdx, TOL[dtype], "dx")
+    assert_rel(f64(dg), rdg, 1e-5, "dgamma")
+    assert_rel(f64(dgb), rdg, TOL["bf16"], "dgamma bf16")
+    if norm_type == "layernorm":
+        assert_rel(f64(db), rdb, 1e-5, "dbeta")
+    else:
+        assert db is None
+    assert torch.equal(dx, dx2) and torch.equal(dg, dg2), "not bitwise reproducible"
+    assert torch.equal(dx, dxn)
+
+
+def test_norm_bwd_zero_rows():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev())
+    gamma = torch.ones(64, dtype=torch.bfloat16, device=dev())
+    mu = torch.empty(0, dtype=torch.float32, device=dev())
+    dx, dg, db = te.layernorm_bwd(x, x, mu, mu, gamma, "layernorm")
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 64) and not dg.any() and not db.any()
