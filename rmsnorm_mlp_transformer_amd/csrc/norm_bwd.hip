@@ -62,7 +62,8 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
   constexpr int VEC = C::VEC;
   __shared__ float red[2][kBwdWaves][2];
   __shared__ float colbuf[kBwdColFloats];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int tw = a.tw, teams = kBwdWaves / tw;
   const int team = wave / tw, wt = wave % tw;
   const int64_t nch = a.hidden / VEC;
@@ -75,11 +76,24 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
     ch[j] = (int64_t)j * tw * 64 + wt * 64 + lane;
     cv[j] = ch[j] < nch;
   }
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+  // Row vectors are read through a buffer resource over the one row (empty for
+  // a row past the end): chunks outside it read as zero, with no branch or
+  // select around the 16-byte load.
+  const uint32_t row_bytes = (uint32_t)(nch * 16);
+  auto rsrc_of = [&](const void* base, int64_t row, bool valid) {
+    const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + (valid ? row : 0) * (int64_t)row_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, valid ? (int)row_bytes : 0,
+                                             0x00020000);
+  };
+  auto load16 = [&](__amdgpu_buffer_rsrc_t r, int64_t c) {
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)c * 16, 0, 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+  };
   float g[2][VEC];
+  const __amdgpu_buffer_rsrc_t rg = rsrc_of(a.gamma, 0, true);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    C::unpack(cv[j] ? reinterpret_cast<const uint4*>(a.gamma)[ch[j]] : zero, g[j]);
+    C::unpack(load16(rg, ch[j]), g[j]);
 #pragma unroll
     for (int i = 0; i < VEC; ++i) g[j][i] = a.zcg ? 1.0f + g[j][i] : g[j][i];
   }
@@ -96,18 +110,16 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
     const int64_t row = r0 + it * teams + team;
     const bool rv = row < r1;
     float dyv[2][VEC], xh[2][VEC];
-    float mu = 0.0f, rs = 0.0f;
-    if (rv) {
-      if constexpr (!RMS) mu = a.mu[row];
-      rs = a.rsigma[row];
-    }
+    const int64_t srow = rv ? row : 0;
+    const float mu = RMS ? 0.0f : a.mu[srow], rs = rv ? a.rsigma[srow] : 0.0f;
     float s1 = 0.0f, s2 = 0.0f;
+    const __amdgpu_buffer_rsrc_t rdy = rsrc_of(a.dy, row, rv), rx = rsrc_of(a.x, row, rv);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bool ok = rv && cv[j];
       float xv[VEC];
-      C::unpack(ok ? reinterpret_cast<const uint4*>(a.dy)[row * nch + ch[j]] : zero, dyv[j]);
-      C::unpack(ok ? reinterpret_cast<const uint4*>(a.x)[row * nch + ch[j]] : zero, xv);
+      C::unpack(load16(rdy, ch[j]), dyv[j]);
+      C::unpack(load16(rx, ch[j]), xv);
 #pragma unroll
       for (int i = 0; i < VEC; ++i) {
         xh[j][i] = ok ? (RMS ? xv[i] : xv[i] - mu) * rs : 0.0f;
@@ -184,24 +196,29 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
   }
 }
 
-// Sum of the per-workgroup partial rows in workgroup order.
+// Sum of the per-workgroup partial rows: 16 threads per column each add a
+// fixed, contiguous range of rows, then one of them adds the 16 results in
+// order (a fixed order: bitwise reproducible).
 template <int OUT>
 __global__ void __launch_bounds__(256) param_finalize_kernel(const float* part, int64_t blocks, int64_t n, void* out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= n) return;
-  constexpr int U = 8;
+  constexpr int S = 16;
+  __shared__ float red[S][16];
+  const int cl = threadIdx.x % 16, sp = threadIdx.x / 16;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+  const int64_t per = (blocks + S - 1) / S;
+  const int64_t k0 = sp * per, k1 = min(k0 + per, blocks);
   float s = 0.0f;
-  int64_t k = 0;
-  for (; k + U <= blocks; k += U) {
-    float v[U];
+  if (c < n)
+    for (int64_t k = k0; k < k1; ++k) s += part[k * n + c];
+  red[sp][cl] = s;
+  __syncthreads();
+  if (sp == 0 && c < n) {
+    float t = red[0][cl];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = part[(k + u) * n + c];
-#pragma unroll
-    for (int u = 0; u < U; ++u) s += v[u];
+    for (int q = 1; q < S; ++q) t += red[q][cl];
+    if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(out)[c] = f32_to_bf16(t);
+    else reinterpret_cast<float*>(out)[c] = t;
   }
-  for (; k < blocks; ++k) s += part[k * n + c];
-  if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(out)[c] = f32_to_bf16(s);
-  else reinterpret_cast<float*>(out)[c] = s;
 }
 
 }  // namespace
@@ -251,7 +268,7 @@ hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const
   }
   if (!params) return hipSuccess;
   LaunchScope scope("norm_bwd_finalize", s);
-  const unsigned g = (unsigned)((hidden + 255) / 256);
+  const unsigned g = (unsigned)((hidden + 15) / 16);
   for (int p = 0; p < 2; ++p) {
     void* out = p == 0 ? dgamma : dbeta;
     const float* part = p == 0 ? part_g : part_b;
