@@ -380,6 +380,43 @@ def layernorm_mlp_fwd(x, gamma, beta, kernel1, kernel2, bias1=None, bias2=None,
     return out
 
 
+def layernorm_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=None,
+                      norm_type="layernorm", zero_centered_gamma=False, epsilon=1e-6,
+                      activation_type=("relu",), h1=None, round_intermediates=False):
+    """[MLP] Description: the backward pass gives the gradients of every
+    parameter through fused backward operations (the activation gradient
+    with the bias reduction); [DENSE] Description: gradients for x, kernel,
+    gamma, beta and bias from the saved forward context. With xn the
+    normalized input, h = xn @ kernel1 + bias1, act = activation(h) and
+    grad = dL/dy:
+      dkernel2 = act^T @ grad,   dbias2 = sum over rows of grad
+      dact = grad @ kernel2^T,   dh, dbias1 = dact_dbias(dact, h)
+      dkernel1 = xn^T @ dh,      dxn = dh @ kernel1^T
+      dx, dgamma, dbeta = norm_bwd(dxn, x, ...)
+    ``h1`` (optional) replaces h by the saved pre-activation.
+    ``round_intermediates`` rounds the tensors a bf16 backward materialises
+    (xn, act, dact, dh, dxn) to bf16, for diagnostics.
+    Returns a dict with dx, dgamma, dbeta (None for RMSNorm), dkernel1,
+    dbias1, dkernel2, dbias2."""
+    r = bf16_round if round_intermediates else (lambda t: t)
+    grad = np.asarray(grad, dtype=np.float64)
+    kernel1 = np.asarray(kernel1, dtype=np.float64)
+    kernel2 = np.asarray(kernel2, dtype=np.float64)
+    xn = normalize(x, gamma, beta, norm_type, epsilon, zero_centered_gamma)[0]
+    h = np.asarray(h1, dtype=np.float64) if h1 is not None else dense(xn, kernel1, bias1)
+    act = r(activation(h, activation_type))
+    dkernel2 = np.matmul(act.T, grad)
+    dbias2 = grad.sum(axis=0)
+    dact = r(np.matmul(grad, kernel2.T))
+    dh, dbias1 = dact_dbias(dact, h, activation_type)
+    dh = r(dh)
+    dkernel1 = np.matmul(r(xn).T, dh)
+    dxn = r(np.matmul(dh, kernel1.T))
+    dx, dgamma, dbeta = norm_bwd(dxn, x, gamma, norm_type, epsilon, zero_centered_gamma)
+    return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta, "dkernel1": dkernel1, "dbias1": dbias1,
+            "dkernel2": dkernel2, "dbias2": dbias2}
+
+
 def rel_l2(got, ref) -> float:
     """Relative L2 error ||got - ref|| / ||ref|| over the whole tensor."""
     got = np.asarray(got, dtype=np.float64)

@@ -157,6 +157,21 @@ def _norm_bwd_dgamma_from_x(dy, x, gamma, norm_type, epsilon, zero_centered_gamm
     return dx, (np.asarray(dy) * np.asarray(x)).sum(axis=0), dbeta
 
 
+_orig_mlp_bwd = T.layernorm_mlp_bwd
+
+
+def _mlp_bwd_dkernel2_from_h(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=None, norm_type="layernorm",
+                             zero_centered_gamma=False, epsilon=1e-6, activation_type=("relu",), h1=None,
+                             round_intermediates=False):
+    out = _orig_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1, bias2, norm_type, zero_centered_gamma,
+                        epsilon, activation_type, h1, round_intermediates)
+    xn = T.normalize(x, gamma, beta, norm_type, epsilon, zero_centered_gamma)[0]
+    h = T.dense(xn, kernel1, bias1)
+    f = np.asarray(kernel2).shape[0]
+    out["dkernel2"] = np.matmul(h[:, :f].T, np.asarray(grad, dtype=np.float64))   # pre-activation instead of act
+    return out
+
+
 MUTANTS = [
     ("layernorm", _ln_unbiased, [P.test_layernorm_invariants_closed_form_variance, P.test_layernorm_brute_force]),
     ("layernorm", _ln_eps_outside, [P.test_layernorm_brute_force]),
@@ -176,6 +191,8 @@ MUTANTS = [
     ("norm_bwd", _norm_bwd_dropped_mean, [P.test_layernorm_bwd_dx_sums_to_zero_per_row,
                                           lambda: P.test_norm_bwd_central_differences("layernorm", False)]),
     ("norm_bwd", _norm_bwd_dgamma_from_x, [lambda: P.test_norm_bwd_central_differences("rmsnorm", True)]),
+    ("layernorm_mlp_bwd", _mlp_bwd_dkernel2_from_h,
+     [lambda: P.test_mlp_bwd_central_differences("layernorm", ("gelu",))]),
 ]
 
 

@@ -458,3 +458,47 @@ def test_norm_bwd_zero_centered_gamma_equivalence():
         a = O.norm_bwd(dy, x, gamma, nt, 1e-6, True)
         b = O.norm_bwd(dy, x, 1.0 + gamma, nt, 1e-6, False)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- layernorm_mlp backward: finite differences of the whole (pinned) forward
+
+@pytest.mark.parametrize("norm_type,act", [("layernorm", ("gelu",)), ("rmsnorm", ("silu", "linear")),
+                                           ("layernorm", ("gelu_erf", "linear"))])
+def test_mlp_bwd_central_differences(norm_type, act):
+    rows, h, f = 3, 4, 5
+    g2 = 2 if len(act) == 2 else 1
+    x = RNG.standard_normal((rows, h))
+    gamma = RNG.standard_normal(h) * 0.3 + 1.0
+    beta = RNG.standard_normal(h) * 0.2 if norm_type == "layernorm" else None
+    w1 = RNG.standard_normal((h, g2 * f)) * 0.5
+    b1 = RNG.standard_normal(g2 * f) * 0.2
+    w2 = RNG.standard_normal((f, h)) * 0.5
+    b2 = RNG.standard_normal(h) * 0.2
+    gy = RNG.standard_normal((rows, h))
+    eps = 1e-3
+    args = dict(x=x, gamma=gamma, beta=beta, kernel1=w1, kernel2=w2, bias1=b1, bias2=b2)
+
+    def loss(**kw):
+        a = dict(args)
+        a.update(kw)
+        y = O.layernorm_mlp_fwd(a["x"], a["gamma"], a["beta"], a["kernel1"], a["kernel2"], a["bias1"], a["bias2"],
+                                norm_type=norm_type, epsilon=eps, activation_type=act)["y"]
+        return float(np.sum(gy * y))
+
+    g = O.layernorm_mlp_bwd(gy, x, gamma, beta, w1, w2, b1, b2, norm_type=norm_type, epsilon=eps,
+                            activation_type=act)
+    names = [("x", "dx"), ("gamma", "dgamma"), ("kernel1", "dkernel1"), ("bias1", "dbias1"),
+             ("kernel2", "dkernel2"), ("bias2", "dbias2")]
+    if norm_type == "layernorm":
+        names.append(("beta", "dbeta"))
+    d = 1e-6
+    for arg, out in names:
+        base = args[arg]
+        for idx in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[idx] += d
+            m[idx] -= d
+            fd = (loss(**{arg: p}) - loss(**{arg: m})) / (2 * d)
+            assert abs(g[out][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (arg, idx, g[out][idx], fd)
+    if norm_type == "rmsnorm":
+        assert g["dbeta"] is None
