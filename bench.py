@@ -40,10 +40,10 @@ import workloads as W  # noqa: E402
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
 CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
-_GEMM = ["gemm_bf16.hip", "gemm_fp8.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
+_GEMM = ["gemm_bf16.hip", "gemm_bt.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
 KERNEL_SOURCES = {
     "gemm_bf16_act": _GEMM, "gemm_bf16": _GEMM, "gemm_bf16_gated": _GEMM, "gemm_fp8_h_amax": _GEMM,
-    "gemm_fp8": _GEMM,
+    "gemm_fp8": _GEMM, "gemm_bf16_dgrad": _GEMM, "gemm_bf16_wgrad": _GEMM,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
     "norm_bwd": ["norm_bwd.hip", "te_common.hpp"],
 }
@@ -189,6 +189,47 @@ class NormBwdCase:
         return 3 * M * H * 2 + 2 * M * 4 + 2 * H * 4
 
 
+class MlpBwdCase:
+    """The LayerNorm-MLP backward from the forward's saved context (h1, mu,
+    rsigma): 4 GEMMs (two data-gradient, two weight-gradient), the activation
+    backward with dbias1, dbias2, and the normalisation backward."""
+
+    def __init__(self, w: W.Workload, te, dev):
+        self.w = w
+        t = W.make_inputs(w)
+        self.g = {k: v.to(dev) for k, v in t.items()}
+        g = self.g
+        gen = torch.Generator(device="cpu").manual_seed(3)
+        self.gy = torch.randn(w.rows, w.hidden, generator=gen).to(torch.bfloat16).to(dev)
+        _, self.saved = te.layernorm_mlp(g["x"], g["gamma"], g.get("beta"), [g["kernel1"], g["kernel2"]],
+                                         [g.get("bias1"), g.get("bias2")], w.norm_type,
+                                         zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
+                                         activation_type=w.activation_type, return_saved=True)
+        B = te._binding
+        act = te.act_type_of(w.activation_type)
+        gg = 2 if w.gated else 1
+        self.out = {"dx": torch.empty_like(g["x"]), "dgamma": torch.empty(w.hidden, device=dev),
+                    "dbeta": torch.empty(w.hidden, device=dev), "dkernel1": torch.empty_like(g["kernel1"]),
+                    "dkernel2": torch.empty_like(g["kernel2"]), "dbias1": torch.empty(gg * w.ffn, device=dev),
+                    "dbias2": torch.empty(w.hidden, device=dev)}
+        n = B.te_layernorm_mlp_bwd_workspace_size(w.rows, w.hidden, w.ffn, act)
+        self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        o, sv = self.out, self.saved
+        norm = B.TE_LAYERNORM if w.norm_type == "layernorm" else B.TE_RMSNORM
+
+        def fn():
+            B.te_layernorm_mlp_bwd(self.gy, g["x"], g["gamma"], g.get("beta"), g["kernel1"], g["kernel2"], sv["mu"],
+                                   sv["rsigma"], sv["h1"], w.rows, w.hidden, w.ffn, B.TE_BF16, norm,
+                                   w.zero_centered_gamma, w.epsilon, act, o["dx"], o["dgamma"], o["dbeta"],
+                                   o["dkernel1"], o["dbias1"], o["dkernel2"], o["dbias2"], B.TE_F32, self.ws,
+                                   self.ws.numel())
+        self.fn = fn
+
+    def flops(self):
+        # two data-gradient and two weight-gradient GEMMs, each 2*M*N*K
+        return 2 * self.w.gemm_flops()
+
+
 def time_steps(fn, steps, warmup, te=None):
     for _ in range(warmup):
         fn()
@@ -221,6 +262,8 @@ def kernel_work(w: W.Workload, name: str):
             return 2 * M * H * F, "flop", "mfma"
         if name in ("gemm_bf16_act", "gemm_bf16_gated", "gemm_fp8_h_amax"):
             return 2 * M * H * g * F, "flop", "mfma"
+        if name in ("gemm_bf16_dgrad", "gemm_bf16_wgrad"):   # average of the launch pair (GEMM1 and GEMM2 shapes)
+            return (2 * M * H * g * F + 2 * M * F * H) // 2, "flop", "mfma"
         return 2 * M * F * H, "flop", "mfma"
     if name == "dact_dbias":   # grad [M, F], h1 and dx [M, G*F], bf16
         return (1 + 2 * g) * M * F * 2, "byte", "hbm"
@@ -372,6 +415,19 @@ def main():
             log(f"bench part {pname}: {dms:.4f} ms, {gbs:.0f} GB/s")
             del d
             torch.cuda.empty_cache()
+        # the whole LayerNorm-MLP backward at the bench workload's shape
+        bw = W.WORKLOADS["ln_mlp_gelu_bf16"]
+        bc = MlpBwdCase(bw, te, dev)
+        bms, bk = time_steps(bc.fn, max(5, args.steps // 2), 2, te)
+        bv = bc.flops() / (bms / 1e3) / 1e12
+        parts["ln_mlp_gelu_bf16_backward"] = {
+            "ms_per_step": round(bms, 4), "TFLOP/s": round(bv, 2), "frac_of_peak": round(bv / PEAK["bf16"], 4),
+            "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in bk.items()},
+            "roofline": roofline(bw, {k: v for k, v in bk.items() if k.startswith("gemm")}, "bf16",
+                                 "ln_mlp_gelu_bf16_backward")}
+        log(f"bench part backward: {bms:.4f} ms, {bv:.1f} TFLOP/s")
+        del bc
+        torch.cuda.empty_cache()
         # normalisation backward at the bench workload's shape
         nw = W.WORKLOADS["ln_mlp_gelu_bf16"]
         nbc = NormBwdCase(nw, te, dev)

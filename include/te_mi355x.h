@@ -250,6 +250,36 @@ size_t te_layernorm_mlp_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t
                                            te_dtype dtype, te_act_type act_type,
                                            te_quant quant);
 
+/* te_layernorm_mlp_bwd - the backward of the fused feed-forward sublayer
+ * ([MLP] Description: the backward pass gives the gradients of every
+ * parameter, with the fused activation gradient + bias reduction; [DENSE]
+ * Description: gradients for x, kernel, gamma, beta and bias from the
+ * saved forward context). With xn the normalised input, act = activation(h1)
+ * and grad = dL/dy [rows, hidden]:
+ *   dkernel2 = act^T @ grad [ffn, hidden]; dbias2 = sum over rows of grad
+ *   dact = grad @ kernel2^T; dh1, dbias1 = te_dact_dbias(dact, h1)
+ *   dkernel1 = xn^T @ dh1 [hidden, G*ffn]; dxn = dh1 @ kernel1^T
+ *   dx, dgamma, dbeta = te_layernorm_bwd(dxn, x, mu, rsigma, gamma).
+ * Inputs are the forward's: x, gamma, beta, kernel1, kernel2, epsilon, and its
+ * saved context te_mlp_saved.h1 (pre-activation [rows, G*ffn]), mu (LayerNorm)
+ * and rsigma. xn and act are recomputed. dtype TE_BF16 only (else
+ * TE_ERR_UNSUPPORTED); all GEMMs accumulate in fp32 and write bf16 (dx,
+ * dkernel1, dkernel2); dgamma, dbeta, dbias1, dbias2 are fixed-order fp32
+ * sums written as dparam_dtype (F32 or BF16), each optional (NULL skips it;
+ * dbeta is ignored for RMSNorm). [rows, features] tensors and the kernels
+ * must be smaller than 2 GiB, hidden at most 16384. Workspace:
+ * te_layernorm_mlp_bwd_workspace_size(). */
+te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamma, const void* beta,
+                               const void* kernel1, const void* kernel2, const float* mu,
+                               const float* rsigma, const void* h1, int64_t rows, int64_t hidden,
+                               int64_t ffn, te_dtype dtype, te_norm_type norm_type,
+                               int zero_centered_gamma, float epsilon, te_act_type act_type,
+                               void* dx, void* dgamma, void* dbeta, void* dkernel1, void* dbias1,
+                               void* dkernel2, void* dbias2, te_dtype dparam_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
+size_t te_layernorm_mlp_bwd_workspace_size(int64_t rows, int64_t hidden, int64_t ffn,
+                                           te_act_type act_type);
+
 /* te_quantize - the per-tensor fp8 quantiser on its own ([ACT] Inputs:
  * quantizer; [DENSE] Description: the normalised output and the kernel are
  * quantised before the GEMM). x: [n] of x_dtype (F32 or BF16); codes: [n]

@@ -394,8 +394,9 @@ def layernorm_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=
       dkernel1 = xn^T @ dh,      dxn = dh @ kernel1^T
       dx, dgamma, dbeta = norm_bwd(dxn, x, ...)
     ``h1`` (optional) replaces h by the saved pre-activation.
-    ``round_intermediates`` rounds the tensors a bf16 backward materialises
-    (xn, act, dact, dh, dxn) to bf16, for diagnostics.
+    ``round_intermediates`` rounds the tensors a bf16 forward/backward pair
+    materialises to bf16: xn, the saved pre-activation h, act, dact, dh and
+    dxn.
     Returns a dict with dx, dgamma, dbeta (None for RMSNorm), dkernel1,
     dbias1, dkernel2, dbias2."""
     r = bf16_round if round_intermediates else (lambda t: t)
@@ -403,7 +404,7 @@ def layernorm_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=
     kernel1 = np.asarray(kernel1, dtype=np.float64)
     kernel2 = np.asarray(kernel2, dtype=np.float64)
     xn = normalize(x, gamma, beta, norm_type, epsilon, zero_centered_gamma)[0]
-    h = np.asarray(h1, dtype=np.float64) if h1 is not None else dense(xn, kernel1, bias1)
+    h = np.asarray(h1, dtype=np.float64) if h1 is not None else r(dense(r(xn), kernel1, bias1))
     act = r(activation(h, activation_type))
     dkernel2 = np.matmul(act.T, grad)
     dbias2 = grad.sum(axis=0)

@@ -90,6 +90,9 @@ _SIGS = {
     "te_layernorm_mlp_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
                                     _int, _f, _int, _int, _vp, _saved_p, _vp, _sz, _vp]),
     "te_layernorm_mlp_fwd_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int]),
+    "te_layernorm_mlp_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
+                                    _int, _f, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
+    "te_layernorm_mlp_bwd_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "te_quantize": (_int, [_vp, _i64, _int, _vp, _meta_p, _vp]),
     "te_dequantize": (_int, [_vp, _i64, _meta_p, _vp, _int, _vp]),
     "te_last_error": (ctypes.c_char_p, []),
@@ -266,6 +269,20 @@ def te_layernorm_mlp_fwd(x, gamma, beta, kernel1, bias1, kernel2, bias2, rows, h
                                      _ptr(kernel2), _ptr(bias2), rows, hidden, ffn, dtype, norm_type,
                                      int(zero_centered_gamma), float(epsilon), act_type, quant, _ptr(y),
                                      ctypes.byref(saved) if saved is not None else None,
+                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def te_layernorm_mlp_bwd_workspace_size(rows, hidden, ffn, act_type) -> int:
+    return _lib.te_layernorm_mlp_bwd_workspace_size(rows, hidden, ffn, act_type)
+
+
+def te_layernorm_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, mu, rsigma, h1, rows, hidden, ffn, dtype, norm_type,
+                         zero_centered_gamma, epsilon, act_type, dx, dgamma, dbeta, dkernel1, dbias1, dkernel2, dbias2,
+                         dparam_dtype, workspace, workspace_bytes, stream=None):
+    _check(_lib.te_layernorm_mlp_bwd(_ptr(grad), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(kernel1), _ptr(kernel2),
+                                     _ptr(mu), _ptr(rsigma), _ptr(h1), rows, hidden, ffn, dtype, norm_type,
+                                     int(zero_centered_gamma), epsilon, act_type, _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                     _ptr(dkernel1), _ptr(dbias1), _ptr(dkernel2), _ptr(dbias2), dparam_dtype,
                                      _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
@@ -477,6 +494,34 @@ def layernorm_mlp(x, gamma, beta, kernels, biases, norm_type, zero_centered_gamm
                          zero_centered_gamma, epsilon, act, quant, y, saved, ws, ws.numel())
     y = y.reshape(*x.shape[:-1], hidden)
     return (y, saved_t) if return_saved else y
+
+
+def layernorm_mlp_bwd(grad, x, gamma, beta, kernels, saved, norm_type="layernorm", zero_centered_gamma=False,
+                      epsilon=1e-6, activation_type=("relu",), dparam_dtype=torch.float32, with_biases=True):
+    """Backward of layernorm_mlp from its saved context (``saved`` as returned
+    by layernorm_mlp(..., return_saved=True, save_h1=True): h1, mu, rsigma).
+    Returns a dict of dx, dgamma, dbeta (None for RMSNorm), dkernel1, dbias1,
+    dkernel2, dbias2 (the biases' gradients None without with_biases)."""
+    act = act_type_of(activation_type)
+    g2, x2 = _flat(grad), _flat(x)
+    rows, hidden = x2.shape
+    k1, k2 = kernels
+    ffn = k2.shape[0]
+    dev = x.device
+    out = {"dx": torch.empty_like(x2),
+           "dgamma": torch.empty(hidden, dtype=dparam_dtype, device=dev),
+           "dbeta": torch.empty(hidden, dtype=dparam_dtype, device=dev) if norm_type == "layernorm" else None,
+           "dkernel1": torch.empty_like(k1), "dkernel2": torch.empty_like(k2),
+           "dbias1": torch.empty(k1.shape[1], dtype=dparam_dtype, device=dev) if with_biases else None,
+           "dbias2": torch.empty(hidden, dtype=dparam_dtype, device=dev) if with_biases else None}
+    nbytes = te_layernorm_mlp_bwd_workspace_size(rows, hidden, ffn, act)
+    ws = _workspace(nbytes, dev)
+    te_layernorm_mlp_bwd(g2, x2, gamma, beta, k1, k2, saved["mu"], saved["rsigma"], _flat(saved["h1"]), rows, hidden,
+                         ffn, _dtype(x2), _NORM[norm_type], zero_centered_gamma, epsilon, act, out["dx"],
+                         out["dgamma"], out["dbeta"], out["dkernel1"], out["dbias1"], out["dkernel2"], out["dbias2"],
+                         _dtype(out["dgamma"]), ws, ws.numel())
+    out["dx"] = out["dx"].reshape(x.shape)
+    return out
 
 
 def quantize(x, quantizer: Fp8Meta):

@@ -269,11 +269,13 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 // dbias_finalize sums in a fixed order (bitwise reproducible).
 // MODE kDactStore writes dx; kDactAmax writes no dx but the block's max |dx|
 // (fp32, before any rounding) to amax_part[block]; kDactQuant writes the E4M3
-// codes of dx * scale, the scale coming from the finished amax.
+// codes of dx * scale, the scale coming from the finished amax; kDactSum
+// writes nothing but the column partials (with the linear activation this is
+// the bias gradient sum over rows of grad).
 constexpr int kDactStrip = 512;
 constexpr int kDactWaves = 8;
 constexpr int kDactUnroll = 4;
-enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2 };
+enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2, kDactSum = 3 };
 
 template <bool BF16, int ACT, bool GATED, int MODE>
 __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad, const void* x, int64_t rows,
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
     } else if constexpr (MODE == kDactAmax) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(d[i]));
-    } else {
+    } else if constexpr (MODE == kDactQuant) {
       *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(dx) + e) = encode8(d, qscale);
     }
   };
@@ -575,6 +577,18 @@ hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int6
   }
   if (dbias != nullptr) return dbias_finalize(partials, rows, cols, gated, dbias, dbias_dtype, s);
   return hipSuccess;
+}
+
+hipError_t launch_colsum(const void* x, int64_t rows, int64_t cols, int dtype, void* sum, int sum_dtype,
+                         float* partials, hipStream_t s) {
+  {
+    LaunchScope scope("colsum", s);
+    // the linear activation's gradient is 1: dact's column partials of grad = x
+    const hipError_t e = dact_dispatch<kDactSum>(x, x, rows, cols, dtype, kLinear, false, nullptr, partials,
+                                                 nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  return dbias_finalize(partials, rows, cols, false, sum, sum_dtype, s);
 }
 
 hipError_t launch_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,

@@ -14,6 +14,11 @@
 // N-contiguous tile on the way out of LDS. STAGES LDS stages (128 KiB in
 // all): the loads of the next STAGES - 1 stages are in flight while the
 // MFMAs of the current one run; one barrier per stage.
+//
+// With AT, A is given transposed, A^T [K, M] row-major (M contiguous): the
+// weight-gradient GEMMs of the backward, x^T @ dY, whose operands are both
+// stored token-major. The A tile is then loaded and read exactly like the B
+// tile (k-rows of 256 values, transposing reads).
 #include "gemm_common.hpp"
 #include "gemm_lds.hpp"
 #include "te_kernels.hpp"
@@ -44,7 +49,8 @@ struct Stage {
 // quarters of the 64 banks.
 __device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES, bool PP>
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES, bool PP,
+          bool AT>
 __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   using St = Stage<BK>;
   constexpr int NJ = 16 / WAVES;                      // 32-column blocks per wave
@@ -53,6 +59,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   constexpr int RB = BK / WAVES;                      // B k-rows loaded per wave
   constexpr int LB = RB / 2;                          // 1 KiB B loads per wave and stage
   static_assert(LA >= 1 && LB >= 1, "tile too small for the wave count");
+  static_assert(!AT || LA == LB, "a transposed A tile is loaded like the B tile");
   // one array per stage: distinct objects let the compiler see that the LDS-DMA
   // of a later stage cannot alias the reads of the current one (no vmcnt wait)
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[St::BYTES];
@@ -72,17 +79,27 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
 
-  // ---- loaders: wave w fills A rows [w RA, (w + 1) RA) and B k-rows [w RB, (w + 1) RB)
+  // ---- loaders: wave w fills A rows [w RA, (w + 1) RA) (AT: A k-rows [w RB,
+  // (w + 1) RB)) and B k-rows [w RB, (w + 1) RB)
   const int rows_a = min(M - m0, kTileM);
-  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      AT ? make_rsrc(a.A, (uint32_t)K * M * 2) : make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K * 2);
   uint32_t off_a[LA];
   int kc_a[LA];
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int r = wave * RA + j * (64 / St::CPR) + lane / St::CPR;
-    const int c = (lane % St::CPR) ^ chunk_swizzle<St::CPR>(r);
-    off_a[j] = (uint32_t)r * K * 2 + c * 16;
-    kc_a[j] = c * 8;
+    if constexpr (AT) {
+      // columns past M read the next k-row (finite data; those output rows are not stored)
+      const int kr = wave * RB + j * 2 + (lane >> 5);
+      const int q = (lane & 31) ^ swz_b(kr);
+      off_a[j] = (uint32_t)kr * M * 2 + (uint32_t)(m0 + 8 * q) * 2;
+      kc_a[j] = kr;
+    } else {
+      const int r = wave * RA + j * (64 / St::CPR) + lane / St::CPR;
+      const int c = (lane % St::CPR) ^ chunk_swizzle<St::CPR>(r);
+      off_a[j] = (uint32_t)r * K * 2 + c * 16;
+      kc_a[j] = c * 8;
+    }
   }
   // the whole B operand (K * NB * 2 < 2^31 bytes, checked by the launcher)
   const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.B, (uint32_t)K * NB * 2);
@@ -105,8 +122,13 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     const bool tail = k0 + BK > K;
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-      const uint32_t v = (tail && k0 + kc_a[j] >= K) ? kOffNone : off_a[j];
-      load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * 2);
+      if constexpr (AT) {
+        const uint32_t v = k0 + kc_a[j] >= K ? kOffNone : off_a[j];
+        load_lds16(rsrc_a, As + wave * RB * 512 + j * 1024, v, (uint32_t)k0 * M * 2);
+      } else {
+        const uint32_t v = (tail && k0 + kc_a[j] >= K) ? kOffNone : off_a[j];
+        load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * 2);
+      }
     }
     // k-rows at or past K (including whole stages past the end) read as zero:
     // their lanes take an offset beyond the range, so the check fails on the
@@ -125,6 +147,15 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   for (int kk = 0; kk < BK / 16; ++kk)
     a_off[kk] = (wm * 128 + lr) * BK * 2 + 16 * ((2 * kk + lh) ^ chunk_swizzle<St::CPR>(lr));
   const int g = lane >> 4, i4 = (lane >> 2) & 3, c4 = lane & 3;
+  // transposing-read offset of the 32-value block starting at column `base`
+  // of a k-row tile (B, and A with AT)
+  auto tr_off = [&](int base) {
+    const int v = base + 16 * (g & 1) + 4 * c4;
+    return (8 * (g >> 1) + i4) * 512 + 16 * ((v >> 3) ^ swz_b(i4)) + 8 * (c4 & 1);
+  };
+  int at_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) at_off[i] = tr_off(wm * 128 + i * 32);
   int b_off[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -153,7 +184,15 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   auto read_frags = [&](int s, int kk, Frags& f) {
     const uint8_t* S = stage_ptr(s);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[kk] + i * 32 * BK * 2);
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (AT) {
+        const i16x4_t lo = lds_read_tr16(S + at_off[i] + (16 * kk) * 512);
+        const i16x4_t hi = lds_read_tr16(S + at_off[i] + (16 * kk + 4) * 512);
+        f.a[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        f.a[i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[kk] + i * 32 * BK * 2);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const i16x4_t lo = lds_read_tr16(S + b_off[j] + (16 * kk) * 512);
@@ -274,18 +313,39 @@ hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
+    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
+    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
+    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages, kPingPong><<<grid, T, 0, s>>>(a);
+    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t n_b, int64_t K, const Epilogue& e,
+                               hipStream_t s) {
+  if (e.act != kLinear || e.gated || e.h_out != nullptr || e.amax != nullptr) return hipErrorInvalidValue;
+  LaunchScope scope("gemm_bf16_wgrad", s);
+  GemmArgs a;
+  a.A = reinterpret_cast<const uint16_t*>(At);
+  a.B = reinterpret_cast<const uint16_t*>(B);
+  a.K = (int)K;
+  a.ep.bias = reinterpret_cast<const uint16_t*>(e.bias);
+  a.ep.out = reinterpret_cast<uint16_t*>(e.out);
+  a.ep.h_out = nullptr;
+  a.ep.amax = nullptr;
+  a.ep.M = (int)M;
+  a.ep.n_b = (int)n_b;
+  a.ep.F = (int)n_b;
+  const unsigned grid = (unsigned)(((M + kTileM - 1) / kTileM) * ((n_b + kTileN - 1) / kTileN));
+  gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, true>
+      <<<grid, 64 * kWaves, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
                             const Epilogue& e, hipStream_t s) {

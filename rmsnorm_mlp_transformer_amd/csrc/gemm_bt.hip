@@ -1,20 +1,26 @@
-// fp8 (E4M3 x E4M3) MFMA GEMM for gfx950 with fp32 accumulation and the
-// fused bias / activation / gate / amax epilogue. Used when the quantizer set
-// enables per-tensor current scaling: "NVIDIA TransformerEngine JAX LayerNorm
-// Dense" (Description: the normalised output and the kernel are quantised,
-// then the GEMM runs) and "... LayerNorm MLP" (Description: the same for
-// GEMM1 and GEMM2).
+// MFMA GEMM for gfx950 with both operands K-contiguous, in fp8 (E4M3 x
+// E4M3) or bf16, fp32 accumulation and the fused bias / activation / gate /
+// amax epilogue.
+//  - fp8: used when the quantizer set enables per-tensor current scaling:
+//    "NVIDIA TransformerEngine JAX LayerNorm Dense" (Description: the
+//    normalised output and the kernel are quantised, then the GEMM runs) and
+//    "... LayerNorm MLP" (Description: the same for GEMM1 and GEMM2). The
+//    weight quantiser writes the kernel transposed; the accumulator is
+//    multiplied by scale_inv(A) * scale_inv(B), derived from the two amax
+//    values exactly as the quantisers did.
+//  - bf16: the data-gradient GEMMs of the backward ("... LayerNorm MLP",
+//    Description: the backward pass gives the gradients of every parameter),
+//    dY @ kernel^T, where the kernel [K_out, N_in] read row by row is exactly
+//    the K-contiguous B^T operand.
 //
-// Both operands arrive K-contiguous: A codes [M, K] and B^T codes [n_b, K]
-// (the weight quantiser writes the kernel transposed). Each k stage holds 64
-// codes of every tile row for 256 rows of each operand; both tiles move HBM ->
-// LDS with buffer_load ... lds (16 bytes per lane, no register staging),
-// 16-byte chunks XOR-swizzled per row, and come back with conflict-free
-// ds_read_b128, two per lane and operand for one
-// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 for both operands, unit block
-// scales). The accumulator is multiplied by scale_inv(A) * scale_inv(B),
-// which the kernel derives from the two amax values exactly as the
-// quantisers did.
+// A is [M, K] and B^T is [n_b, K], both K-contiguous. Each k stage holds 64
+// bytes of every tile row (64 fp8 or 32 bf16 values) for 256 rows of each
+// operand; both tiles move HBM -> LDS with buffer_load ... lds (16 bytes per
+// lane, no register staging), 16-byte chunks XOR-swizzled per row, and come
+// back with conflict-free ds_read_b128: an fp8 MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 for both operands, unit block
+// scales) takes two 16-byte chunks per lane and operand, a bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16) one.
 //
 // 256 x 256 output tile per workgroup, 8 waves of 128 x 64, 4 LDS stages
 // (128 KiB). Ping-pong schedule: waves 0-3 and 4-7 hold one wave per SIMD
@@ -49,18 +55,27 @@ struct FpArgs {
   EpiArgs ep;
 };
 
-struct Frags {
-  i32x8_t a[4];             // row blocks
-  i32x8_t b[kNJ];           // column blocks
+template <bool FP8>
+struct Frags;
+template <>
+struct Frags<true> {        // one 64-k step: [row block] / [column block]
+  i32x8_t a[4];
+  i32x8_t b[kNJ];
+};
+template <>
+struct Frags<false> {       // two 16-k substeps: [substep][row block] / [substep][column block]
+  bf16x8_t a[2][4];
+  bf16x8_t b[2][kNJ];
 };
 
 __device__ __forceinline__ i32x8_t join16x2(const uint4& lo, const uint4& hi) {
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
-__global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
-  constexpr int KE = kRowBytes;            // codes (k values) per stage
+template <bool FP8, int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
+__global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
+  constexpr int E = FP8 ? 1 : 2;           // bytes per element
+  constexpr int KE = kRowBytes / E;        // k values per stage
   // one array per stage: distinct objects let the compiler see that the
   // LDS-DMA of a later stage cannot alias the reads of the current one
   __shared__ __attribute__((aligned(1024))) uint8_t sm0[kStageBytes];
@@ -78,7 +93,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
   tile_coords(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
-  const uint32_t pitch = (uint32_t)K;      // bytes per operand row (< 2^31, checked by the caller)
+  const uint32_t pitch = (uint32_t)K * E;  // bytes per operand row (< 2^31, checked by the caller)
 
   // ---- loaders: wave w fills tile rows [w R, (w + 1) R) of both operands
   const int rows_a = min(M - m0, kTileM);
@@ -103,7 +118,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
     const int c = (lane % kCpr) ^ chunk_swizzle<kCpr>(r);
     off_a[j] = (uint32_t)r * pitch + c * 16;
     off_b[j] = (uint32_t)(b_first + j * (64 / kCpr) + lane / kCpr) * pitch + c * 16;
-    kc[j] = c * 16;
+    kc[j] = c * (16 / E);
   }
   auto issue_stage = [&](int kt, int s) {
     const int k0 = kt * KE;
@@ -113,8 +128,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
 #pragma unroll
     for (int j = 0; j < kLJ; ++j) {
       const bool out = k0 + kc[j] >= K;
-      load_lds16(rsrc_a, As + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0);
-      load_lds16(rsrc_b, Bs + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0);
+      load_lds16(rsrc_a, As + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0 * E);
+      load_lds16(rsrc_b, Bs + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0 * E);
     }
   };
 
@@ -125,8 +140,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
   int a_off[2], b_off[kNJ][2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    // the lane's 32 k bytes are chunks 2 lh and 2 lh + 1
-    const int c = 2 * lh + h;
+    // fp8: the lane's 32 k bytes are chunks 2 lh and 2 lh + 1; bf16: substep h uses chunk 2 h + lh
+    const int c = FP8 ? 2 * lh + h : 2 * h + lh;
     a_off[h] = (wm * 128 + lr) * kRowBytes + 16 * (c ^ sw);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j)
@@ -144,26 +159,47 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  Frags f;
+  Frags<FP8> f;
   auto read_frags = [&](int s) {
     const uint8_t* S = stage_ptr(s);
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.a[i] = join16x2(*reinterpret_cast<const uint4*>(S + a_off[0] + i * 32 * kRowBytes),
-                        *reinterpret_cast<const uint4*>(S + a_off[1] + i * 32 * kRowBytes));
+      for (int i = 0; i < 4; ++i)
+        f.a[i] = join16x2(*reinterpret_cast<const uint4*>(S + a_off[0] + i * 32 * kRowBytes),
+                          *reinterpret_cast<const uint4*>(S + a_off[1] + i * 32 * kRowBytes));
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j)
-      f.b[j] = join16x2(*reinterpret_cast<const uint4*>(S + b_off[j][0]),
-                        *reinterpret_cast<const uint4*>(S + b_off[j][1]));
+      for (int j = 0; j < kNJ; ++j)
+        f.b[j] = join16x2(*reinterpret_cast<const uint4*>(S + b_off[j][0]),
+                          *reinterpret_cast<const uint4*>(S + b_off[j][1]));
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          f.a[h][i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[h] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) f.b[h][j] = *reinterpret_cast<const bf16x8_t*>(S + b_off[j][h]);
+      }
+    }
   };
   // B fragment first: each lane then holds 4 consecutive output columns
   auto mfmas = [&]() {
+    if constexpr (FP8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-        // cbsz/blgp = 0: both operands E4M3; scales 127 = 2^0 (no block scaling)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+        for (int j = 0; j < kNJ; ++j)
+          // cbsz/blgp = 0: both operands E4M3; scales 127 = 2^0 (no block scaling)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < kNJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
+    }
   };
 
   // ---- ping-pong pipeline.
@@ -208,36 +244,37 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_fp8_kernel(FpArgs a) {
   if (!late) block_barrier();
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the epilogue reuses the LDS
 
-  const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
-  const float scale = (1.0f / sa) * (1.0f / sb);
+  float scale = 1.0f;
+  if constexpr (FP8) {
+    const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
+    scale = (1.0f / sa) * (1.0f / sb);
+  }
   gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, kNJ, 64 * kWaves>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
                                                                        scale, stage_ptr);
 }
 
-template <int ACT, bool GATED>
+template <bool FP8, int ACT, bool GATED>
 hipError_t launch_flags(const FpArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_fp8_kernel<ACT, GATED, false, true, true><<<grid, T, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, false, true><<<grid, T, 0, s>>>(a);
+    if (h) gemm_bt_kernel<FP8, ACT, GATED, false, true, true><<<grid, T, 0, s>>>(a);
+    else gemm_bt_kernel<FP8, ACT, GATED, false, false, true><<<grid, T, 0, s>>>(a);
   } else if (h) {
-    if (out) gemm_fp8_kernel<ACT, GATED, true, true, false><<<grid, T, 0, s>>>(a);
-    else gemm_fp8_kernel<ACT, GATED, false, true, false><<<grid, T, 0, s>>>(a);
+    if (out) gemm_bt_kernel<FP8, ACT, GATED, true, true, false><<<grid, T, 0, s>>>(a);
+    else gemm_bt_kernel<FP8, ACT, GATED, false, true, false><<<grid, T, 0, s>>>(a);
   } else {
-    gemm_fp8_kernel<ACT, GATED, true, false, false><<<grid, T, 0, s>>>(a);
+    gemm_bt_kernel<FP8, ACT, GATED, true, false, false><<<grid, T, 0, s>>>(a);
   }
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b, int64_t K,
-                           const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s) {
-  LaunchScope scope(e.amax != nullptr ? "gemm_fp8_h_amax" : "gemm_fp8", s);
+template <bool FP8>
+hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K, const float* amax_a,
+                     const float* amax_b, const Epilogue& e, hipStream_t s) {
   FpArgs a;
-  a.A = A;
-  a.Bt = Bt;
+  a.A = static_cast<const uint8_t*>(A);
+  a.Bt = static_cast<const uint8_t*>(Bt);
   a.K = (int)K;
   a.amax_a = amax_a;
   a.amax_b = amax_b;
@@ -251,15 +288,34 @@ hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
-#define TE_G(A_) return e.gated ? launch_flags<A_, true>(a, grid, s) : launch_flags<A_, false>(a, grid, s)
-  switch (e.act) {
-    case kRelu: TE_G(kRelu);
-    case kGelu: TE_G(kGelu);
-    case kGeluErf: TE_G(kGeluErf);
-    case kSilu: TE_G(kSilu);
-    default: TE_G(kLinear);
-  }
+  if constexpr (!FP8) {   // the bf16 data-gradient GEMMs have a plain linear epilogue
+    return launch_flags<false, kLinear, false>(a, grid, s);
+  } else {
+#define TE_G(A_) return e.gated ? launch_flags<true, A_, true>(a, grid, s) : launch_flags<true, A_, false>(a, grid, s)
+    switch (e.act) {
+      case kRelu: TE_G(kRelu);
+      case kGelu: TE_G(kGelu);
+      case kGeluErf: TE_G(kGeluErf);
+      case kSilu: TE_G(kSilu);
+      default: TE_G(kLinear);
+    }
 #undef TE_G
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b, int64_t K,
+                           const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s) {
+  LaunchScope scope(e.amax != nullptr ? "gemm_fp8_h_amax" : "gemm_fp8", s);
+  return launch_bt<true>(A, Bt, M, n_b, K, amax_a, amax_b, e, s);
+}
+
+hipError_t launch_gemm_bf16_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K, const Epilogue& e,
+                               hipStream_t s) {
+  if (e.act != kLinear || e.gated || e.h_out != nullptr || e.amax != nullptr) return hipErrorInvalidValue;
+  LaunchScope scope("gemm_bf16_dgrad", s);
+  return launch_bt<false>(A, Bt, M, n_b, K, nullptr, nullptr, e, s);
 }
 
 }  // namespace te

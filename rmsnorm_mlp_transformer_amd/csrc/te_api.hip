@@ -401,6 +401,109 @@ te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, 
   return ok();
 }
 
+// ---------------------------------------------------------------- layernorm MLP backward
+namespace {
+struct MlpBwdWs {
+  void* xn; void* act; void* dact; void* dh1; void* dxn;
+  float* part_dact; float* part_b2; float* part_g; float* part_beta;
+};
+MlpBwdWs mlp_bwd_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int act) {
+  const int64_t g = is_gated(act) ? 2 : 1;
+  MlpBwdWs w{};
+  w.xn = c.take((size_t)rows * hidden * 2);
+  w.act = c.take((size_t)rows * ffn * 2);
+  w.dact = c.take((size_t)rows * ffn * 2);
+  w.dh1 = c.take((size_t)rows * g * ffn * 2);
+  w.dxn = c.take((size_t)rows * hidden * 2);
+  w.part_dact = c.floats((size_t)te::dact_row_chunks(rows, ffn, g == 2) * g * ffn);
+  w.part_b2 = c.floats((size_t)te::dact_row_chunks(rows, hidden, false) * hidden);
+  const int64_t nb = te::norm_bwd_blocks(rows, hidden, TE_BF16);
+  w.part_g = c.floats((size_t)nb * hidden);
+  w.part_beta = c.floats((size_t)nb * hidden);
+  return w;
+}
+}  // namespace
+
+size_t te_layernorm_mlp_bwd_workspace_size(int64_t rows, int64_t hidden, int64_t ffn, te_act_type act_type) {
+  if (rows <= 0 || hidden <= 0 || ffn <= 0) return 0;
+  Carver c(nullptr);
+  mlp_bwd_ws(c, rows, hidden, ffn, act_type);
+  return c.off;
+}
+
+te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamma, const void* beta,
+                               const void* kernel1, const void* kernel2, const float* mu, const float* rsigma,
+                               const void* h1, int64_t rows, int64_t hidden, int64_t ffn, te_dtype dtype,
+                               te_norm_type norm_type, int zero_centered_gamma, float epsilon, te_act_type act_type,
+                               void* dx, void* dgamma, void* dbeta, void* dkernel1, void* dbias1, void* dkernel2,
+                               void* dbias2, te_dtype dparam_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  TE_REQUIRE(dtype == TE_BF16, TE_ERR_UNSUPPORTED, "the backward supports dtype TE_BF16 only");
+  te_status st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
+  if (st != TE_SUCCESS) return st;
+  TE_ARG(feature_ok(ffn), "ffn must be a positive multiple of 16 (at most 2^22), got %lld", (long long)ffn);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  const bool gated = is_gated(act_type), rms = norm_type == TE_RMSNORM;
+  const int64_t nb1 = (gated ? 2 : 1) * ffn;
+  TE_REQUIRE(weight_ok(hidden, nb1, dtype) && weight_ok(ffn, hidden, dtype) && weight_ok(rows, nb1, dtype) &&
+                 weight_ok(rows, hidden, dtype),
+             TE_ERR_UNSUPPORTED, "kernels and [rows, features] activations must be smaller than 2 GiB");
+  TE_REQUIRE(te::norm_bwd_fits(hidden, dtype), TE_ERR_UNSUPPORTED, "hidden too wide for the normalisation backward");
+  TE_ARG(dparam_dtype == TE_F32 || dparam_dtype == TE_BF16, "dparam_dtype must be TE_F32 or TE_BF16");
+  TE_ARG(rows == 0 || (grad != nullptr && h1 != nullptr && rsigma != nullptr && (rms || mu != nullptr) &&
+                       dx != nullptr),
+         "grad, h1, rsigma, (LayerNorm) mu and dx are required");
+  TE_ARG(kernel1 != nullptr && kernel2 != nullptr && dkernel1 != nullptr && dkernel2 != nullptr,
+         "kernels and their gradients are required");
+  TE_ARG(aligned16(grad) && aligned16(h1) && aligned16(dx) && aligned16(kernel1) && aligned16(kernel2) &&
+             aligned16(dkernel1) && aligned16(dkernel2) && aligned16(dgamma) && aligned16(dbeta) &&
+             aligned16(dbias1) && aligned16(dbias2),
+         "pointers must be 16-byte aligned");
+  if (rms) dbeta = nullptr;
+  const size_t need = te_layernorm_mlp_bwd_workspace_size(rows, hidden, ffn, act_type);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
+  hipStream_t s = as_stream(stream);
+  const int64_t ps = esize(dparam_dtype);
+  if (rows == 0) {   // every parameter gradient of an empty batch is zero
+    TE_HIP(te::launch_fill_zero_bytes(dkernel1, hidden * nb1 * 2, s), "fill");
+    TE_HIP(te::launch_fill_zero_bytes(dkernel2, ffn * hidden * 2, s), "fill");
+    for (void* p : {dgamma, dbeta, dbias2})
+      if (p != nullptr) TE_HIP(te::launch_fill_zero_bytes(p, hidden * ps, s), "fill");
+    if (dbias1 != nullptr) TE_HIP(te::launch_fill_zero_bytes(dbias1, nb1 * ps, s), "fill");
+    return ok();
+  }
+  Carver c(workspace);
+  MlpBwdWs w = mlp_bwd_ws(c, rows, hidden, ffn, act_type);
+  const int k = act_kind(act_type);
+  const te::Epilogue lin{nullptr, nullptr, nullptr, nullptr, te::kLinear, false};
+  // the normalised input (GEMM1's A operand) and the activation output, recomputed
+  TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zero_centered_gamma != 0, epsilon, te::kNormStore,
+                         dtype, w.xn, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
+  TE_HIP(te::launch_act(h1, rows, ffn, dtype, k, gated, 0, w.act, dtype, nullptr, nullptr, nullptr, s), "act");
+  // GEMM2: dact = grad @ kernel2^T, dkernel2 = act^T @ grad, dbias2 = sum of grad
+  te::Epilogue e = lin;
+  e.out = w.dact;
+  TE_HIP(te::launch_gemm_bf16_bt(grad, kernel2, rows, ffn, hidden, e, s), "dgrad2");
+  e.out = dkernel2;
+  TE_HIP(te::launch_gemm_bf16_at(w.act, grad, ffn, hidden, rows, e, s), "wgrad2");
+  if (dbias2 != nullptr) TE_HIP(te::launch_colsum(grad, rows, hidden, dtype, dbias2, dparam_dtype, w.part_b2, s), "dbias2");
+  // activation backward with dbias1
+  TE_HIP(te::launch_dact_dbias(w.dact, h1, rows, ffn, dtype, k, gated, w.dh1, dbias1, dparam_dtype, w.part_dact, s),
+         "dact");
+  // GEMM1: dxn = dh1 @ kernel1^T, dkernel1 = xn^T @ dh1
+  e.out = w.dxn;
+  TE_HIP(te::launch_gemm_bf16_bt(w.dh1, kernel1, rows, hidden, nb1, e, s), "dgrad1");
+  e.out = dkernel1;
+  TE_HIP(te::launch_gemm_bf16_at(w.xn, w.dh1, hidden, nb1, rows, e, s), "wgrad1");
+  // normalisation backward
+  TE_HIP(te::launch_norm_bwd(w.dxn, x, mu, rsigma, gamma, rows, hidden, dtype, rms, zero_centered_gamma != 0, dx,
+                             dgamma, dbeta, dparam_dtype, w.part_g, w.part_beta, s),
+         "norm backward");
+  return ok();
+}
+
 // ---------------------------------------------------------------- normalisation backward
 size_t te_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden, te_dtype dtype) {
   if (rows <= 0 || hidden <= 0) return 0;

@@ -81,6 +81,10 @@ int64_t dact_blocks(int64_t rows, int64_t cols, bool gated);
 hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,
                              int dtype, int act, bool gated, void* dx, void* dbias,
                              int dbias_dtype, float* partials, hipStream_t s);
+// Column sums of x [rows, cols] (fp32, fixed order) into sum [cols];
+// partials: dact_row_chunks(rows, cols, false) * cols floats.
+hipError_t launch_colsum(const void* x, int64_t rows, int64_t cols, int dtype, void* sum, int sum_dtype,
+                         float* partials, hipStream_t s);
 // dact + dbias with the activation gradient quantised to E4M3 (current
 // scaling): pass 1 computes dx for the bias partials and per-workgroup amax
 // partials (amax_part: dact_blocks() floats), a one-workgroup kernel reduces
@@ -107,6 +111,15 @@ struct Epilogue {
 // bf16: C[M, n_out] from A [M, K] (row-major) and B [K, n_b] (row-major).
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
                             const Epilogue& ep, hipStream_t s);
+
+// bf16 with B^T [n_b, K] (both operands K-contiguous), linear epilogue
+// (optional bias): the data-gradient GEMMs of the backward.
+hipError_t launch_gemm_bf16_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K,
+                               const Epilogue& ep, hipStream_t s);
+// bf16 with A^T [K, M] and B [K, n_b] (both row-major with K the row index),
+// linear epilogue: the weight-gradient GEMMs of the backward.
+hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t n_b, int64_t K,
+                               const Epilogue& ep, hipStream_t s);
 
 // fp8: A codes [M, K] and B^T codes [n_b, K] (both K-contiguous); the
 // accumulator is multiplied by scale_inv(amax_a) * scale_inv(amax_b).
