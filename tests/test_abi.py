@@ -178,6 +178,20 @@ def test_norm_act_dact_quant_validation():
                                 None) == B.TE_ERR_UNSUPPORTED
     assert lib.te_layernorm_bwd(P, P, P, P, P, 64, 40, B.TE_BF16, B.TE_LAYERNORM, 0, P, P, P, B.TE_F32, P, nb,
                                 None) == B.TE_ERR_INVALID_ARGUMENT
+    # LayerNorm-MLP backward
+    nm = lib.te_layernorm_mlp_bwd_workspace_size(256, 512, 1024, B.TE_ACT_GELU)
+    assert nm > lib.te_layernorm_mlp_bwd_workspace_size(128, 512, 1024, B.TE_ACT_GELU) > 0
+    assert lib.te_layernorm_mlp_bwd_workspace_size(256, 512, 1024, B.TE_ACT_SWIGLU) > nm
+
+    def mlp_bwd(dtype=B.TE_BF16, ffn=1024, act=B.TE_ACT_GELU, mu=P, h1=P, ws=nm, norm=B.TE_LAYERNORM):
+        return lib.te_layernorm_mlp_bwd(P, P, P, P, P, P, mu, P, h1, 256, 512, ffn, dtype, norm, 0, 1e-6, act,
+                                        P, P, P, P, P, P, P, B.TE_F32, P, ws, None)
+    assert mlp_bwd(dtype=B.TE_F32) == B.TE_ERR_UNSUPPORTED
+    assert mlp_bwd(ws=nm - 1) == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert mlp_bwd(ffn=1000) == B.TE_ERR_INVALID_ARGUMENT
+    assert mlp_bwd(mu=None) == B.TE_ERR_INVALID_ARGUMENT
+    assert mlp_bwd(h1=None) == B.TE_ERR_INVALID_ARGUMENT
+    assert mlp_bwd(act=99) == B.TE_ERR_INVALID_ARGUMENT
     # quantiser
     assert lib.te_quantize(P, 24, B.TE_BF16, P, ctypes.byref(m), None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_quantize(P, 32, B.TE_BF16, P, None, None) == B.TE_ERR_INVALID_ARGUMENT
