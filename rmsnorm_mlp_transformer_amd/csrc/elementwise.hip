@@ -28,15 +28,16 @@ __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
-// Load 8 consecutive elements (bf16: one 16-byte load; fp32: two).
+// Load 8 consecutive elements (bf16: one 16-byte load; fp32: two), streaming.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, int64_t e, float* f) {
   if constexpr (BF16) {
-    unpack8_bf16(*reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + e), f);
+    unpack8_bf16(load_stream16(reinterpret_cast<const uint16_t*>(base) + e), f);
   } else {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + e);
-    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + e + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    const uint4 a = load_stream16(reinterpret_cast<const float*>(base) + e);
+    const uint4 b = load_stream16(reinterpret_cast<const float*>(base) + e + 4);
+    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
   }
 }
 template <bool BF16>
@@ -261,10 +262,11 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 }
 
 // ------------------------------------------------------------------ dact + dbias
-// Block = 8 waves over one strip of 512 output columns (8 per lane) and one
-// chunk of rows; wave w takes rows w, w+8, ... of the chunk, 4 rows per
-// iteration so that each lane has 8 (gated 12) 16-byte loads in flight. Each
-// lane keeps fp32 column sums in registers; the 8 waves are combined in LDS
+// Block = W waves over one strip of 512 output columns (8 per lane) and one
+// short chunk of rows (about 32: many small blocks balance well over the
+// CUs); wave w takes rows w, w+W, ... of the chunk, 4 rows per iteration so
+// that each lane has 8 (gated 12) 16-byte streaming loads in flight. Each
+// lane keeps fp32 column sums in registers; the W waves are combined in LDS
 // in a fixed order and every block writes one row of fp32 partials, which
 // dbias_finalize sums in a fixed order (bitwise reproducible).
 // MODE kDactStore writes dx; kDactAmax writes no dx but the block's max |dx|
@@ -272,9 +274,18 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 // codes of dx * scale, the scale coming from the finished amax; kDactSum
 // writes nothing but the column partials (with the linear activation this is
 // the bias gradient sum over rows of grad).
+#ifndef TE_DACT_WAVES
+#define TE_DACT_WAVES 4
+#endif
+#ifndef TE_DACT_UNROLL
+#define TE_DACT_UNROLL 4
+#endif
+#ifndef TE_DACT_TARGET_BLOCKS
+#define TE_DACT_TARGET_BLOCKS 8192
+#endif
 constexpr int kDactStrip = 512;
-constexpr int kDactWaves = 8;
-constexpr int kDactUnroll = 4;
+constexpr int kDactWaves = TE_DACT_WAVES;
+constexpr int kDactUnroll = TE_DACT_UNROLL;
 enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2, kDactSum = 3 };
 
 template <bool BF16, int ACT, bool GATED, int MODE>
@@ -399,25 +410,41 @@ __global__ void __launch_bounds__(kThreads) amax_finalize_kernel(const float* pa
   }
 }
 
+// Column sums of the per-chunk partials. A block owns 64 columns (one per
+// lane, 256-byte rows of partials) and its 8 waves sum disjoint, contiguous
+// ranges of chunks, 8 loads in flight per lane; the wave sums are then added
+// in wave order, so the result does not depend on timing.
+constexpr int kFinWaves = 8;
 template <int OUT>
-__global__ void __launch_bounds__(kThreads) dbias_finalize_kernel(const float* partials, int64_t chunks,
-                                                                  int64_t n, void* dbias) {
-  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (c >= n) return;
-  // 8 loads in flight per lane; the sum still runs over k = 0, 1, 2, ... in order
-  constexpr int U = 8;
+__global__ void __launch_bounds__(64 * kFinWaves) dbias_finalize_kernel(const float* partials, int64_t chunks,
+                                                                        int64_t n, void* dbias) {
+  __shared__ float red[kFinWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t per = (chunks + kFinWaves - 1) / kFinWaves;
+  const int64_t k1 = min((w + 1) * per, chunks);
   float s = 0.0f;
-  int64_t k = 0;
-  for (; k + U <= chunks; k += U) {
-    float v[U];
+  if (c < n) {
+    constexpr int U = 8;
+    int64_t k = w * per;
+    for (; k + U <= k1; k += U) {
+      float v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = partials[(k + u) * n + c];
+      for (int u = 0; u < U; ++u) v[u] = partials[(k + u) * n + c];
 #pragma unroll
-    for (int u = 0; u < U; ++u) s += v[u];
+      for (int u = 0; u < U; ++u) s += v[u];
+    }
+    for (; k < k1; ++k) s += partials[k * n + c];
   }
-  for (; k < chunks; ++k) s += partials[k * n + c];
-  if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(dbias)[c] = f32_to_bf16(s);
-  else reinterpret_cast<float*>(dbias)[c] = s;
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && c < n) {
+    float t = red[0][lane];
+#pragma unroll
+    for (int q = 1; q < kFinWaves; ++q) t += red[q][lane];
+    if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(dbias)[c] = f32_to_bf16(t);
+    else reinterpret_cast<float*>(dbias)[c] = t;
+  }
 }
 
 template <bool BF16>
@@ -519,7 +546,7 @@ hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, in
 int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated) {
   (void)gated;
   const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
-  int64_t chunks = (2048 + strips - 1) / strips;     // aim for ~2048 blocks (8 per CU)
+  int64_t chunks = (TE_DACT_TARGET_BLOCKS + strips - 1) / strips;     // aim for ~8192 blocks (32 per CU)
   const int64_t max_chunks = (rows + 15) / 16;         // at least 16 rows per block
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
@@ -559,9 +586,9 @@ hipError_t dbias_finalize(const float* partials, int64_t rows, int64_t cols, boo
   LaunchScope scope("dbias_finalize", s);
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
   const int64_t n = (gated ? 2 : 1) * cols;
-  const unsigned g2 = (unsigned)((n + kThreads - 1) / kThreads);
-  if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
-  else dbias_finalize_kernel<kF32><<<g2, kThreads, 0, s>>>(partials, chunks, n, dbias);
+  const unsigned g2 = (unsigned)((n + 63) / 64);
+  if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, 64 * kFinWaves, 0, s>>>(partials, chunks, n, dbias);
+  else dbias_finalize_kernel<kF32><<<g2, 64 * kFinWaves, 0, s>>>(partials, chunks, n, dbias);
   return hipGetLastError();
 }
 }  // namespace

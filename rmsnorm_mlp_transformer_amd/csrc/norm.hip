@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
       for (int j = 0; j < NCH; ++j) {
         const int64_t c = lane + 64 * j;
         if (c < nch) {
-          I::unpack(xr[c], v[j]);
+          I::unpack(load_stream16(xr + c), v[j]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) v[j][i] = 0.0f;

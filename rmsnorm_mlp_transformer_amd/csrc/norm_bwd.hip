@@ -85,8 +85,8 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, valid ? (int)row_bytes : 0,
                                              0x00020000);
   };
-  auto load16 = [&](__amdgpu_buffer_rsrc_t r, int64_t c) {
-    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)c * 16, 0, 0);
+  auto load16 = [&](__amdgpu_buffer_rsrc_t r, int64_t c) {   // streaming: every row is read once
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)c * 16, 0, kBufAuxStream);
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
   };
   float g[2][VEC];
