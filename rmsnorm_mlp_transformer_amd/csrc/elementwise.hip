@@ -60,6 +60,93 @@ __device__ __forceinline__ uint2 encode8(const float* f, float scale) {
   return make_uint2(w0, w1);
 }
 
+// Products and sums that must round the same way in every kernel that forms
+// them (the dact variants must give bitwise equal bias gradients): no fusion
+// into an fma.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+// Raw buffer access (32-bit byte offsets inside one descriptor): a lane's
+// offset plus a wave-uniform soffset, so that the unrolled row loop costs no
+// 64-bit address arithmetic. Accesses at or past the descriptor's size read
+// zeros and are dropped when storing.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc buf_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// 8 elements as raw 16-byte words (bf16: one, fp32: two), unpacked later so
+// that a wave can keep all of its loads in flight before the first use.
+template <bool BF16>
+struct Raw8 {
+  i32x4_t w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ void load8_raw(Rsrc r, uint32_t voff, uint32_t soff, Raw8<BF16>& d) {
+  d.w[0] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufAuxStream);
+  if constexpr (!BF16) d.w[1] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kBufAuxStream);
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack8_raw(const Raw8<BF16>& d, float* f) {
+  if constexpr (BF16) {
+    unpack8_bf16(make_uint4((uint32_t)d.w[0][0], (uint32_t)d.w[0][1], (uint32_t)d.w[0][2], (uint32_t)d.w[0][3]), f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = __int_as_float(d.w[0][i]); f[4 + i] = __int_as_float(d.w[1][i]); }
+  }
+}
+// The same from a plain pointer (element offset e).
+template <bool BF16>
+__device__ __forceinline__ void load8_raw_ptr(const void* base, int64_t e, Raw8<BF16>& d) {
+  const uint8_t* p = reinterpret_cast<const uint8_t*>(base) + e * (BF16 ? 2 : 4);
+  const uint4 a = load_stream16(p);
+  d.w[0] = i32x4_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+  if constexpr (!BF16) {
+    const uint4 b = load_stream16(p + 16);
+    d.w[1] = i32x4_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void load8_buf(Rsrc r, uint32_t voff, uint32_t soff, float* f) {
+  const i32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufAuxStream);
+  if constexpr (BF16) {
+    unpack8_bf16(make_uint4((uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3]), f);
+  } else {
+    const i32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kBufAuxStream);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = __int_as_float(a[i]); f[4 + i] = __int_as_float(b[i]); }
+  }
+}
+// Stores fold the row offset into the lane offset and pass a zero soffset:
+// a 16-byte store whose data registers a VALU instruction rewrites right
+// after it needs one wait state, and the compiler only inserts it for stores
+// without a register soffset (with one, lanes 12-15 of each 16 were seen to
+// store the rewritten values).
+template <bool BF16>
+__device__ __forceinline__ void store8_buf(Rsrc r, uint32_t voff, uint32_t soff, const float* f) {
+  const uint32_t o = voff + soff;
+  if constexpr (BF16) {
+    const uint4 v = pack8_bf16(f);
+    const i32x4_t w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, o, 0, 0);
+  } else {
+    const i32x4_t a = {__float_as_int(f[0]), __float_as_int(f[1]), __float_as_int(f[2]), __float_as_int(f[3])};
+    const i32x4_t b = {__float_as_int(f[4]), __float_as_int(f[5]), __float_as_int(f[6]), __float_as_int(f[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(a, r, o, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, o + 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void store8_codes_buf(Rsrc r, uint32_t voff, uint32_t soff, uint2 c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2_t;
+  const i32x2_t w = {(int)c.x, (int)c.y};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, voff + soff, 0, 0);
+}
+
 unsigned grid_for(int64_t work_items, int per_thread) {
   int64_t blocks = (work_items + (int64_t)kThreads * per_thread - 1) / ((int64_t)kThreads * per_thread);
   if (blocks < 1) blocks = 1;
@@ -97,21 +184,19 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const void* x, int64_t n
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < n8; c0 += stride * kUnroll) {
-    float f[kUnroll][8];
+    // chunks past the end re-read the last one (no change to the max), so
+    // every load is unconditional and all are in flight before the first use
+    Raw8<BF16> w[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load8_raw_ptr<BF16>(x, min(c0 + u * stride, n8 - 1) * 8, w[u]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = c0 + u * stride;
-      if (c < n8) {
-        load8<BF16>(x, c * 8, f[u]);
-      } else {
+      float f[8];
+      unpack8_raw<BF16>(w[u], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[u][i] = 0.0f;
-      }
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[u][i]));
   }
   __shared__ float red[kThreads / 64];
   block_max_atomic(m, amax, red);
@@ -129,16 +214,18 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64
   constexpr int U = 4;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < n8; c0 += stride * U) {
-    float f[U][8];
+    // unconditional loads (past the end: the last chunk again), all in flight
+    // before the first use; only the stores are guarded
+    Raw8<BF16> w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load8_raw_ptr<BF16>(x, min(c0 + u * stride, n8 - 1) * 8, w[u]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + u * stride;
-      if (c < n8) load8<BF16>(x, c * 8, f[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + u * stride;
-      if (c < n8) *reinterpret_cast<uint2*>(codes + c * 8) = encode8(f[u], scale);
+      float f[8];
+      unpack8_raw<BF16>(w[u], f);
+      if (c < n8) *reinterpret_cast<uint2*>(codes + c * 8) = encode8(f, scale);
     }
   }
 }
@@ -159,18 +246,23 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
   const int64_t tiles_c = (cols + 63) / 64;
   const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
   const int t = threadIdx.x;
-  // read: 64 rows x 8 column-chunks = 512 chunks, 2 per thread
+  // read: 64 rows x 8 column-chunks = 512 chunks, 2 per thread, both loads in
+  // flight before the first use. Chunks outside the matrix re-read a clamped
+  // in-range chunk: their codes land in tile cells that are never stored.
+  Raw8<BF16> w[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int idx = t + p * kThreads;
+    const int r = idx >> 3, cc = (idx & 7) * 8;
+    load8_raw_ptr<BF16>(x, min(r0 + r, rows - 1) * cols + min(c0 + cc, cols - 8), w[p]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int idx = t + p * kThreads;
     const int r = idx >> 3, cc = (idx & 7) * 8;
     float f[8];
-    if (r0 + r < rows && c0 + cc < cols) {
-      load8<BF16>(x, (r0 + r) * cols + c0 + cc, f);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) f[i] = 0.0f;
-    }
+    unpack8_raw<BF16>(w[p], f);
 #pragma unroll
     for (int i = 0; i < 8; ++i) tile[cc + i][r] = (uint8_t)e4m3_encode(f[i] * scale);
   }
@@ -283,6 +375,9 @@ dim3 act_grid(int64_t rows, int64_t cols) {
 #ifndef TE_DACT_TARGET_BLOCKS
 #define TE_DACT_TARGET_BLOCKS 8192
 #endif
+#ifndef TE_DACT_RESIDENT_BLOCKS
+#define TE_DACT_RESIDENT_BLOCKS 8192
+#endif
 constexpr int kDactStrip = 512;
 constexpr int kDactWaves = TE_DACT_WAVES;
 constexpr int kDactUnroll = TE_DACT_UNROLL;
@@ -295,64 +390,88 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
                                                                const float* amax) {
   constexpr int G = GATED ? 2 : 1;
   constexpr int W = kDactWaves, U = kDactUnroll;
+  constexpr int64_t ES = BF16 ? 2 : 4;                    // bytes per input / dx element
+  constexpr int64_t OS = MODE == kDactQuant ? 1 : ES;     // bytes per output element
   __shared__ float red[W][G][kDactStrip];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int64_t col = (int64_t)blockIdx.x * kDactStrip + lane * 8;
-  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_chunk;
-  int64_t r_end = r_begin + rows_per_chunk;
-  if (r_end > rows) r_end = rows;
   const int64_t xcols = G * cols;
+  const int64_t nchunks = (rows + rows_per_chunk - 1) / rows_per_chunk;
+  const bool writes = MODE == kDactStore || MODE == kDactQuant;
+  // the lane's offsets in row w of a chunk; row w + k is k row pitches further (soffset)
+  const uint32_t vg = (uint32_t)((w * cols + col) * ES);
+  const uint32_t vx = (uint32_t)((w * xcols + col) * ES);
+  const uint32_t vd = (uint32_t)((w * xcols + col) * OS);
   float qscale = 1.0f;
   if constexpr (MODE == kDactQuant) qscale = fp8_scale_from_amax(*amax);
   float sa[8], sb[8], m = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { sa[i] = 0.0f; sb[i] = 0.0f; }
-  // one output chunk of 8 values at element offset e: bf16/fp32 dx, or codes
-  auto emit = [&](int64_t e, const float* d) {
-    if constexpr (MODE == kDactStore) {
-      store8<BF16>(dx, e, d);
-    } else if constexpr (MODE == kDactAmax) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(d[i]));
-    } else if constexpr (MODE == kDactQuant) {
-      *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(dx) + e) = encode8(d, qscale);
-    }
-  };
   if (col < cols) {
-    for (int64_t r0 = r_begin + w; r0 < r_end; r0 += W * U) {
-      float g[U][8], a[U][8], b[U][8];
+    // chunks blockIdx.y, blockIdx.y + gridDim.y, ...: the sums run over all of them
+    for (int64_t ch = blockIdx.y; ch < nchunks; ch += gridDim.y) {
+      const int64_t r_begin = ch * rows_per_chunk;
+      const int64_t nr = min(rows_per_chunk, rows - r_begin);   // rows of this chunk, >= 1
+      // descriptors over the chunk's rows (below 2 GiB: the host sizes the chunks)
+      const Rsrc rg = buf_rsrc(reinterpret_cast<const uint8_t*>(grad) + r_begin * cols * ES, nr * cols * ES);
+      const Rsrc rx = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + r_begin * xcols * ES, nr * xcols * ES);
+      const Rsrc rd = buf_rsrc(writes ? reinterpret_cast<const uint8_t*>(dx) + r_begin * xcols * OS : nullptr,
+                               writes ? nr * xcols * OS : 0);
+      // one output chunk of 8 values at byte offset voff (+ soff) of the chunk's dx
+      auto emit = [&](uint32_t voff, uint32_t soff, const float* d) {
+        if constexpr (MODE == kDactStore) {
+          store8_buf<BF16>(rd, voff, soff, d);
+        } else if constexpr (MODE == kDactAmax) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t r = r0 + (int64_t)u * W;
-        if (r < r_end) {
-          load8<BF16>(grad, r * cols + col, g[u]);
-          load8<BF16>(x, r * xcols + col, a[u]);
-          if constexpr (GATED) load8<BF16>(x, r * xcols + cols + col, b[u]);
+          for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(d[i]));
+        } else if constexpr (MODE == kDactQuant) {
+          store8_codes_buf(rd, voff, soff, encode8(d, qscale));
         }
-      }
+      };
+      // rows past the chunk (the last iteration's tail) load as zero, which adds
+      // nothing to the sums or the amax, and their stores are dropped
+      for (int64_t r0 = 0; r0 < nr; r0 += W * U) {
+        Raw8<BF16> gw[U], aw[U], bw[GATED ? U : 1];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t r = r0 + (int64_t)u * W;
-        if (r < r_end) {
+        for (int u = 0; u < U; ++u) {
+          const int64_t rr = r0 + (int64_t)u * W;
+          load8_raw<BF16>(rg, vg, (uint32_t)(rr * cols * ES), gw[u]);
+          load8_raw<BF16>(rx, vx, (uint32_t)(rr * xcols * ES), aw[u]);
+          if constexpr (GATED) load8_raw<BF16>(rx, vx + (uint32_t)(cols * ES), (uint32_t)(rr * xcols * ES), bw[u]);
+        }
+        // every load of the step is issued before the first use (left to itself the
+        // scheduler interleaves load, wait and unpack, one load in flight at a time)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t rr = r0 + (int64_t)u * W;
+          const uint32_t so = (uint32_t)(rr * xcols * OS);
+          float g[1][8], a[1][8], b[1][8];
+          unpack8_raw<BF16>(gw[u], g[0]);
+          unpack8_raw<BF16>(aw[u], a[0]);
+          if constexpr (GATED) unpack8_raw<BF16>(bw[u], b[0]);
           float d[8];
           if constexpr (GATED) {
             float db[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              d[i] = g[u][i] * b[u][i] * act_bwd<ACT>(a[u][i]);
-              db[i] = g[u][i] * act_fwd<ACT>(a[u][i]);
-              sa[i] += d[i];
-              sb[i] += db[i];
+              float f, df;
+              act_fwd_bwd<ACT>(a[0][i], f, df);
+              d[i] = mul_rn(mul_rn(g[0][i], b[0][i]), df);
+              db[i] = mul_rn(g[0][i], f);
+              sa[i] = add_rn(sa[i], d[i]);
+              sb[i] = add_rn(sb[i], db[i]);
             }
-            emit(r * xcols + col, d);
-            emit(r * xcols + cols + col, db);
+            emit(vd, so, d);
+            emit(vd + (uint32_t)(cols * OS), so, db);
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              d[i] = g[u][i] * act_bwd<ACT>(a[u][i]);
-              sa[i] += d[i];
+              d[i] = mul_rn(g[0][i], act_bwd<ACT>(a[0][i]));
+              sa[i] = add_rn(sa[i], d[i]);
             }
-            emit(r * xcols + col, d);
+            emit(vd, so, d);
           }
         }
       }
@@ -543,14 +662,34 @@ hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, in
   return act_dispatch<false>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
 }
 
-int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated) {
-  (void)gated;
+namespace {
+// Rows per dact work chunk: about TE_DACT_TARGET_BLOCKS chunks in all, at
+// least 16 rows each, and a chunk's rows of x (fp32, gated: 2 cols) below
+// 2 GiB so that one buffer descriptor with 32-bit offsets covers them.
+int64_t dact_rows_per_chunk(int64_t rows, int64_t cols, bool gated) {
   const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
-  int64_t chunks = (TE_DACT_TARGET_BLOCKS + strips - 1) / strips;     // aim for ~8192 blocks (32 per CU)
-  const int64_t max_chunks = (rows + 15) / 16;         // at least 16 rows per block
+  int64_t chunks = (TE_DACT_TARGET_BLOCKS + strips - 1) / strips;
+  const int64_t max_chunks = (rows + 15) / 16;
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
-  return chunks;
+  int64_t rpc = (rows + chunks - 1) / chunks;
+  const int64_t row_bytes = (gated ? 2 : 1) * cols * 4;
+  const int64_t max_rpc = (((int64_t)1 << 31) - 1) / row_bytes;
+  if (rpc > max_rpc) rpc = max_rpc;
+  return rpc < 1 ? 1 : rpc;
+}
+}  // namespace
+
+// Workgroups along the row axis (= rows of partial column sums): one per
+// work chunk, at most about TE_DACT_RESIDENT_BLOCKS workgroups in all; a
+// workgroup then takes every gridDim.y-th chunk.
+int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated) {
+  if (rows <= 0) return 1;
+  const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
+  const int64_t work = (rows + rpc - 1) / rpc;
+  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
+  const int64_t cap = max((int64_t)1, (int64_t)TE_DACT_RESIDENT_BLOCKS / strips);
+  return work < cap ? work : cap;
 }
 
 int64_t dact_blocks(int64_t rows, int64_t cols, bool gated) {
@@ -562,7 +701,7 @@ template <int MODE>
 hipError_t dact_dispatch(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype, int act, bool gated,
                          void* dx, float* partials, float* amax_part, const float* amax, hipStream_t s) {
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
-  const int64_t rpc = (rows + chunks - 1) / chunks;
+  const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
   const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
 #define TE_DACT(B, A, G) dact_kernel<B, A, G, MODE><<<grid, 64 * kDactWaves, 0, s>>>(grad, x, rows, cols, rpc, dx, partials, amax_part, amax)
 #define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);

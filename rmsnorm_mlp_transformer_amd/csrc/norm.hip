@@ -13,6 +13,8 @@
 // zero_centered_gamma, epsilon): LayerNorm y = (x - mean) / sqrt(var + eps)
 // * g + beta with the biased variance; RMSNorm y = x / sqrt(mean(x^2) + eps)
 // * g; g = 1 + gamma for a zero-centred gamma.
+#include <type_traits>
+
 #include "te_common.hpp"
 #include "te_kernels.hpp"
 
@@ -94,22 +96,42 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
     }
   }
   float lmax = 0.0f;
+  // byte-range descriptors: chunks past the row (lane + 64 j >= nch) read as zero
+  const uint32_t row_bytes = (uint32_t)(nch * 16);
+  const __amdgpu_buffer_rsrc_t rgam = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.gamma), (short)0,
+                                                                        (int)row_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rbet = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(RMS ? a.gamma : a.beta),
+                                                                        (short)0, (int)row_bytes, 0x00020000);
+  auto load16 = [&](__amdgpu_buffer_rsrc_t r, int64_t c, auto stream) {
+    const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)c * 16, 0, decltype(stream)::value ? kBufAuxStream : 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+  };
+  using Stream = std::true_type;
+  using Cached = std::false_type;
   // one wave per row (the loop covers grids smaller than rows / 4)
-  for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < a.rows; row += (int64_t)gridDim.x * 4) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
     const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
     float mean = 0.0f, rs;
     if constexpr (NCH > 0) {
+      // all of the row's loads (x, gamma, beta) are issued before the first
+      // use, so that a wave has them in flight together
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(xr), (short)0,
+                                                                          (int)row_bytes, 0x00020000);
+      uint4 xw[NCH], gw[NCH], bw[NCH];
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) xw[j] = load16(rx, lane + 64 * j, Stream{});
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        gw[j] = load16(rgam, lane + 64 * j, Cached{});
+        if constexpr (!RMS) bw[j] = load16(rbet, lane + 64 * j, Cached{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float v[NCH][VEC];
       float s = 0.0f;
 #pragma unroll
       for (int j = 0; j < NCH; ++j) {
-        const int64_t c = lane + 64 * j;
-        if (c < nch) {
-          I::unpack(load_stream16(xr + c), v[j]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) v[j][i] = 0.0f;
-        }
+        I::unpack(xw[j], v[j]);
         if constexpr (!RMS) {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) s += v[j][i];
@@ -139,8 +161,8 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
         const int64_t c = lane + 64 * j;
         if (c < nch) {
           float g[VEC], b[VEC], y[VEC];
-          I::unpack(gr[c], g);
-          if constexpr (!RMS) I::unpack(br[c], b);
+          I::unpack(gw[j], g);
+          if constexpr (!RMS) I::unpack(bw[j], b);
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
             const float gi = a.zcg ? 1.0f + g[i] : g[i];

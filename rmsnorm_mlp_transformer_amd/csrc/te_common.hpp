@@ -46,8 +46,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 b = (__bf16)f;
   return __builtin_bit_cast(uint16_t, b);
 }
+// Two values in one v_cvt_pk_bf16_f32 (round to nearest even), lo in bits 15:0.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  const f32x2_v f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_v));
 }
 
 // OCP E4M3 encoder: saturate to +-448, then round to nearest even on the
@@ -96,9 +100,17 @@ constexpr float kGeluD1 = 6.0f * 0.7978845608028654f * 0.044715f;
 
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// tanh(u) = 1 - 2 / (1 + e^(2u)); saturates cleanly to +-1 for large |u|.
-__device__ __forceinline__ float tanh_fast(float u) {
-  return 1.0f - 2.0f * fast_rcp(1.0f + __expf(2.0f * u));
+// GELU (tanh form) and its derivative from one sigmoid: with s = sigmoid(2u),
+// u = K0 (x + K1 x^3), gelu = x s and
+// gelu' = s + x s (1 - s) 2u' = s (1 + (x - x s) (2 K0 + 6 K0 K1 x^2)).
+// Past |x| = 20 s is exactly 0 or 1 in fp32; the clamp (med3) keeps x^2
+// finite (no 0 * inf), and the unclamped x still carries a NaN through.
+__device__ __forceinline__ void gelu_fwd_bwd(float x, float& f, float& d) {
+  const float xc = __builtin_amdgcn_fmed3f(x, -20.0f, 20.0f);
+  const float x2 = xc * xc;
+  const float s = fast_rcp(1.0f + __builtin_amdgcn_exp2f(xc * fmaf(kGeluE1, x2, kGeluE0)));
+  f = x * s;
+  d = s * fmaf(fmaf(-x, s, x), fmaf(kGeluD1, x2, kGeluD0), 1.0f);
 }
 
 template <int A>
@@ -124,14 +136,9 @@ __device__ __forceinline__ float act_bwd(float x) {
   if constexpr (A == kRelu) {
     return x > 0.0f ? 1.0f : 0.0f;
   } else if constexpr (A == kGelu) {
-    // with s = sigmoid(2u), u = K0 (x + K1 x^3): gelu = x s and
-    // gelu' = s + x s (1 - s) 2u' = s (1 + x (1 - s) (2 K0 + 6 K0 K1 x^2)).
-    // Past |x| = 20 s is 0 or 1 in fp32; clamping there keeps x^2 finite
-    // (no 0 * inf), while the unclamped x still carries a NaN through.
-    const float xc = fminf(fmaxf(x, -20.0f), 20.0f);
-    const float x2 = xc * xc;
-    const float s = fast_rcp(1.0f + __builtin_amdgcn_exp2f(xc * fmaf(kGeluE1, x2, kGeluE0)));
-    return s * fmaf(x * (1.0f - s), fmaf(kGeluD1, x2, kGeluD0), 1.0f);
+    float f, d;
+    gelu_fwd_bwd(x, f, d);
+    return d;
   } else if constexpr (A == kGeluErf) {
     return 0.5f * (1.0f + erff(x * kInvSqrt2)) + x * __expf(-0.5f * x * x) * kInvSqrt2Pi;
   } else if constexpr (A == kSilu) {
@@ -139,6 +146,22 @@ __device__ __forceinline__ float act_bwd(float x) {
     return s * (1.0f + x * (1.0f - s));
   } else {
     return 1.0f;
+  }
+}
+
+// Both the activation and its derivative at x (the gated backward needs the
+// two), sharing the exponential where the forms allow.
+template <int A>
+__device__ __forceinline__ void act_fwd_bwd(float x, float& f, float& d) {
+  if constexpr (A == kGelu) {
+    gelu_fwd_bwd(x, f, d);
+  } else if constexpr (A == kSilu) {
+    const float s = fast_rcp(1.0f + __expf(-x));
+    f = x * s;
+    d = s * (1.0f + x * (1.0f - s));
+  } else {
+    f = act_fwd<A>(x);
+    d = act_bwd<A>(x);
   }
 }
 
