@@ -509,19 +509,28 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
   }
 }
 
-// Max over the per-block partial amaxes; writes amax, scale, scale_inv.
-__global__ void __launch_bounds__(kThreads) amax_finalize_kernel(const float* part, int64_t n, float* amax,
-                                                                  float* scale, float* scale_inv) {
+// Max over the per-block partial amaxes; writes amax, scale, scale_inv. One
+// workgroup of 1024 threads, 8 loads in flight per lane.
+constexpr int kFinThreads = 1024;
+__global__ void __launch_bounds__(kFinThreads) amax_finalize_kernel(const float* part, int64_t n, float* amax,
+                                                                     float* scale, float* scale_inv) {
   float m = 0.0f;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) m = fmaxf(m, part[i]);
-  __shared__ float red[kThreads / 64];
+  constexpr int U = 8;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kFinThreads * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = part[min(i0 + (int64_t)u * kFinThreads, n - 1)];   // past the end: the last again
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, v[u]);
+  }
+  __shared__ float red[kFinThreads / 64];
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     float r = red[0];
 #pragma unroll
-    for (int k = 1; k < kThreads / 64; ++k) r = fmaxf(r, red[k]);
+    for (int k = 1; k < kFinThreads / 64; ++k) r = fmaxf(r, red[k]);
     const float sc = fp8_scale_from_amax(r);
     *amax = r;
     *scale = sc;
@@ -773,7 +782,7 @@ hipError_t launch_dact_dbias_quantize(const void* grad, const void* x, int64_t r
   }
   {
     LaunchScope scope("amax_finalize", s);
-    amax_finalize_kernel<<<1, kThreads, 0, s>>>(amax_part, dact_blocks(rows, cols, gated), amax, scale, scale_inv);
+    amax_finalize_kernel<<<1, kFinThreads, 0, s>>>(amax_part, dact_blocks(rows, cols, gated), amax, scale, scale_inv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
