@@ -169,6 +169,24 @@ __device__ __forceinline__ void stage_copy_out(St st, int tid, int rows_valid, D
   }
 }
 
+// max |act(h)| over values whose range is [hmin, hmax]. Each supported
+// activation is increasing for h >= 0 and bounded in magnitude by a small
+// constant for h < 0 (GELU: 0.170 near h = -0.75, SiLU: 0.279 near h = -1.28,
+// ReLU: 0), so once |act(hmax)| reaches amax_exact_from() the negative side
+// cannot exceed it and the max is act(hmax). Linear: max(|hmax|, |hmin|).
+// No values (hmax < hmin): 0.
+template <int ACT>
+__device__ __forceinline__ float amax_from_range(float hmax, float hmin) {
+  if (!(hmax >= hmin)) return 0.0f;
+  if constexpr (ACT == kLinear) return fmaxf(fabsf(hmax), fabsf(hmin));
+  else if constexpr (ACT == kRelu) return fmaxf(hmax, 0.0f);
+  else return hmax > 0.0f ? fabsf(act_fwd<ACT>(hmax)) : 0.0f;
+}
+template <int ACT>
+constexpr float amax_exact_from() {
+  return ACT == kGelu || ACT == kGeluErf ? 0.2f : ACT == kSilu ? 0.3f : 0.0f;
+}
+
 // h = acc * scale + bias; then the stores / amax selected by the flags. Both
 // stores go through the LDS staging tile (the main loop's LDS is free here).
 // AMAX evaluates the activation from h rounded to bf16, exactly as a later
@@ -180,6 +198,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
   const int lm = lane & 31, lh = lane >> 5;
   const int rows_valid = min(ep.M - m0, kTileM);
   float lmax = 0.0f;
+  float hmax = -INFINITY, hmin = INFINITY;   // range of the lane's rounded h (plain amax)
   // every wave's LDS reads of the main loop are done before the staging writes
   __syncthreads();
 
@@ -207,7 +226,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
             if (in_range && m0 + r < ep.M) {
               round_bf16x4(h);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(h[q])));
+              for (int q = 0; q < 4; ++q) { hmax = fmaxf(hmax, h[q]); hmin = fminf(hmin, h[q]); }
             }
           }
         }
@@ -295,6 +314,37 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     });
   }
 
+  if constexpr (AMAX && !GATED) {
+    // max |act(h)| from the range of h: exact whenever it reaches the
+    // activation's threshold; otherwise (a lane whose values are all small)
+    // every value is evaluated.
+    lmax = amax_from_range<ACT>(hmax, hmin);
+    if (lmax < amax_exact_from<ACT>()) {
+      lmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + lm;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;
+            bool in_range;
+            tile_col<GATED>(ep, n0, tc, in_range);
+            if (in_range && m0 + r < ep.M) {
+              float h[4], b[4];
+              unpack_bias4(bv[j][g], b);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale + b[q];
+              round_bf16x4(h);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(h[q])));
+            }
+          }
+        }
+      }
+    }
+  }
   if constexpr (AMAX) {
     __shared__ float red[NT / 64];
     block_max_atomic(lmax, ep.amax, red);

@@ -162,6 +162,34 @@ def test_mlp_fp8(name, rows, hidden, ffn, gated):
     assert_rel(f64(y), o["y"], TOL["fp8"], "y")
 
 
+@pytest.mark.parametrize("act", ["gelu", "gelu_erf", "silu", "relu", "linear"])
+@pytest.mark.parametrize("regime", ["small", "negative"])
+def test_mlp_fp8_activation_amax_regimes(act, regime):
+    """The amax of act(h) that GEMM1's epilogue reduces, where every value is
+    small (kernel1 scaled by 0.05: |act(h)| < 0.1) or h is mostly negative
+    (bias1 = -2: GELU and SiLU take their negative-side values): the epilogue
+    then evaluates the activation of every element instead of taking it from
+    the largest h, and must still match the oracle."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["ln_mlp_gelu_fp8"].scaled(300, 272, 400), activation_type=(act,),
+                            name=f"fp8-{act}-{regime}")
+    print(f"layernorm_mlp fp8 amax {act} {regime}", flush=True)
+    t = W.make_inputs(w, seed=3)
+    if regime == "small":
+        t["kernel1"] = (t["kernel1"].float() * 0.05).to(t["kernel1"].dtype)
+    else:
+        t["bias1"] = torch.full_like(t["bias1"], -2.0)
+    g = to_dev(t)
+    q = te.QuantizerSet()
+    y, saved = _mlp_gpu(w, g, quantizer_set=q, return_saved=True, save_codes=True)
+    torch.cuda.synchronize()
+    o = _mlp_oracle(w, t, quant="fp8_e4m3_current")
+    got, ref = q.act.values()["amax"], o["act_meta"]["amax"]
+    assert abs(got - ref) <= 1e-5 * ref, (got, ref)
+    if ref > 0:
+        assert_rel(f64(y), o["y"], TOL["fp8"], "y")
+
+
 def test_mlp_zero_rows():
     w = W.WORKLOADS["ln_mlp_gelu_bf16"].scaled(1, 64, 128)
     t = to_dev(W.make_inputs(w))
