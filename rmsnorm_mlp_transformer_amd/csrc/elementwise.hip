@@ -51,13 +51,8 @@ __device__ __forceinline__ void store8(void* base, int64_t e, const float* f) {
   }
 }
 __device__ __forceinline__ uint2 encode8(const float* f, float scale) {
-  uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    w0 |= e4m3_encode(f[i] * scale) << (8 * i);
-    w1 |= e4m3_encode(f[i + 4] * scale) << (8 * i);
-  }
-  return make_uint2(w0, w1);
+  return make_uint2(e4m3_pack4(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale),
+                    e4m3_pack4(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale));
 }
 
 // Products and sums that must round the same way in every kernel that forms
@@ -264,7 +259,11 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
     float f[8];
     unpack8_raw<BF16>(w[p], f);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tile[cc + i][r] = (uint8_t)e4m3_encode(f[i] * scale);
+    for (int i = 0; i < 8; i += 2) {
+      const uint32_t c = e4m3_pack2(f[i] * scale, f[i + 1] * scale);
+      tile[cc + i][r] = (uint8_t)c;
+      tile[cc + i + 1][r] = (uint8_t)(c >> 8);
+    }
   }
   __syncthreads();
   // write: 64 output rows (= input columns) x 4 chunks of 16 codes
@@ -300,58 +299,6 @@ __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* cod
 // ------------------------------------------------------------------ act_lu
 // Thread (x) = 8 output columns; blocks in y walk the rows with a stride.
 // MODE 0: store; 1: amax only; 2: E4M3 codes.
-template <bool BF16, int ACT, bool GATED, int MODE, int OUT>
-__global__ void __launch_bounds__(kThreads) act_kernel(const void* x, int64_t rows, int64_t cols,
-                                                       void* y, float* amax, float* scale_out,
-                                                       float* scale_inv_out) {
-  const int64_t in_cols = GATED ? 2 * cols : cols;
-  const int64_t cc = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
-  float scale = 1.0f;
-  if constexpr (MODE == 2) {
-    scale = fp8_scale_from_amax(*amax);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-      *scale_out = scale;
-      *scale_inv_out = 1.0f / scale;
-    }
-  }
-  float m = 0.0f;
-  if (cc < cols) {
-    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-      float a[8], o[8];
-      load8<BF16>(x, r * in_cols + cc, a);
-      if constexpr (GATED) {
-        float b[8];
-        load8<BF16>(x, r * in_cols + cols + cc, b);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]) * b[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]);
-      }
-      if constexpr (MODE == 0) {
-        store8<OUT == kBF16>(y, r * cols + cc, o);
-      } else if constexpr (MODE == 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(o[i]));
-      } else {
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(y) + r * cols + cc) = encode8(o, scale);
-      }
-    }
-  }
-  if constexpr (MODE == 1) {
-    __shared__ float red[kThreads / 64];
-    block_max_atomic(m, amax, red);
-  }
-}
-
-dim3 act_grid(int64_t rows, int64_t cols) {
-  const int64_t gx = (cols / 8 + kThreads - 1) / kThreads;
-  int64_t gy = (8192 + gx - 1) / gx;          // ~8192 blocks, each row handled by one block
-  if (gy > rows) gy = rows;
-  if (gy < 1) gy = 1;
-  if (gy > 65535) gy = 65535;
-  return dim3((unsigned)gx, (unsigned)gy);
-}
 
 // ------------------------------------------------------------------ dact + dbias
 // Block = W waves over one strip of 512 output columns (8 per lane) and one
@@ -575,17 +522,117 @@ __global__ void __launch_bounds__(64 * kFinWaves) dbias_finalize_kernel(const fl
   }
 }
 
+// Rows per work chunk of the strip kernels (dact, act): about TE_DACT_TARGET_BLOCKS chunks in all, at
+// least 16 rows each, and a chunk's rows of x (fp32, gated: 2 cols) below
+// 2 GiB so that one buffer descriptor with 32-bit offsets covers them.
+int64_t dact_rows_per_chunk(int64_t rows, int64_t cols, bool gated) {
+  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
+  int64_t chunks = (TE_DACT_TARGET_BLOCKS + strips - 1) / strips;
+  const int64_t max_chunks = (rows + 15) / 16;
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  int64_t rpc = (rows + chunks - 1) / chunks;
+  const int64_t row_bytes = (gated ? 2 : 1) * cols * 4;
+  const int64_t max_rpc = (((int64_t)1 << 31) - 1) / row_bytes;
+  if (rpc > max_rpc) rpc = max_rpc;
+  return rpc < 1 ? 1 : rpc;
+}
+
+// Activation forward (act_lu): y = act(x), gated y = act(a) * b for x = [a | b].
+// The same layout as dact: 512-column strips, W waves over short row chunks
+// read through per-chunk buffer descriptors, U rows per step with all loads
+// in flight before the first use. MODE 0 stores y (OUT bf16 / fp32), 1 the
+// amax of y only (workgroup max + one atomic; the grid is capped and a
+// workgroup loops over chunks), 2 the E4M3 codes of y * scale with the scale
+// from the finished amax.
+template <bool BF16, int ACT, bool GATED, int MODE, int OUT>
+__global__ void __launch_bounds__(64 * kDactWaves) act_kernel(const void* x, int64_t rows, int64_t cols,
+                                                              int64_t rows_per_chunk, void* y, float* amax,
+                                                              float* scale_out, float* scale_inv_out) {
+  constexpr int G = GATED ? 2 : 1;
+  constexpr int W = kDactWaves, U = kDactUnroll;
+  constexpr int64_t ES = BF16 ? 2 : 4;
+  constexpr int64_t OS = MODE == 2 ? 1 : (OUT == kBF16 ? 2 : 4);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int64_t col = (int64_t)blockIdx.x * kDactStrip + lane * 8;
+  const int64_t xcols = G * cols;
+  const int64_t nchunks = (rows + rows_per_chunk - 1) / rows_per_chunk;
+  float qscale = 1.0f;
+  if constexpr (MODE == 2) {
+    qscale = fp8_scale_from_amax(*amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      *scale_out = qscale;
+      *scale_inv_out = 1.0f / qscale;
+    }
+  }
+  const uint32_t vx = (uint32_t)((w * xcols + col) * ES);
+  const uint32_t vy = (uint32_t)((w * cols + col) * OS);
+  float m = 0.0f;
+  if (col < cols) {
+    for (int64_t ch = blockIdx.y; ch < nchunks; ch += gridDim.y) {
+      const int64_t r_begin = ch * rows_per_chunk;
+      const int64_t nr = min(rows_per_chunk, rows - r_begin);
+      const Rsrc rx = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + r_begin * xcols * ES, nr * xcols * ES);
+      const Rsrc ry = buf_rsrc(MODE != 1 ? reinterpret_cast<const uint8_t*>(y) + r_begin * cols * OS : nullptr,
+                               MODE != 1 ? nr * cols * OS : 0);
+      for (int64_t r0 = 0; r0 < nr; r0 += W * U) {
+        Raw8<BF16> aw[U], bw[GATED ? U : 1];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t so = (uint32_t)((r0 + (int64_t)u * W) * xcols * ES);
+          load8_raw<BF16>(rx, vx, so, aw[u]);
+          if constexpr (GATED) load8_raw<BF16>(rx, vx + (uint32_t)(cols * ES), so, bw[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float a[8], o[8];
+          unpack8_raw<BF16>(aw[u], a);
+          if constexpr (GATED) {
+            float b[8];
+            unpack8_raw<BF16>(bw[u], b);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]) * b[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = act_fwd<ACT>(a[i]);
+          }
+          const uint32_t so = (uint32_t)((r0 + (int64_t)u * W) * cols * OS);
+          if constexpr (MODE == 0) {
+            store8_buf<OUT == kBF16>(ry, vy, so, o);
+          } else if constexpr (MODE == 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(o[i]));
+          } else {
+            store8_codes_buf(ry, vy, so, encode8(o, qscale));
+          }
+        }
+      }
+    }
+  }
+  if constexpr (MODE == 1) {
+    __shared__ float red[W];
+    block_max_atomic(m, amax, red);
+  }
+}
+
 template <bool BF16>
 hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool gated, int mode,
                         void* y, int y_dtype, float* amax, float* so, float* sio, hipStream_t s) {
-  const dim3 grid = act_grid(rows, cols);
-  dim3 grid_amax = grid;                         // amax pass: at most ~1024 workgroups
-  if (grid_amax.x * grid_amax.y > 1024) grid_amax.y = max(1u, 1024u / grid_amax.x);
-#define TE_ACT_CASE(A, G)                                                                         \
-  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid_amax, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
-  else if (mode == 2) act_kernel<BF16, A, G, 2, kE4M3><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
-  else if (y_dtype == kBF16) act_kernel<BF16, A, G, 0, kBF16><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio); \
-  else act_kernel<BF16, A, G, 0, kF32><<<grid, kThreads, 0, s>>>(x, rows, cols, y, amax, so, sio);
+  if (rows <= 0) return hipSuccess;
+  const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
+  const int64_t chunks = (rows + rpc - 1) / rpc;
+  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
+  const dim3 grid((unsigned)strips, (unsigned)chunks);
+  // amax pass: at most ~1024 workgroups (one atomic each on a single address)
+  const dim3 grid_amax((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, 1024 / strips)));
+  constexpr int T = 64 * kDactWaves;
+#define TE_ACT_CASE(A, G)                                                                                      \
+  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid_amax, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio);   \
+  else if (mode == 2) act_kernel<BF16, A, G, 2, kE4M3><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio); \
+  else if (y_dtype == kBF16) act_kernel<BF16, A, G, 0, kBF16><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio); \
+  else act_kernel<BF16, A, G, 0, kF32><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio);
 #define TE_ACT_G(A) if (gated) { TE_ACT_CASE(A, true) } else { TE_ACT_CASE(A, false) }
   switch (act) {
     case kRelu: TE_ACT_G(kRelu) break;
@@ -671,23 +718,6 @@ hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, in
   return act_dispatch<false>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
 }
 
-namespace {
-// Rows per dact work chunk: about TE_DACT_TARGET_BLOCKS chunks in all, at
-// least 16 rows each, and a chunk's rows of x (fp32, gated: 2 cols) below
-// 2 GiB so that one buffer descriptor with 32-bit offsets covers them.
-int64_t dact_rows_per_chunk(int64_t rows, int64_t cols, bool gated) {
-  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
-  int64_t chunks = (TE_DACT_TARGET_BLOCKS + strips - 1) / strips;
-  const int64_t max_chunks = (rows + 15) / 16;
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  int64_t rpc = (rows + chunks - 1) / chunks;
-  const int64_t row_bytes = (gated ? 2 : 1) * cols * 4;
-  const int64_t max_rpc = (((int64_t)1 << 31) - 1) / row_bytes;
-  if (rpc > max_rpc) rpc = max_rpc;
-  return rpc < 1 ? 1 : rpc;
-}
-}  // namespace
 
 // Workgroups along the row axis (= rows of partial column sums): one per
 // work chunk, at most about TE_DACT_RESIDENT_BLOCKS workgroups in all; a

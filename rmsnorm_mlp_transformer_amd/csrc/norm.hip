@@ -64,7 +64,8 @@ __device__ __forceinline__ void store_chunk(void* y, int64_t row, int64_t hidden
     uint8_t* p = reinterpret_cast<uint8_t*>(y) + e;
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) w[i / 4] |= e4m3_encode(v[i] * qscale) << (8 * (i % 4));
+    for (int i = 0; i < VEC; i += 4)
+      w[i / 4] = e4m3_pack4(v[i] * qscale, v[i + 1] * qscale, v[i + 2] * qscale, v[i + 3] * qscale);
     if constexpr (VEC == 8) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
     else *reinterpret_cast<uint32_t*>(p) = w[0];
   }
