@@ -7,9 +7,15 @@ GEMM) divided by the step's wall time, in TFLOP/s. The other workloads
 (LayerNorm+Dense, RMSNorm-SwiGLU, the fp8 forward and the activation
 backward) are measured the same way and reported under "parts".
 
-Per-kernel durations come from HIP events the library records around each
-of its launches on the launch stream (te_timing_enable) during the timed
-region; the dominant kernel's figure is the "roofline" entry. The
+Each measurement has two timed regions of K steps, back to back on the
+same inputs. The first has no instrumentation: its wall time gives
+"ms_per_step" and "value". In the second the library's per-kernel timing is
+on (te_timing_enable): each launch carries two HIP events on its stream that
+the runtime stamps with the kernel's own start and end (the durations sum to
+the uninstrumented step time), but the event-carrying dispatches lengthen the
+step by several microseconds per launch, which is why the step time comes
+from the first region. The dominant kernel's average duration from the
+second region is the "roofline" entry. The
 "cpu_baseline" entry times the fp64 oracle on a bounded row sample.
 
 The "traffic" entry is the HBM traffic per launch of the dominant kernel
@@ -231,12 +237,10 @@ class MlpBwdCase:
 
 
 def time_steps(fn, steps, warmup, te=None):
+    """(ms per step over `steps` uninstrumented steps, per-kernel timing of
+    `steps` more steps with the library's launch events on)."""
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
-    if te is not None:
-        te.te_timing_reset()
-        te.te_timing_enable(True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -247,6 +251,11 @@ def time_steps(fn, steps, warmup, te=None):
     ms = start.elapsed_time(stop) / steps
     kernels = {}
     if te is not None:
+        te.te_timing_reset()
+        te.te_timing_enable(True)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
         kernels = te.te_timing_collect()
         te.te_timing_enable(False)
     return ms, kernels

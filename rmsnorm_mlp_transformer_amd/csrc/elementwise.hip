@@ -629,10 +629,10 @@ hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool
   const dim3 grid_amax((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, 1024 / strips)));
   constexpr int T = 64 * kDactWaves;
 #define TE_ACT_CASE(A, G)                                                                                      \
-  if (mode == 1) act_kernel<BF16, A, G, 1, kF32><<<grid_amax, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio);   \
-  else if (mode == 2) act_kernel<BF16, A, G, 2, kE4M3><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio); \
-  else if (y_dtype == kBF16) act_kernel<BF16, A, G, 0, kBF16><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio); \
-  else act_kernel<BF16, A, G, 0, kF32><<<grid, T, 0, s>>>(x, rows, cols, rpc, y, amax, so, sio);
+  if (mode == 1) launch_kernel(act_kernel<BF16, A, G, 1, kF32>, grid_amax, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);   \
+  else if (mode == 2) launch_kernel(act_kernel<BF16, A, G, 2, kE4M3>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio); \
+  else if (y_dtype == kBF16) launch_kernel(act_kernel<BF16, A, G, 0, kBF16>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio); \
+  else launch_kernel(act_kernel<BF16, A, G, 0, kF32>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);
 #define TE_ACT_G(A) if (gated) { TE_ACT_CASE(A, true) } else { TE_ACT_CASE(A, false) }
   switch (act) {
     case kRelu: TE_ACT_G(kRelu) break;
@@ -650,20 +650,20 @@ hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool
 
 hipError_t launch_fill_zero(float* p, int n, hipStream_t s) {
   LaunchScope scope("fill_zero", s);
-  fill_zero_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n);
+  launch_kernel(fill_zero_kernel, (n + 255) / 256, 256, 0, s, p, n);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero_bytes(void* p, int64_t nbytes, hipStream_t s) {
   LaunchScope scope("fill_zero", s);
   const int64_t words = nbytes / 4;
-  fill_zero_words_kernel<<<(unsigned)((words + 255) / 256), 256, 0, s>>>(reinterpret_cast<uint32_t*>(p), words);
+  launch_kernel(fill_zero_words_kernel, (unsigned)((words + 255) / 256), 256, 0, s, reinterpret_cast<uint32_t*>(p), words);
   return hipGetLastError();
 }
 
 hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStream_t s) {
   LaunchScope scope("empty_meta", s);
-  empty_meta_kernel<<<1, 64, 0, s>>>(amax, scale, scale_inv);
+  launch_kernel(empty_meta_kernel, 1, 64, 0, s, amax, scale, scale_inv);
   return hipGetLastError();
 }
 
@@ -671,8 +671,8 @@ hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipSt
   LaunchScope scope("amax", s);
   // one atomic per workgroup on a single address: few workgroups, each looping
   const unsigned grid = min(grid_for(n / 8, kUnroll), 1024u);
-  if (x_dtype == kBF16) amax_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
-  else amax_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, amax);
+  if (x_dtype == kBF16) launch_kernel(amax_kernel<true>, grid, kThreads, 0, s, x, n / 8, amax);
+  else launch_kernel(amax_kernel<false>, grid, kThreads, 0, s, x, n / 8, amax);
   return hipGetLastError();
 }
 
@@ -681,9 +681,9 @@ hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes
   LaunchScope scope("quantize", s);
   const unsigned grid = grid_for(n / 8, 4);
   if (x_dtype == kBF16)
-    quantize_kernel<true><<<grid, kThreads, 0, s>>>(x, n / 8, codes, amax, scale_out, scale_inv_out);
+    launch_kernel(quantize_kernel<true>, grid, kThreads, 0, s, x, n / 8, codes, amax, scale_out, scale_inv_out);
   else
-    quantize_kernel<false><<<grid, kThreads, 0, s>>>(x, n / 8, codes, amax, scale_out, scale_inv_out);
+    launch_kernel(quantize_kernel<false>, grid, kThreads, 0, s, x, n / 8, codes, amax, scale_out, scale_inv_out);
   return hipGetLastError();
 }
 
@@ -693,9 +693,9 @@ hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, 
   LaunchScope scope("quantize_transpose", s);
   const unsigned grid = (unsigned)(((cols + 63) / 64) * ((rows + 63) / 64));   // < 2^18 for weights < 2 GiB
   if (x_dtype == kBF16)
-    quantize_transpose_kernel<true><<<grid, kThreads, 0, s>>>(x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
+    launch_kernel(quantize_transpose_kernel<true>, grid, kThreads, 0, s, x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
   else
-    quantize_transpose_kernel<false><<<grid, kThreads, 0, s>>>(x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
+    launch_kernel(quantize_transpose_kernel<false>, grid, kThreads, 0, s, x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
   return hipGetLastError();
 }
 
@@ -703,8 +703,8 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale
                              int y_dtype, hipStream_t s) {
   LaunchScope scope("dequantize", s);
   const unsigned grid = grid_for(n / 8, 4);
-  if (y_dtype == kBF16) dequantize_kernel<true><<<grid, kThreads, 0, s>>>(codes, n / 8, scale_inv, y);
-  else dequantize_kernel<false><<<grid, kThreads, 0, s>>>(codes, n / 8, scale_inv, y);
+  if (y_dtype == kBF16) launch_kernel(dequantize_kernel<true>, grid, kThreads, 0, s, codes, n / 8, scale_inv, y);
+  else launch_kernel(dequantize_kernel<false>, grid, kThreads, 0, s, codes, n / 8, scale_inv, y);
   return hipGetLastError();
 }
 
@@ -742,7 +742,7 @@ hipError_t dact_dispatch(const void* grad, const void* x, int64_t rows, int64_t 
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
   const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
   const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
-#define TE_DACT(B, A, G) dact_kernel<B, A, G, MODE><<<grid, 64 * kDactWaves, 0, s>>>(grad, x, rows, cols, rpc, dx, partials, amax_part, amax)
+#define TE_DACT(B, A, G) launch_kernel(dact_kernel<B, A, G, MODE>, grid, 64 * kDactWaves, 0, s, grad, x, rows, cols, rpc, dx, partials, amax_part, amax)
 #define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);
 #define TE_DACT_A(B)                                   \
   switch (act) {                                       \
@@ -765,8 +765,8 @@ hipError_t dbias_finalize(const float* partials, int64_t rows, int64_t cols, boo
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
   const int64_t n = (gated ? 2 : 1) * cols;
   const unsigned g2 = (unsigned)((n + 63) / 64);
-  if (dbias_dtype == kBF16) dbias_finalize_kernel<kBF16><<<g2, 64 * kFinWaves, 0, s>>>(partials, chunks, n, dbias);
-  else dbias_finalize_kernel<kF32><<<g2, 64 * kFinWaves, 0, s>>>(partials, chunks, n, dbias);
+  if (dbias_dtype == kBF16) launch_kernel(dbias_finalize_kernel<kBF16>, g2, 64 * kFinWaves, 0, s, partials, chunks, n, dbias);
+  else launch_kernel(dbias_finalize_kernel<kF32>, g2, 64 * kFinWaves, 0, s, partials, chunks, n, dbias);
   return hipGetLastError();
 }
 }  // namespace
@@ -812,7 +812,7 @@ hipError_t launch_dact_dbias_quantize(const void* grad, const void* x, int64_t r
   }
   {
     LaunchScope scope("amax_finalize", s);
-    amax_finalize_kernel<<<1, kFinThreads, 0, s>>>(amax_part, dact_blocks(rows, cols, gated), amax, scale, scale_inv);
+    launch_kernel(amax_finalize_kernel, 1, kFinThreads, 0, s, amax_part, dact_blocks(rows, cols, gated), amax, scale, scale_inv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

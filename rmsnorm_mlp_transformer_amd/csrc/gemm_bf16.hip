@@ -313,13 +313,13 @@ hipError_t launch_flags(const GemmArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
+    if (h) launch_kernel(gemm_bf16_kernel<ACT, GATED, false, true, true, kWaves, kBK, kStages, kPingPong, false>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bf16_kernel<ACT, GATED, false, false, true, kWaves, kBK, kStages, kPingPong, false>, grid, T, 0, s, a);
   } else if (h) {
-    if (out) gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
-    else gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
+    if (out) launch_kernel(gemm_bf16_kernel<ACT, GATED, true, true, false, kWaves, kBK, kStages, kPingPong, false>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bf16_kernel<ACT, GATED, false, true, false, kWaves, kBK, kStages, kPingPong, false>, grid, T, 0, s, a);
   } else {
-    gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages, kPingPong, false><<<grid, T, 0, s>>>(a);
+    launch_kernel(gemm_bf16_kernel<ACT, GATED, true, false, false, kWaves, kBK, kStages, kPingPong, false>, grid, T, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -342,8 +342,7 @@ hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t
   a.ep.n_b = (int)n_b;
   a.ep.F = (int)n_b;
   const unsigned grid = (unsigned)(((M + kTileM - 1) / kTileM) * ((n_b + kTileN - 1) / kTileN));
-  gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, true>
-      <<<grid, 64 * kWaves, 0, s>>>(a);
+  launch_kernel(gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, true>, grid, 64 * kWaves, 0, s, a);
   return hipGetLastError();
 }
 

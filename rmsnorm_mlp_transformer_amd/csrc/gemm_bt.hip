@@ -258,13 +258,13 @@ hipError_t launch_flags(const FpArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) gemm_bt_kernel<FP8, ACT, GATED, false, true, true><<<grid, T, 0, s>>>(a);
-    else gemm_bt_kernel<FP8, ACT, GATED, false, false, true><<<grid, T, 0, s>>>(a);
+    if (h) launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, true, true>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, false, true>, grid, T, 0, s, a);
   } else if (h) {
-    if (out) gemm_bt_kernel<FP8, ACT, GATED, true, true, false><<<grid, T, 0, s>>>(a);
-    else gemm_bt_kernel<FP8, ACT, GATED, false, true, false><<<grid, T, 0, s>>>(a);
+    if (out) launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, true, true, false>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, true, false>, grid, T, 0, s, a);
   } else {
-    gemm_bt_kernel<FP8, ACT, GATED, true, false, false><<<grid, T, 0, s>>>(a);
+    launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, true, false, false>, grid, T, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -105,10 +105,10 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(F32Args a) {
 template <int ACT, bool GATED>
 hipError_t launch_flags(const F32Args& a, dim3 grid, hipStream_t s) {
   if (a.h_out != nullptr) {
-    if (a.out != nullptr) gemm_f32_kernel<ACT, GATED, true, true><<<grid, 256, 0, s>>>(a);
-    else gemm_f32_kernel<ACT, GATED, false, true><<<grid, 256, 0, s>>>(a);
+    if (a.out != nullptr) launch_kernel(gemm_f32_kernel<ACT, GATED, true, true>, grid, 256, 0, s, a);
+    else launch_kernel(gemm_f32_kernel<ACT, GATED, false, true>, grid, 256, 0, s, a);
   } else {
-    gemm_f32_kernel<ACT, GATED, true, false><<<grid, 256, 0, s>>>(a);
+    launch_kernel(gemm_f32_kernel<ACT, GATED, true, false>, grid, 256, 0, s, a);
   }
   return hipGetLastError();
 }

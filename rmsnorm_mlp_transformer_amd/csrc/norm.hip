@@ -227,13 +227,13 @@ hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s
   const int64_t blocks = (a.rows + 3) / 4;
   const dim3 grid((unsigned)(mode == kNormAmax && blocks > 1024 ? 1024 : blocks)), block(256);
   if (mode == kNormAmax) {
-    norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32><<<grid, block, 0, s>>>(a);
+    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32>, grid, block, 0, s, a);
   } else if (mode == kNormQuant) {
-    norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3><<<grid, block, 0, s>>>(a);
+    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3>, grid, block, 0, s, a);
   } else if (y_dtype == kF32) {
-    norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kF32><<<grid, block, 0, s>>>(a);
+    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kF32>, grid, block, 0, s, a);
   } else {
-    norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kBF16><<<grid, block, 0, s>>>(a);
+    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kBF16>, grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -257,11 +257,11 @@ hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const
     BwdArgs a{dy, x, mu, rsigma, gamma, rows, hidden, zcg ? 1 : 0, tw, (rows + blocks - 1) / blocks, dx,
               params ? part_g : nullptr, params ? part_b : nullptr};
     if (dtype == kBF16) {
-      if (rms) norm_bwd_kernel<true, true><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
-      else norm_bwd_kernel<true, false><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+      if (rms) launch_kernel(norm_bwd_kernel<true, true>, (unsigned)blocks, kBwdThreads, 0, s, a);
+      else launch_kernel(norm_bwd_kernel<true, false>, (unsigned)blocks, kBwdThreads, 0, s, a);
     } else {
-      if (rms) norm_bwd_kernel<false, true><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
-      else norm_bwd_kernel<false, false><<<(unsigned)blocks, kBwdThreads, 0, s>>>(a);
+      if (rms) launch_kernel(norm_bwd_kernel<false, true>, (unsigned)blocks, kBwdThreads, 0, s, a);
+      else launch_kernel(norm_bwd_kernel<false, false>, (unsigned)blocks, kBwdThreads, 0, s, a);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -273,8 +273,8 @@ hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const
     void* out = p == 0 ? dgamma : dbeta;
     const float* part = p == 0 ? part_g : part_b;
     if (out == nullptr || (p == 1 && rms)) continue;
-    if (dparam_dtype == kBF16) param_finalize_kernel<kBF16><<<g, 256, 0, s>>>(part, blocks, hidden, out);
-    else param_finalize_kernel<kF32><<<g, 256, 0, s>>>(part, blocks, hidden, out);
+    if (dparam_dtype == kBF16) launch_kernel(param_finalize_kernel<kBF16>, g, 256, 0, s, part, blocks, hidden, out);
+    else launch_kernel(param_finalize_kernel<kF32>, g, 256, 0, s, part, blocks, hidden, out);
   }
   return hipGetLastError();
 }

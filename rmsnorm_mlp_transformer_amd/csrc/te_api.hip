@@ -105,6 +105,7 @@ Meta pick_meta(const te_fp8_meta* user, float* ws3) {
 struct TimingRec {
   const char* name;
   hipEvent_t start, stop;
+  bool started;   // a launch has taken the start event
 };
 struct TimingTotal {
   std::string name;
@@ -113,6 +114,7 @@ struct TimingTotal {
 };
 bool g_timing = false;
 std::vector<TimingRec> g_pending;
+int g_active = -1;   // g_pending index of the innermost open scope
 std::vector<hipEvent_t> g_event_pool;
 std::vector<TimingTotal> g_totals;
 
@@ -196,16 +198,31 @@ te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t
 }  // namespace
 
 namespace te {
-LaunchScope::LaunchScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : slot(-1), prev(g_active), stream(s) {
   if (!g_timing) return;
   hipEvent_t a = pooled_event(), b = pooled_event();
   if (a == nullptr || b == nullptr) return;
-  if (hipEventRecord(a, s) != hipSuccess) return;
-  g_pending.push_back({name, a, b});
+  g_pending.push_back({name, a, b, false});
   slot = (int)g_pending.size() - 1;
+  g_active = slot;
 }
 LaunchScope::~LaunchScope() {
-  if (slot >= 0) (void)hipEventRecord(g_pending[slot].stop, stream);
+  if (slot < 0) return;
+  TimingRec& r = g_pending[slot];
+  if (!r.started) {   // nothing was launched: an empty interval
+    (void)hipEventRecord(r.start, stream);
+    (void)hipEventRecord(r.stop, stream);
+  }
+  g_active = prev;
+}
+void scope_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_active < 0) return;
+  TimingRec& r = g_pending[g_active];
+  if (!r.started) {
+    *start = r.start;
+    r.started = true;
+  }
+  *stop = r.stop;
 }
 }  // namespace te
 

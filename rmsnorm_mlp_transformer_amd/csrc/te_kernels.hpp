@@ -3,6 +3,7 @@
 // returns the HIP error of its launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -14,13 +15,33 @@ enum { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
 // Activation kinds (kernel template parameters).
 enum ActKind { kRelu = 0, kGelu = 1, kGeluErf = 2, kSilu = 3, kLinear = 4 };
 
-// Brackets one kernel launch with HIP events when per-kernel timing is on.
+// Per-kernel timing: while timing is on, the launches made inside a scope
+// carry its two HIP events (launch_kernel below), which the runtime stamps
+// with the first kernel's start and the last kernel's end, with no separate
+// event packets around the dispatches. A scope without a launch records both
+// events back to back.
 struct LaunchScope {
   LaunchScope(const char* name, hipStream_t s);
   ~LaunchScope();
   int slot;
+  int prev;
   hipStream_t stream;
 };
+// Events for a kernel launched in the innermost timing scope (both null
+// unless timing is on): the scope's start event on its first launch, its stop
+// event on every launch.
+void scope_launch_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through this: the arguments are
+// converted to the kernel's parameter types, and the active scope's events
+// ride on the dispatch.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                          Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  scope_launch_events(&e0, &e1);
+  hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<KArgs>(args)...);
+}
 
 // ---------------------------------------------------------------- norm
 enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
