@@ -625,8 +625,8 @@ hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool
   const int64_t chunks = (rows + rpc - 1) / rpc;
   const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
   const dim3 grid((unsigned)strips, (unsigned)chunks);
-  // amax pass: at most ~1024 workgroups (one atomic each on a single address)
-  const dim3 grid_amax((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, 1024 / strips)));
+  // amax pass: at most kAmaxBlocks workgroups (one atomic each on a single address)
+  const dim3 grid_amax((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, (int64_t)kAmaxBlocks / strips)));
   constexpr int T = 64 * kDactWaves;
 #define TE_ACT_CASE(A, G)                                                                                      \
   if (mode == 1) launch_kernel(act_kernel<BF16, A, G, 1, kF32>, grid_amax, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);   \
@@ -670,7 +670,7 @@ hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStr
 hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s) {
   LaunchScope scope("amax", s);
   // one atomic per workgroup on a single address: few workgroups, each looping
-  const unsigned grid = min(grid_for(n / 8, kUnroll), 1024u);
+  const unsigned grid = min(grid_for(n / 8, kUnroll), kAmaxBlocks / 2);
   if (x_dtype == kBF16) launch_kernel(amax_kernel<true>, grid, kThreads, 0, s, x, n / 8, amax);
   else launch_kernel(amax_kernel<false>, grid, kThreads, 0, s, x, n / 8, amax);
   return hipGetLastError();

@@ -225,7 +225,7 @@ hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s
   // one row per wave; the amax pass caps the grid (one atomic per workgroup on
   // a single address serialises in the L2) and its waves loop over rows
   const int64_t blocks = (a.rows + 3) / 4;
-  const dim3 grid((unsigned)(mode == kNormAmax && blocks > 1024 ? 1024 : blocks)), block(256);
+  const dim3 grid((unsigned)(mode == kNormAmax && blocks > kAmaxBlocks ? kAmaxBlocks : blocks)), block(256);
   if (mode == kNormAmax) {
     launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32>, grid, block, 0, s, a);
   } else if (mode == kNormQuant) {

@@ -184,6 +184,15 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
 // thousands of waves hitting one address serialise in the L2, so each
 // workgroup contributes one atomic. Must be reached by every thread of the
 // workgroup (it synchronises); red must hold one float per wave.
+// Most workgroups an amax pass launches: each adds one atomic on the same
+// address at its end, and those serialise in the L2 at the kernel's tail. A
+// sweep (256-2048) at the bench shapes put the norm amax pass best at 512
+// and the plain amax (8 loads in flight per lane) at 256.
+#ifndef TE_AMAX_BLOCKS
+#define TE_AMAX_BLOCKS 512
+#endif
+constexpr unsigned kAmaxBlocks = TE_AMAX_BLOCKS;
+
 __device__ __forceinline__ void block_max_atomic(float v, float* amax, float* red) {
   v = wave_max(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
