@@ -28,18 +28,6 @@ __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
-// Load 8 consecutive elements (bf16: one 16-byte load; fp32: two), streaming.
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t e, float* f) {
-  if constexpr (BF16) {
-    unpack8_bf16(load_stream16(reinterpret_cast<const uint16_t*>(base) + e), f);
-  } else {
-    const uint4 a = load_stream16(reinterpret_cast<const float*>(base) + e);
-    const uint4 b = load_stream16(reinterpret_cast<const float*>(base) + e + 4);
-    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
-    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
-  }
-}
 template <bool BF16>
 __device__ __forceinline__ void store8(void* base, int64_t e, const float* f) {
   if constexpr (BF16) {
@@ -104,17 +92,6 @@ __device__ __forceinline__ void load8_raw_ptr(const void* base, int64_t e, Raw8<
   if constexpr (!BF16) {
     const uint4 b = load_stream16(p + 16);
     d.w[1] = i32x4_t{(int)b.x, (int)b.y, (int)b.z, (int)b.w};
-  }
-}
-template <bool BF16>
-__device__ __forceinline__ void load8_buf(Rsrc r, uint32_t voff, uint32_t soff, float* f) {
-  const i32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kBufAuxStream);
-  if constexpr (BF16) {
-    unpack8_bf16(make_uint4((uint32_t)a[0], (uint32_t)a[1], (uint32_t)a[2], (uint32_t)a[3]), f);
-  } else {
-    const i32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kBufAuxStream);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { f[i] = __int_as_float(a[i]); f[4 + i] = __int_as_float(b[i]); }
   }
 }
 // Stores fold the row offset into the lane offset and pass a zero soffset:
