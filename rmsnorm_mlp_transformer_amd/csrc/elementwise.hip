@@ -202,57 +202,67 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64
   }
 }
 
-// Quantise x [rows, cols] into codes_t [cols, rows]. A 64 x 64 tile goes
-// through LDS: each lane reads 8 consecutive columns of one row (16 bytes for
-// bf16) and writes 16 consecutive rows of one column as 16 code bytes.
+// Quantise x [rows, cols] into codes_t [cols, rows]. A workgroup takes a
+// 128-row x 64-column tile: each thread loads 4 consecutive rows x 8 columns
+// (four 16-byte bf16 loads, all in flight before the first use), encodes
+// them, transposes the 4 x 4 code blocks in registers (v_perm_b32) and
+// writes one 4-byte word per column into an LDS tile [64 columns][128 rows];
+// the tile then leaves as 64 output rows of 128 codes (full 128-byte lines),
+// two 16-byte stores per thread.
+constexpr int kQtRows = 128, kQtCols = 64;
+constexpr int kQtPitch = kQtRows + 4;   // bytes per LDS row: 33 words, odd, spreads the word writes over the banks
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
     const void* x, int64_t rows, int64_t cols, uint8_t* codes_t, const float* amax,
     float* scale_out, float* scale_inv_out) {
-  __shared__ uint8_t tile[64][64 + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kQtCols * kQtPitch];
   const float scale = fp8_scale_from_amax(*amax);
   if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out != nullptr) {
     *scale_out = scale;
     *scale_inv_out = 1.0f / scale;
   }
-  const int64_t tiles_c = (cols + 63) / 64;
-  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * 64, c0 = (int64_t)(blockIdx.x % tiles_c) * 64;
+  const int64_t tiles_c = (cols + kQtCols - 1) / kQtCols;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kQtRows, c0 = (int64_t)(blockIdx.x % tiles_c) * kQtCols;
   const int t = threadIdx.x;
-  // read: 64 rows x 8 column-chunks = 512 chunks, 2 per thread, both loads in
-  // flight before the first use. Chunks outside the matrix re-read a clamped
-  // in-range chunk: their codes land in tile cells that are never stored.
-  Raw8<BF16> w[2];
+  // rows 4 rg .. 4 rg + 3, columns cc .. cc + 7 of the tile. Rows or columns
+  // outside the matrix re-read a clamped in-range chunk: their codes land in
+  // tile cells that are never stored.
+  const int rg = t >> 3, cc = (t & 7) * 8;
+  Raw8<BF16> w[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + p * kThreads;
-    const int r = idx >> 3, cc = (idx & 7) * 8;
-    load8_raw_ptr<BF16>(x, min(r0 + r, rows - 1) * cols + min(c0 + cc, cols - 8), w[p]);
-  }
+  for (int k = 0; k < 4; ++k)
+    load8_raw_ptr<BF16>(x, min(r0 + 4 * rg + k, rows - 1) * cols + min(c0 + cc, cols - 8), w[k]);
   __builtin_amdgcn_sched_barrier(0);
+  uint32_t lo[4], hi[4];   // row k: codes of columns cc..cc+3 and cc+4..cc+7
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + p * kThreads;
-    const int r = idx >> 3, cc = (idx & 7) * 8;
+  for (int k = 0; k < 4; ++k) {
     float f[8];
-    unpack8_raw<BF16>(w[p], f);
+    unpack8_raw<BF16>(w[k], f);
+    lo[k] = e4m3_pack4(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
+    hi[k] = e4m3_pack4(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale);
+  }
+  // column j of a 4 x 4 block: byte j of rows 0..3 -> one word (row 0 in byte 0)
+  auto column = [](const uint32_t (&v)[4], int j) {
+    const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 8);
+    const uint32_t r01 = __builtin_amdgcn_perm(v[1], v[0], sel);   // bytes: v0.j, v1.j
+    const uint32_t r23 = __builtin_amdgcn_perm(v[3], v[2], sel);   // bytes: v2.j, v3.j
+    return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
+  };
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const uint32_t c = e4m3_pack2(f[i] * scale, f[i + 1] * scale);
-      tile[cc + i][r] = (uint8_t)c;
-      tile[cc + i + 1][r] = (uint8_t)(c >> 8);
-    }
+  for (int j = 0; j < 4; ++j) {
+    *reinterpret_cast<uint32_t*>(tile + (cc + j) * kQtPitch + 4 * rg) = column(lo, j);
+    *reinterpret_cast<uint32_t*>(tile + (cc + 4 + j) * kQtPitch + 4 * rg) = column(hi, j);
   }
   __syncthreads();
-  // write: 64 output rows (= input columns) x 4 chunks of 16 codes
-  const int oc = t >> 2, orr = (t & 3) * 16;
-  if (c0 + oc < cols && r0 + orr < rows) {
-    uint32_t w[4];
+  // write: 64 output rows (= input columns) x 8 chunks of 16 codes, 2 per thread
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[q] = (uint32_t)tile[oc][orr + 4 * q] | ((uint32_t)tile[oc][orr + 4 * q + 1] << 8) |
-             ((uint32_t)tile[oc][orr + 4 * q + 2] << 16) | ((uint32_t)tile[oc][orr + 4 * q + 3] << 24);
+  for (int p = 0; p < 2; ++p) {
+    const int idx = t + p * kThreads;
+    const int oc = idx >> 3, orr = (idx & 7) * 16;
+    if (c0 + oc < cols && r0 + orr < rows) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + oc * kQtPitch + orr);
+      *reinterpret_cast<uint4*>(codes_t + (c0 + oc) * rows + r0 + orr) = make_uint4(src[0], src[1], src[2], src[3]);
     }
-    *reinterpret_cast<uint4*>(codes_t + (c0 + oc) * rows + r0 + orr) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -668,7 +678,7 @@ hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, 
                                      uint8_t* codes_t, const float* amax, float* scale_out,
                                      float* scale_inv_out, hipStream_t s) {
   LaunchScope scope("quantize_transpose", s);
-  const unsigned grid = (unsigned)(((cols + 63) / 64) * ((rows + 63) / 64));   // < 2^18 for weights < 2 GiB
+  const unsigned grid = (unsigned)(((cols + kQtCols - 1) / kQtCols) * ((rows + kQtRows - 1) / kQtRows));   // < 2^17 for weights < 2 GiB
   if (x_dtype == kBF16)
     launch_kernel(quantize_transpose_kernel<true>, grid, kThreads, 0, s, x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
   else
