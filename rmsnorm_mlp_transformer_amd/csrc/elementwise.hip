@@ -151,11 +151,26 @@ __global__ void empty_meta_kernel(float* amax, float* scale, float* scale_inv) {
 // lane keeps kUnroll 16-byte loads in flight per iteration.
 constexpr int kUnroll = 8;
 
+// One tensor of an amax pass: n8 chunks of 8 elements, its own amax slot.
+struct AmaxJob {
+  const void* x;
+  int64_t n8;
+  float* amax;
+};
+
+// Workgroups [0, blocks0) reduce job 0, the rest job 1 (two weights in one
+// launch), each set looping over its tensor.
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) amax_kernel(const void* x, int64_t n8, float* amax) {
+__global__ void __launch_bounds__(kThreads) amax_kernel(AmaxJob j0, AmaxJob j1, unsigned blocks0) {
+  const bool second = blockIdx.x >= blocks0;
+  const AmaxJob& j = second ? j1 : j0;
+  const int64_t blk = second ? blockIdx.x - blocks0 : blockIdx.x;
+  const int64_t nblk = second ? gridDim.x - blocks0 : blocks0;
+  const void* x = j.x;
+  const int64_t n8 = j.n8;
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; c0 < n8; c0 += stride * kUnroll) {
+  const int64_t stride = nblk * kThreads;
+  for (int64_t c0 = blk * kThreads + threadIdx.x; c0 < n8; c0 += stride * kUnroll) {
     // chunks past the end re-read the last one (no change to the max), so
     // every load is unconditional and all are in flight before the first use
     Raw8<BF16> w[kUnroll];
@@ -171,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) amax_kernel(const void* x, int64_t n
     }
   }
   __shared__ float red[kThreads / 64];
-  block_max_atomic(m, amax, red);
+  block_max_atomic(m, j.amax, red);
 }
 
 template <bool BF16>
@@ -211,18 +226,33 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64
 // two 16-byte stores per thread.
 constexpr int kQtRows = 128, kQtCols = 64;
 constexpr int kQtPitch = kQtRows + 4;   // bytes per LDS row: 33 words, odd, spreads the word writes over the banks
+// One matrix of a quantise-transpose pass.
+struct QtJob {
+  const void* x;
+  int64_t rows, cols;
+  uint8_t* codes_t;
+  const float* amax;
+  float* scale_out;        // nullable
+  float* scale_inv_out;
+};
+
+// Workgroups [0, tiles0) take the tiles of job 0, the rest those of job 1.
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(
-    const void* x, int64_t rows, int64_t cols, uint8_t* codes_t, const float* amax,
-    float* scale_out, float* scale_inv_out) {
+__global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(QtJob j0, QtJob j1, unsigned tiles0) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kQtCols * kQtPitch];
-  const float scale = fp8_scale_from_amax(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out != nullptr) {
-    *scale_out = scale;
-    *scale_inv_out = 1.0f / scale;
+  const bool second = blockIdx.x >= tiles0;
+  const QtJob& job = second ? j1 : j0;
+  const int64_t blk = second ? blockIdx.x - tiles0 : blockIdx.x;
+  const void* x = job.x;
+  const int64_t rows = job.rows, cols = job.cols;
+  uint8_t* codes_t = job.codes_t;
+  const float scale = fp8_scale_from_amax(*job.amax);
+  if (blk == 0 && threadIdx.x == 0 && job.scale_out != nullptr) {
+    *job.scale_out = scale;
+    *job.scale_inv_out = 1.0f / scale;
   }
   const int64_t tiles_c = (cols + kQtCols - 1) / kQtCols;
-  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kQtRows, c0 = (int64_t)(blockIdx.x % tiles_c) * kQtCols;
+  const int64_t r0 = (blk / tiles_c) * kQtRows, c0 = (blk % tiles_c) * kQtCols;
   const int t = threadIdx.x;
   // rows 4 rg .. 4 rg + 3, columns cc .. cc + 7 of the tile. Rows or columns
   // outside the matrix re-read a clamped in-range chunk: their codes land in
@@ -655,11 +685,18 @@ hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStr
 }
 
 hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s) {
+  return launch_amax2(x, n, amax, nullptr, 0, nullptr, x_dtype, s);
+}
+
+hipError_t launch_amax2(const void* x0, int64_t n0, float* amax0, const void* x1, int64_t n1, float* amax1,
+                        int x_dtype, hipStream_t s) {
   LaunchScope scope("amax", s);
-  // one atomic per workgroup on a single address: few workgroups, each looping
-  const unsigned grid = min(grid_for(n / 8, kUnroll), kAmaxBlocks / 2);
-  if (x_dtype == kBF16) launch_kernel(amax_kernel<true>, grid, kThreads, 0, s, x, n / 8, amax);
-  else launch_kernel(amax_kernel<false>, grid, kThreads, 0, s, x, n / 8, amax);
+  // one atomic per workgroup on the job's address: few workgroups, each looping
+  const unsigned b0 = min(grid_for(n0 / 8, kUnroll), kAmaxBlocks / 2);
+  const unsigned b1 = n1 > 0 ? min(grid_for(n1 / 8, kUnroll), kAmaxBlocks / 2) : 0u;
+  const AmaxJob j0{x0, n0 / 8, amax0}, j1{x1, n1 / 8, amax1};
+  if (x_dtype == kBF16) launch_kernel(amax_kernel<true>, b0 + b1, kThreads, 0, s, j0, j1, b0);
+  else launch_kernel(amax_kernel<false>, b0 + b1, kThreads, 0, s, j0, j1, b0);
   return hipGetLastError();
 }
 
@@ -677,12 +714,23 @@ hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes
 hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
                                      uint8_t* codes_t, const float* amax, float* scale_out,
                                      float* scale_inv_out, hipStream_t s) {
+  return launch_quantize_transpose2(x, rows, cols, codes_t, amax, scale_out, scale_inv_out, nullptr, 0, 0, nullptr,
+                                    nullptr, nullptr, nullptr, x_dtype, s);
+}
+
+hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes_t0,
+                                      const float* amax0, float* scale0, float* scale_inv0, const void* x1,
+                                      int64_t rows1, int64_t cols1, uint8_t* codes_t1, const float* amax1,
+                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s) {
   LaunchScope scope("quantize_transpose", s);
-  const unsigned grid = (unsigned)(((cols + kQtCols - 1) / kQtCols) * ((rows + kQtRows - 1) / kQtRows));   // < 2^17 for weights < 2 GiB
-  if (x_dtype == kBF16)
-    launch_kernel(quantize_transpose_kernel<true>, grid, kThreads, 0, s, x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
-  else
-    launch_kernel(quantize_transpose_kernel<false>, grid, kThreads, 0, s, x, rows, cols, codes_t, amax, scale_out, scale_inv_out);
+  auto tiles = [](int64_t r, int64_t c) {   // < 2^17 for weights < 2 GiB
+    return (unsigned)(((c + kQtCols - 1) / kQtCols) * ((r + kQtRows - 1) / kQtRows));
+  };
+  const unsigned t0 = tiles(rows0, cols0), t1 = rows1 > 0 ? tiles(rows1, cols1) : 0u;
+  const QtJob j0{x0, rows0, cols0, codes_t0, amax0, scale0, scale_inv0};
+  const QtJob j1{x1, rows1, cols1, codes_t1, amax1, scale1, scale_inv1};
+  if (x_dtype == kBF16) launch_kernel(quantize_transpose_kernel<true>, t0 + t1, kThreads, 0, s, j0, j1, t0);
+  else launch_kernel(quantize_transpose_kernel<false>, t0 + t1, kThreads, 0, s, j0, j1, t0);
   return hipGetLastError();
 }
 

@@ -741,14 +741,12 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
     if (m->amax < w.metas || m->amax >= w.metas + 12) TE_HIP(te::launch_fill_zero(m->amax, 1, s), "fill");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr, mu,
                          rsigma, mx.amax, nullptr, nullptr, s), "norm amax");
-  TE_HIP(te::launch_amax(kernel1, hidden * nb1, dtype, m1.amax, s), "kernel1 amax");
-  TE_HIP(te::launch_amax(kernel2, ffn * hidden, dtype, m2.amax, s), "kernel2 amax");
+  TE_HIP(te::launch_amax2(kernel1, hidden * nb1, m1.amax, kernel2, ffn * hidden, m2.amax, dtype, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
                          nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, s), "norm quantise");
-  TE_HIP(te::launch_quantize_transpose(kernel1, hidden, nb1, dtype, w.w1t, m1.amax, m1.scale, m1.scale_inv, s),
-         "kernel1 quantise");
-  TE_HIP(te::launch_quantize_transpose(kernel2, ffn, hidden, dtype, w.w2t, m2.amax, m2.scale, m2.scale_inv, s),
-         "kernel2 quantise");
+  TE_HIP(te::launch_quantize_transpose2(kernel1, hidden, nb1, w.w1t, m1.amax, m1.scale, m1.scale_inv, kernel2, ffn,
+                                        hidden, w.w2t, m2.amax, m2.scale, m2.scale_inv, dtype, s),
+         "kernel quantise");
   te::Epilogue e1{bias1, nullptr, h1, ma.amax, k, gated};
   TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.w1t, rows, nb1, hidden, mx.amax, m1.amax, e1, s),
          "fp8 gemm1");

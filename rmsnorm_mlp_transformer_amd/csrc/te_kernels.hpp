@@ -63,6 +63,9 @@ hipError_t launch_empty_meta(float* amax, float* scale, float* scale_inv, hipStr
 
 // amax of |x| over n elements into *amax (atomic max, *amax must start at 0).
 hipError_t launch_amax(const void* x, int64_t n, int x_dtype, float* amax, hipStream_t s);
+// The same for two tensors of one dtype in one launch (n1 = 0: only the first).
+hipError_t launch_amax2(const void* x0, int64_t n0, float* amax0, const void* x1, int64_t n1, float* amax1,
+                        int x_dtype, hipStream_t s);
 
 // codes[i] = E4M3(x[i] * scale), scale from *amax; writes scale/scale_inv.
 hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes,
@@ -74,6 +77,11 @@ hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes
 hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
                                      uint8_t* codes_t, const float* amax, float* scale_out,
                                      float* scale_inv_out, hipStream_t s);
+// The same for two matrices of one dtype in one launch (rows1 = 0: only the first).
+hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes_t0,
+                                      const float* amax0, float* scale0, float* scale_inv0, const void* x1,
+                                      int64_t rows1, int64_t cols1, uint8_t* codes_t1, const float* amax1,
+                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s);
 
 hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale_inv, void* y,
                              int y_dtype, hipStream_t s);
