@@ -1,12 +1,15 @@
 // Row-wise LayerNorm / RMSNorm forward for gfx950.
 //
-// One 64-lane wavefront owns one row: the row is read once into registers
-// with 16-byte loads (each load instruction of the wave covers 1 KiB of the
-// row), the mean and the centred sum of squares are reduced across the wave
-// in fp32, and the normalised row is written straight out in the layout and
-// precision the following GEMM reads as its A operand (fp32, bf16 or E4M3),
-// so no separate normalised tensor is produced. Rows wider than the register
-// budget fall back to a loop that re-reads the row from cache.
+// One 64-lane wavefront owns one row at a time: the row is read once into
+// registers with 16-byte loads (each load instruction of the wave covers
+// 1 KiB of the row), the mean and the centred sum of squares are reduced
+// across the wave in fp32, and the normalised row is written straight out in
+// the layout and precision the following GEMM reads as its A operand (fp32,
+// bf16 or E4M3), so no separate normalised tensor is produced. The grid is
+// capped and each wave walks several rows with the next row's loads in
+// flight while the current one is reduced; gamma and beta sit in LDS, read
+// once per workgroup. Rows wider than the register budget fall back to a
+// loop that re-reads the row from cache.
 //
 // Definitions ("NVIDIA TransformerEngine JAX LayerNorm MLP", Description step
 // (1); "... LayerNorm Dense", Inputs: gamma, beta, norm_type,
@@ -20,6 +23,14 @@
 
 namespace te {
 namespace {
+
+// Workgroups of the norm forward's store and quantise passes (4 waves each;
+// 768 = three per CU, the occupancy of the 8-chunk row at ~140 VGPRs, was the
+// fastest of 512 / 768 / 1024 at 8192 x 4096).
+#ifndef TE_NORM_BLOCKS
+#define TE_NORM_BLOCKS 768
+#endif
+constexpr int kNormBlocks = TE_NORM_BLOCKS;
 
 template <bool BF16>
 struct Io {
@@ -109,71 +120,105 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   };
   using Stream = std::true_type;
   using Cached = std::false_type;
-  // one wave per row (the loop covers grids smaller than rows / 4)
+  // gamma and beta, read once per workgroup into LDS (rows of up to NCH * 64
+  // chunks use the register path below)
+  __shared__ uint4 sg[NCH > 0 ? NCH * 64 : 1], sb[NCH > 0 && !RMS ? NCH * 64 : 1];
+  if constexpr (NCH > 0) {
+    for (int64_t c = threadIdx.x; c < nch; c += blockDim.x) {
+      sg[c] = load16(rgam, c, Cached{});
+      if constexpr (!RMS) sb[c] = load16(rbet, c, Cached{});
+    }
+    __syncthreads();
+  }
+  // one wave per row; a wave loops over rows wave, wave + 4 G, ... of a grid
+  // of G workgroups
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < a.rows; row += (int64_t)gridDim.x * 4) {
-    const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
+  const int64_t step = (int64_t)gridDim.x * 4;
+  int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  // the output of one row from its 16-byte chunks (x, gamma, beta in registers)
+  auto finish_row = [&](int64_t row, const uint4* xw) {
     float mean = 0.0f, rs;
+    float v[NCH > 0 ? NCH : 1][VEC];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      I::unpack(xw[j], v[j]);
+      if constexpr (!RMS) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s += v[j][i];
+      }
+    }
+    if constexpr (!RMS) mean = wave_sum(s) * inv_h;
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      if (lane + 64 * j < nch) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float d = v[j][i] - mean;
+          ss += d * d;
+        }
+      }
+    }
+    rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
+    if constexpr (MODE != kNormQuant) {
+      if (lane == 0) {
+        if (a.mu != nullptr && !RMS) a.mu[row] = mean;
+        if (a.rsigma != nullptr) a.rsigma[row] = rs;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int64_t c = lane + 64 * j;
+      if (c < nch) {
+        float g[VEC], b[VEC], y[VEC];
+        I::unpack(sg[c], g);
+        if constexpr (!RMS) I::unpack(sb[c], b);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+          const float gi = a.zcg ? 1.0f + g[i] : g[i];
+          y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
+          lmax = fmaxf(lmax, fabsf(y[i]));
+        }
+        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+      }
+    }
+  };
+  if (row < a.rows) {
     if constexpr (NCH > 0) {
-      // all of the row's loads (x, gamma, beta) are issued before the first
-      // use, so that a wave has them in flight together
-      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(xr), (short)0,
-                                                                          (int)row_bytes, 0x00020000);
-      uint4 xw[NCH], gw[NCH], bw[NCH];
+      // the next row's x is in flight while the current one is reduced and
+      // written (two register sets used
+      // alternately, so no load result is copied before it arrives). Rows past
+      // the end get an empty buffer range: their loads return zero and touch
+      // no memory, so every load is unconditional.
+      auto load_row = [&](int64_t r, uint4* xw) {
+        const bool ok = r < a.rows;
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint4*>(reinterpret_cast<const uint4*>(a.x) + (ok ? r : 0) * nch), (short)0,
+            ok ? (int)row_bytes : 0, 0x00020000);
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) xw[j] = load16(rx, lane + 64 * j, Stream{});
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        gw[j] = load16(rgam, lane + 64 * j, Cached{});
-        if constexpr (!RMS) bw[j] = load16(rbet, lane + 64 * j, Cached{});
+        for (int j = 0; j < NCH; ++j) xw[j] = load16(rx, lane + 64 * j, Stream{});
+      };
+      uint4 xa[NCH], xb[NCH];
+      load_row(row, xa);
+      while (true) {
+        load_row(row + step, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        finish_row(row, xa);
+        row += step;
+        if (row >= a.rows) break;
+        load_row(row + step, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        finish_row(row, xb);
+        row += step;
+        if (row >= a.rows) break;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      float v[NCH][VEC];
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        I::unpack(xw[j], v[j]);
-        if constexpr (!RMS) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) s += v[j][i];
-        }
-      }
-      if constexpr (!RMS) mean = wave_sum(s) * inv_h;
-      float ss = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        if (lane + 64 * j < nch) {
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            const float d = v[j][i] - mean;
-            ss += d * d;
-          }
-        }
-      }
-      rs = rsqrtf(wave_sum(ss) * inv_h + a.eps);
-      if constexpr (MODE != kNormQuant) {
-        if (lane == 0) {
-          if (a.mu != nullptr && !RMS) a.mu[row] = mean;
-          if (a.rsigma != nullptr) a.rsigma[row] = rs;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int64_t c = lane + 64 * j;
-        if (c < nch) {
-          float g[VEC], b[VEC], y[VEC];
-          I::unpack(gw[j], g);
-          if constexpr (!RMS) I::unpack(bw[j], b);
-#pragma unroll
-          for (int i = 0; i < VEC; ++i) {
-            const float gi = a.zcg ? 1.0f + g[i] : g[i];
-            y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
-            lmax = fmaxf(lmax, fabsf(y[i]));
-          }
-          if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
-        }
-      }
-    } else {
+    }
+  }
+  if constexpr (NCH == 0) {
+    for (; row < a.rows; row += step) {
+      const uint4* xr = reinterpret_cast<const uint4*>(a.x) + row * nch;
+      float mean = 0.0f, rs;
       float s = 0.0f, v[VEC];
       if constexpr (!RMS) {
         for (int64_t c = lane; c < nch; c += 64) {
@@ -222,10 +267,12 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
 
 template <bool BF16, int NCH, bool RMS>
 hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s) {
-  // one row per wave; the amax pass caps the grid (one atomic per workgroup on
-  // a single address serialises in the L2) and its waves loop over rows
+  // one row per wave at a time; the grid is capped and the waves loop over
+  // rows (the next row loads while one is reduced). The amax pass keeps its
+  // own cap: one atomic per workgroup on a single address serialises in the L2.
   const int64_t blocks = (a.rows + 3) / 4;
-  const dim3 grid((unsigned)(mode == kNormAmax && blocks > kAmaxBlocks ? kAmaxBlocks : blocks)), block(256);
+  const int64_t cap = mode == kNormAmax ? (int64_t)kAmaxBlocks : (int64_t)kNormBlocks;
+  const dim3 grid((unsigned)(blocks > cap ? cap : blocks)), block(256);
   if (mode == kNormAmax) {
     launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32>, grid, block, 0, s, a);
   } else if (mode == kNormQuant) {

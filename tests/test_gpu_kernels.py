@@ -22,7 +22,10 @@ def _norm_inputs(rows, hidden, dtype, zcg, seed=0):
     return x, gamma, beta
 
 
-NORM_SHAPES = [(1, 16), (37, 128), (64, 4096), (5, 4112), (130, 768), (3, 8192 + 512)]
+# the last two give every wave of the capped grid several rows (the
+# next-row prefetch) and a ragged final round
+NORM_SHAPES = [(1, 16), (37, 128), (64, 4096), (5, 4112), (130, 768), (3, 8192 + 512), (4099, 1024),
+               (2309, 4096)]
 
 
 @pytest.mark.parametrize("rows,hidden", NORM_SHAPES)
@@ -46,7 +49,7 @@ def test_norm_matches_oracle(rows, hidden, dtype, norm, zcg):
         assert np.max(np.abs(f64(mu) - rmu)) <= 1e-5 * scale
 
 
-@pytest.mark.parametrize("rows,hidden", [(37, 128), (64, 4096), (5, 4112)])
+@pytest.mark.parametrize("rows,hidden", [(37, 128), (64, 4096), (5, 4112), (2309, 4096)])
 @pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
 def test_norm_e4m3_output(rows, hidden, norm):
     print(f"norm e4m3 {norm} {rows}x{hidden}", flush=True)
