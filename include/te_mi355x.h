@@ -15,7 +15,11 @@
  *    caller. The library never allocates or frees device memory and keeps no
  *    pointer after a call returns. Device pointers must be 16-byte aligned.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the
- *    null stream) and never synchronises the host.
+ *    null stream) and never synchronises the host. A call issues kernel
+ *    launches only (no allocation, copy, memset or event), so it can be
+ *    captured into a HIP graph and replayed; with timing on
+ *    (te_timing_enable) the launches also carry events and must not be
+ *    captured.
  *  - Arguments are fully validated before the first launch: a non-zero status
  *    means nothing was written. The message for the last failure on the
  *    calling thread is available from te_last_error(). Launch failures map to
