@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   const int tiles_m = (M + kTileM - 1) / kTileM;
   const int tiles_n = GATED ? (F + 127) / 128 : (NB + kTileN - 1) / kTileN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, a.ep.group, tm, tn);
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
 
@@ -341,6 +341,7 @@ hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t
   a.ep.M = (int)M;
   a.ep.n_b = (int)n_b;
   a.ep.F = (int)n_b;
+  a.ep.group = 8;
   const unsigned grid = (unsigned)(((M + kTileM - 1) / kTileM) * ((n_b + kTileN - 1) / kTileN));
   launch_kernel(gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, true>, grid, 64 * kWaves, 0, s, a);
   return hipGetLastError();
@@ -362,6 +363,7 @@ hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b
   a.ep.F = e.gated ? (int)(n_b / 2) : (int)n_b;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
+  a.ep.group = tile_group(tiles_n, false, e.gated);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
 #define TE_G(A_) return e.gated ? launch_flags<A_, true>(a, grid, s) : launch_flags<A_, false>(a, grid, s)
   switch (e.act) {

@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   const int tiles_m = (M + kTileM - 1) / kTileM;
   const int tiles_n = GATED ? (F + 127) / 128 : (NB + kTileN - 1) / kTileN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, a.ep.group, tm, tn);
   const int m0 = tm * kTileM;
   const int n0 = GATED ? tn * 128 : tn * kTileN;
   const uint32_t pitch = (uint32_t)K * E;  // bytes per operand row (< 2^31, checked by the caller)
@@ -287,6 +287,7 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
   a.ep.F = e.gated ? (int)(n_b / 2) : (int)n_b;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
+  a.ep.group = FP8 ? tile_group(tiles_n, true, e.gated) : 8;
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
   if constexpr (!FP8) {   // the bf16 data-gradient GEMMs have a plain linear epilogue
     return launch_flags<false, kLinear, false>(a, grid, s);

@@ -48,6 +48,7 @@ struct EpiArgs {
   uint16_t* h_out;        // bf16 [M, n_b] or NULL
   float* amax;            // or NULL
   int M, n_b, F;          // F = n_b / 2 when gated, else n_b
+  int group;              // row-tiles per group of the tile walk (tile_group())
 };
 
 // LDS row (0..255) of B-fragment block j (of NJ) for wave column wn.
@@ -64,20 +65,32 @@ __device__ __forceinline__ int b_block_row(int wn, int j) {
 // Maps the linear workgroup index to a (tile_m, tile_n) pair. Workgroups are
 // dealt round-robin to the 8 XCDs (each with its own L2), so the index is
 // first regrouped so that consecutive logical tiles land on one XCD; the
-// logical order then walks groups of 8 row-tiles across all column-tiles, so
-// the tiles resident on an XCD at one time share A and B panels in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+// logical order then walks groups of `group` row-tiles across all
+// column-tiles, so the tiles resident on an XCD at one time share A and B
+// panels in its L2.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   int b = blockIdx.x;
   if ((total & 7) == 0) b = (b & 7) * (total >> 3) + (b >> 3);
-  constexpr int kGroup = 8;
-  const int per_group = kGroup * tiles_n;
-  const int group = b / per_group;
-  const int first_m = group * kGroup;
-  const int gsz = min(tiles_m - first_m, kGroup);
-  const int in_group = b - group * per_group;
+  const int per_group = group * tiles_n;
+  const int grp = b / per_group;
+  const int first_m = grp * group;
+  const int gsz = min(tiles_m - first_m, group);
+  const int in_group = b - grp * per_group;
   tm = first_m + in_group % gsz;
   tn = in_group / gsz;
+}
+
+// Row-tiles per group of the walk above. The XCD's ~32 resident tiles cover
+// group x (32 / group) tiles; 4 and 8 minimise the panels they read. A sweep
+// at the workloads' shapes (2, 4, 8, 16; interleaved runs on one box) picked,
+// for 64 or more column-tiles, 4 for the bf16 GEMM and 2 for the fp8 GEMM
+// (0.5% and 1-3% faster than 8), and for fewer column-tiles 8 and 4; the
+// gated GEMM1 keeps 8 (4 was 0.4% slower); 16 was up to 30% slower.
+inline int tile_group(int64_t tiles_n, bool fp8, bool gated) {
+  if (gated) return 8;
+  if (fp8) return tiles_n >= 64 ? 2 : 4;
+  return tiles_n >= 64 ? 4 : 8;
 }
 
 // Global column of tile column tc (gated tiles hold [n0, n0 + 128) of the
