@@ -60,8 +60,8 @@ KERNEL_SOURCES = {
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summaries are
 # profiles/gemm_bf16_act_ln_mlp_gelu_bf16.md and profiles/dact_dbias_8192x16384_gelu.md.
 TRAFFIC = {
-    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879608648, "2ee1e708d851d94a"),
-    ("dact_dbias_gelu_bf16", "dact_dbias"): (822160875, "563261d78375dbc6"),
+    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879501139, "c126a16acd15a30a"),
+    ("dact_dbias_gelu_bf16", "dact_dbias"): (822150329, "07a208341bb88ca7"),
 }
 
 
