@@ -49,10 +49,12 @@ import workloads as W  # noqa: E402
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
 CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
-_GEMM = ["gemm_bf16.hip", "gemm_bt.hip", "gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
+_GEMM_HDR = ["gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
+_GEMM_NC = ["gemm_bf16.hip"] + _GEMM_HDR     # N-contiguous bf16 kernel
+_GEMM_KC = ["gemm_bt.hip"] + _GEMM_HDR       # K-contiguous kernel (fp8, bf16 data-gradient)
 KERNEL_SOURCES = {
-    "gemm_bf16_act": _GEMM, "gemm_bf16": _GEMM, "gemm_bf16_gated": _GEMM, "gemm_fp8_h_amax": _GEMM,
-    "gemm_fp8": _GEMM, "gemm_bf16_dgrad": _GEMM, "gemm_bf16_wgrad": _GEMM,
+    "gemm_bf16_act": _GEMM_NC, "gemm_bf16": _GEMM_NC, "gemm_bf16_gated": _GEMM_NC, "gemm_bf16_wgrad": _GEMM_NC,
+    "gemm_fp8_h_amax": _GEMM_KC, "gemm_fp8": _GEMM_KC, "gemm_bf16_dgrad": _GEMM_KC,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
     "norm_bwd": ["norm_bwd.hip", "te_common.hpp"],
 }
@@ -60,7 +62,7 @@ KERNEL_SOURCES = {
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summaries are
 # profiles/gemm_bf16_act_ln_mlp_gelu_bf16.md and profiles/dact_dbias_8192x16384_gelu.md.
 TRAFFIC = {
-    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879501139, "c126a16acd15a30a"),
+    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879501139, "86903035431b075e"),
     ("dact_dbias_gelu_bf16", "dact_dbias"): (822150329, "07a208341bb88ca7"),
 }
 
