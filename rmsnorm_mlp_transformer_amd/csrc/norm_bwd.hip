@@ -198,26 +198,44 @@ __global__ void __launch_bounds__(kBwdThreads) norm_bwd_kernel(BwdArgs a) {
 
 // Sum of the per-workgroup partial rows: 16 threads per column each add a
 // fixed, contiguous range of rows, then one of them adds the 16 results in
-// order (a fixed order: bitwise reproducible).
+// order (a fixed order: bitwise reproducible). blockIdx.y selects the
+// parameter (0: dgamma, 1: dbeta), so both sums take one launch; the row
+// loop is unrolled so that four loads per thread are in flight.
+struct FinJob {
+  const float* part;
+  void* out;            // nullable: the parameter is not wanted
+};
 template <int OUT>
-__global__ void __launch_bounds__(256) param_finalize_kernel(const float* part, int64_t blocks, int64_t n, void* out) {
+__global__ void __launch_bounds__(256) param_finalize_kernel(FinJob j0, FinJob j1, int64_t blocks, int64_t n) {
   constexpr int S = 16;
   __shared__ float red[S][16];
+  const FinJob& j = blockIdx.y == 0 ? j0 : j1;
+  if (j.out == nullptr) return;   // uniform across the workgroup
   const int cl = threadIdx.x % 16, sp = threadIdx.x / 16;
   const int64_t c = (int64_t)blockIdx.x * 16 + cl;
   const int64_t per = (blocks + S - 1) / S;
   const int64_t k0 = sp * per, k1 = min(k0 + per, blocks);
   float s = 0.0f;
-  if (c < n)
-    for (int64_t k = k0; k < k1; ++k) s += part[k * n + c];
+  if (c < n) {
+    int64_t k = k0;
+    for (; k + 4 <= k1; k += 4) {
+      const float a0 = j.part[k * n + c], a1 = j.part[(k + 1) * n + c];
+      const float a2 = j.part[(k + 2) * n + c], a3 = j.part[(k + 3) * n + c];
+      s += a0;
+      s += a1;
+      s += a2;
+      s += a3;
+    }
+    for (; k < k1; ++k) s += j.part[k * n + c];
+  }
   red[sp][cl] = s;
   __syncthreads();
   if (sp == 0 && c < n) {
     float t = red[0][cl];
 #pragma unroll
     for (int q = 1; q < S; ++q) t += red[q][cl];
-    if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(out)[c] = f32_to_bf16(t);
-    else reinterpret_cast<float*>(out)[c] = t;
+    if constexpr (OUT == kBF16) reinterpret_cast<uint16_t*>(j.out)[c] = f32_to_bf16(t);
+    else reinterpret_cast<float*>(j.out)[c] = t;
   }
 }
 
@@ -268,14 +286,10 @@ hipError_t launch_norm_bwd(const void* dy, const void* x, const float* mu, const
   }
   if (!params) return hipSuccess;
   LaunchScope scope("norm_bwd_finalize", s);
-  const unsigned g = (unsigned)((hidden + 15) / 16);
-  for (int p = 0; p < 2; ++p) {
-    void* out = p == 0 ? dgamma : dbeta;
-    const float* part = p == 0 ? part_g : part_b;
-    if (out == nullptr || (p == 1 && rms)) continue;
-    if (dparam_dtype == kBF16) launch_kernel(param_finalize_kernel<kBF16>, g, 256, 0, s, part, blocks, hidden, out);
-    else launch_kernel(param_finalize_kernel<kF32>, g, 256, 0, s, part, blocks, hidden, out);
-  }
+  const FinJob jg{part_g, dgamma}, jb{part_b, rms ? nullptr : dbeta};
+  const dim3 g((unsigned)((hidden + 15) / 16), jb.out != nullptr ? 2u : 1u);
+  if (dparam_dtype == kBF16) launch_kernel(param_finalize_kernel<kBF16>, g, 256, 0, s, jg, jb, blocks, hidden);
+  else launch_kernel(param_finalize_kernel<kF32>, g, 256, 0, s, jg, jb, blocks, hidden);
   return hipGetLastError();
 }
 
