@@ -218,13 +218,21 @@ __global__ void __launch_bounds__(kThreads) quantize_kernel(const void* x, int64
 }
 
 // Quantise x [rows, cols] into codes_t [cols, rows]. A workgroup takes a
-// 128-row x 64-column tile: each thread loads 4 consecutive rows x 8 columns
-// (four 16-byte bf16 loads, all in flight before the first use), encodes
-// them, transposes the 4 x 4 code blocks in registers (v_perm_b32) and
-// writes one 4-byte word per column into an LDS tile [64 columns][128 rows];
-// the tile then leaves as 64 output rows of 128 codes (full 128-byte lines),
-// two 16-byte stores per thread.
-constexpr int kQtRows = 128, kQtCols = 64;
+// 128-row x kQtCols-column tile: for each 64-column half, each thread loads 4
+// consecutive rows x 8 columns (all 16-byte loads of the tile in flight
+// before the first use), encodes them, transposes the 4 x 4 code blocks in
+// registers (v_perm_b32) and writes one 4-byte word per column into an LDS
+// tile [kQtCols columns][128 rows]; the tile then leaves as kQtCols output
+// rows of 128 codes (full 128-byte lines), 16-byte stores.
+// 256 columns (four halves, 16 loads per thread in flight): a sweep of
+// 64 / 128 / 256 at the 4096 x 16384 and 16384 x 4096 weights took the
+// pass over both from 0.0715 to 0.066 ms.
+#ifndef TE_QT_COLS
+#define TE_QT_COLS 256
+#endif
+constexpr int kQtRows = 128, kQtCols = TE_QT_COLS;
+constexpr int kQtHalves = kQtCols / 64;
+static_assert(kQtCols % 64 == 0, "whole 64-column halves");
 constexpr int kQtPitch = kQtRows + 4;   // bytes per LDS row: 33 words, odd, spreads the word writes over the banks
 // One matrix of a quantise-transpose pass.
 struct QtJob {
@@ -257,20 +265,16 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(QtJob j0, 
   // rows 4 rg .. 4 rg + 3, columns cc .. cc + 7 of the tile. Rows or columns
   // outside the matrix re-read a clamped in-range chunk: their codes land in
   // tile cells that are never stored.
-  const int rg = t >> 3, cc = (t & 7) * 8;
-  Raw8<BF16> w[4];
+  const int rg = t >> 3;
+  Raw8<BF16> w[kQtHalves][4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    load8_raw_ptr<BF16>(x, min(r0 + 4 * rg + k, rows - 1) * cols + min(c0 + cc, cols - 8), w[k]);
-  __builtin_amdgcn_sched_barrier(0);
-  uint32_t lo[4], hi[4];   // row k: codes of columns cc..cc+3 and cc+4..cc+7
+  for (int h = 0; h < kQtHalves; ++h) {
+    const int cc = (t & 7) * 8 + 64 * h;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float f[8];
-    unpack8_raw<BF16>(w[k], f);
-    lo[k] = e4m3_pack4(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
-    hi[k] = e4m3_pack4(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale);
+    for (int k = 0; k < 4; ++k)
+      load8_raw_ptr<BF16>(x, min(r0 + 4 * rg + k, rows - 1) * cols + min(c0 + cc, cols - 8), w[h][k]);
   }
+  __builtin_amdgcn_sched_barrier(0);
   // column j of a 4 x 4 block: byte j of rows 0..3 -> one word (row 0 in byte 0)
   auto column = [](const uint32_t (&v)[4], int j) {
     const uint32_t sel = (uint32_t)j | ((uint32_t)(4 + j) << 8);
@@ -279,14 +283,26 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(QtJob j0, 
     return __builtin_amdgcn_perm(r23, r01, 0x05040100u);
   };
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    *reinterpret_cast<uint32_t*>(tile + (cc + j) * kQtPitch + 4 * rg) = column(lo, j);
-    *reinterpret_cast<uint32_t*>(tile + (cc + 4 + j) * kQtPitch + 4 * rg) = column(hi, j);
+  for (int h = 0; h < kQtHalves; ++h) {
+    const int cc = (t & 7) * 8 + 64 * h;
+    uint32_t lo[4], hi[4];   // row k: codes of columns cc..cc+3 and cc+4..cc+7
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float f[8];
+      unpack8_raw<BF16>(w[h][k], f);
+      lo[k] = e4m3_pack4(f[0] * scale, f[1] * scale, f[2] * scale, f[3] * scale);
+      hi[k] = e4m3_pack4(f[4] * scale, f[5] * scale, f[6] * scale, f[7] * scale);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint32_t*>(tile + (cc + j) * kQtPitch + 4 * rg) = column(lo, j);
+      *reinterpret_cast<uint32_t*>(tile + (cc + 4 + j) * kQtPitch + 4 * rg) = column(hi, j);
+    }
   }
   __syncthreads();
-  // write: 64 output rows (= input columns) x 8 chunks of 16 codes, 2 per thread
+  // write: kQtCols output rows (= input columns) x 8 chunks of 16 codes
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < 2 * kQtHalves; ++p) {
     const int idx = t + p * kThreads;
     const int oc = idx >> 3, orr = (idx & 7) * 16;
     if (c0 + oc < cols && r0 + orr < rows) {
