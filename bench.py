@@ -63,7 +63,7 @@ KERNEL_SOURCES = {
 # profiles/gemm_bf16_act_ln_mlp_gelu_bf16.md and profiles/dact_dbias_8192x16384_gelu.md.
 TRAFFIC = {
     ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879501139, "86903035431b075e"),
-    ("dact_dbias_gelu_bf16", "dact_dbias"): (822139476, "553fec836c60ffe6"),
+    ("dact_dbias_gelu_bf16", "dact_dbias"): (822149715, "aca40937c0da79e2"),
 }
 
 
