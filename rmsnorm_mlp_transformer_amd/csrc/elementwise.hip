@@ -312,6 +312,48 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(QtJob j0, 
   }
 }
 
+// y [cols, rows] = x [rows, cols]^T for bf16 (the weights of the backward's
+// data-gradient GEMMs, so that they run on the N-contiguous kernel). A
+// workgroup takes a 64 x 64 tile: each thread loads two 16-byte row chunks
+// (rows and columns past the matrix re-read a clamped in-range chunk whose
+// values are never stored), writes them into an LDS tile with an odd word
+// pitch, and gathers 8 consecutive rows of one column into a 16-byte output
+// chunk; a wave stores 8 output rows of 128 bytes.
+constexpr int kTrTile = 64;
+constexpr int kTrPitch = kTrTile * 2 + 4;   // bytes per LDS row: 33 words
+__global__ void __launch_bounds__(kThreads) transpose_bf16_kernel(const uint16_t* x, int64_t rows, int64_t cols,
+                                                                  uint16_t* y) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTrTile * kTrPitch];
+  const int64_t tiles_c = (cols + kTrTile - 1) / kTrTile;
+  const int64_t r0 = (int64_t)(blockIdx.x / tiles_c) * kTrTile, c0 = (int64_t)(blockIdx.x % tiles_c) * kTrTile;
+  const int t = threadIdx.x, q = t & 7, rr = t >> 3;
+  uint4 v[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int64_t r = min(r0 + rr + 32 * k, rows - 1), c = min(c0 + 8 * q, cols - 8);
+    v[k] = load_stream16(x + r * cols + c);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    uint32_t* d = reinterpret_cast<uint32_t*>(tile + (rr + 32 * k) * kTrPitch + 16 * q);
+    d[0] = v[k].x; d[1] = v[k].y; d[2] = v[k].z; d[3] = v[k].w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = t + k * kThreads;
+    const int oc = idx >> 3, p = idx & 7;   // output row (input column), 8-row chunk
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = *reinterpret_cast<const uint16_t*>(tile + (8 * p + i) * kTrPitch + 2 * oc);
+    if (c0 + oc < cols && r0 + 8 * p < rows) {
+      const uint4 w = make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                                 e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16));
+      *reinterpret_cast<uint4*>(y + (c0 + oc) * rows + r0 + 8 * p) = w;
+    }
+  }
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* codes, int64_t n8,
                                                               const float* scale_inv, void* y) {
@@ -764,6 +806,14 @@ hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t col
   const QtJob j1{x1, rows1, cols1, codes_t1, amax1, scale1, scale_inv1};
   if (x_dtype == kBF16) launch_kernel(quantize_transpose_kernel<true>, t0 + t1, kThreads, 0, s, j0, j1, t0);
   else launch_kernel(quantize_transpose_kernel<false>, t0 + t1, kThreads, 0, s, j0, j1, t0);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* x, int64_t rows, int64_t cols, void* y, hipStream_t s) {
+  LaunchScope scope("transpose", s);
+  const unsigned tiles = (unsigned)(((rows + kTrTile - 1) / kTrTile) * ((cols + kTrTile - 1) / kTrTile));
+  launch_kernel(transpose_bf16_kernel, tiles, kThreads, 0, s, reinterpret_cast<const uint16_t*>(x), rows, cols,
+                reinterpret_cast<uint16_t*>(y));
   return hipGetLastError();
 }
 

@@ -349,7 +349,9 @@ hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t
 
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
                             const Epilogue& e, hipStream_t s) {
-  LaunchScope scope(e.gated ? "gemm_bf16_gated" : (e.act == kLinear ? "gemm_bf16" : "gemm_bf16_act"), s);
+  LaunchScope scope(e.name != nullptr ? e.name
+                                      : e.gated ? "gemm_bf16_gated" : (e.act == kLinear ? "gemm_bf16" : "gemm_bf16_act"),
+                    s);
   GemmArgs a;
   a.A = reinterpret_cast<const uint16_t*>(A);
   a.B = reinterpret_cast<const uint16_t*>(B);

@@ -422,6 +422,7 @@ te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, 
 namespace {
 struct MlpBwdWs {
   void* xn; void* act; void* dact; void* dh1; void* dxn;
+  void* wt;   // kernel2^T, then kernel1^T (the data-gradient GEMMs' N-contiguous B operand)
   float* part_dact; float* part_b2; float* part_g; float* part_beta;
 };
 MlpBwdWs mlp_bwd_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int act) {
@@ -432,6 +433,7 @@ MlpBwdWs mlp_bwd_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int ac
   w.dact = c.take((size_t)rows * ffn * 2);
   w.dh1 = c.take((size_t)rows * g * ffn * 2);
   w.dxn = c.take((size_t)rows * hidden * 2);
+  w.wt = c.take((size_t)hidden * g * ffn * 2);
   w.part_dact = c.floats((size_t)te::dact_row_chunks(rows, ffn, g == 2) * g * ffn);
   w.part_b2 = c.floats((size_t)te::dact_row_chunks(rows, hidden, false) * hidden);
   const int64_t nb = te::norm_bwd_blocks(rows, hidden, TE_BF16);
@@ -499,10 +501,16 @@ te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamm
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zero_centered_gamma != 0, epsilon, te::kNormStore,
                          dtype, w.xn, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
   TE_HIP(te::launch_act(h1, rows, ffn, dtype, k, gated, 0, w.act, dtype, nullptr, nullptr, nullptr, s), "act");
-  // GEMM2: dact = grad @ kernel2^T, dkernel2 = act^T @ grad, dbias2 = sum of grad
+  // GEMM2: dact = grad @ kernel2^T, dkernel2 = act^T @ grad, dbias2 = sum of grad.
+  // The data-gradient GEMMs run on the N-contiguous kernel with a transposed
+  // copy of the weight (one streaming pass), faster than the K-contiguous
+  // kernel on the weight as stored.
   te::Epilogue e = lin;
   e.out = w.dact;
-  TE_HIP(te::launch_gemm_bf16_bt(grad, kernel2, rows, ffn, hidden, e, s), "dgrad2");
+  e.name = "gemm_bf16_dgrad";
+  TE_HIP(te::launch_transpose_bf16(kernel2, ffn, hidden, w.wt, s), "transpose kernel2");
+  TE_HIP(te::launch_gemm_bf16(grad, w.wt, rows, ffn, hidden, e, s), "dgrad2");
+  e.name = nullptr;
   e.out = dkernel2;
   TE_HIP(te::launch_gemm_bf16_at(w.act, grad, ffn, hidden, rows, e, s), "wgrad2");
   if (dbias2 != nullptr) TE_HIP(te::launch_colsum(grad, rows, hidden, dtype, dbias2, dparam_dtype, w.part_b2, s), "dbias2");
@@ -511,7 +519,10 @@ te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamm
          "dact");
   // GEMM1: dxn = dh1 @ kernel1^T, dkernel1 = xn^T @ dh1
   e.out = w.dxn;
-  TE_HIP(te::launch_gemm_bf16_bt(w.dh1, kernel1, rows, hidden, nb1, e, s), "dgrad1");
+  e.name = "gemm_bf16_dgrad";
+  TE_HIP(te::launch_transpose_bf16(kernel1, hidden, nb1, w.wt, s), "transpose kernel1");
+  TE_HIP(te::launch_gemm_bf16(w.dh1, w.wt, rows, hidden, nb1, e, s), "dgrad1");
+  e.name = nullptr;
   e.out = dkernel1;
   TE_HIP(te::launch_gemm_bf16_at(w.xn, w.dh1, hidden, nb1, rows, e, s), "wgrad1");
   // normalisation backward

@@ -78,6 +78,8 @@ hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, 
                                      uint8_t* codes_t, const float* amax, float* scale_out,
                                      float* scale_inv_out, hipStream_t s);
 // The same for two matrices of one dtype in one launch (rows1 = 0: only the first).
+// y [cols, rows] = x [rows, cols]^T, bf16; rows and cols multiples of 16.
+hipError_t launch_transpose_bf16(const void* x, int64_t rows, int64_t cols, void* y, hipStream_t s);
 hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes_t0,
                                       const float* amax0, float* scale0, float* scale_inv0, const void* x1,
                                       int64_t rows1, int64_t cols1, uint8_t* codes_t1, const float* amax1,
@@ -135,6 +137,7 @@ struct Epilogue {
   float* amax;
   int act;                // ActKind
   bool gated;
+  const char* name = nullptr;   // timing-scope name (default: from act / gated)
 };
 
 // bf16: C[M, n_out] from A [M, K] (row-major) and B [K, n_b] (row-major).
