@@ -51,10 +51,10 @@ CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
 _GEMM_HDR = ["gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
 _GEMM_NC = ["gemm_bf16.hip"] + _GEMM_HDR     # N-contiguous bf16 kernel
-_GEMM_KC = ["gemm_bt.hip"] + _GEMM_HDR       # K-contiguous kernel (fp8, bf16 data-gradient)
+_GEMM_KC = ["gemm_bt.hip"] + _GEMM_HDR       # K-contiguous fp8 kernel
 KERNEL_SOURCES = {
     "gemm_bf16_act": _GEMM_NC, "gemm_bf16": _GEMM_NC, "gemm_bf16_gated": _GEMM_NC, "gemm_bf16_wgrad": _GEMM_NC,
-    "gemm_fp8_h_amax": _GEMM_KC, "gemm_fp8": _GEMM_KC, "gemm_bf16_dgrad": _GEMM_KC,
+    "gemm_bf16_dgrad": _GEMM_NC, "gemm_fp8_h_amax": _GEMM_KC, "gemm_fp8": _GEMM_KC,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
     "norm_bwd": ["norm_bwd.hip", "te_common.hpp"],
 }

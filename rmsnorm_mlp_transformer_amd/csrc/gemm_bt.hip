@@ -1,26 +1,20 @@
-// MFMA GEMM for gfx950 with both operands K-contiguous, in fp8 (E4M3 x
-// E4M3) or bf16, fp32 accumulation and the fused bias / activation / gate /
-// amax epilogue.
-//  - fp8: used when the quantizer set enables per-tensor current scaling:
-//    "NVIDIA TransformerEngine JAX LayerNorm Dense" (Description: the
-//    normalised output and the kernel are quantised, then the GEMM runs) and
-//    "... LayerNorm MLP" (Description: the same for GEMM1 and GEMM2). The
-//    weight quantiser writes the kernel transposed; the accumulator is
-//    multiplied by scale_inv(A) * scale_inv(B), derived from the two amax
-//    values exactly as the quantisers did.
-//  - bf16: the data-gradient GEMMs of the backward ("... LayerNorm MLP",
-//    Description: the backward pass gives the gradients of every parameter),
-//    dY @ kernel^T, where the kernel [K_out, N_in] read row by row is exactly
-//    the K-contiguous B^T operand.
+// fp8 MFMA GEMM for gfx950 with both operands K-contiguous (E4M3 x E4M3),
+// fp32 accumulation and the fused bias / activation / gate / amax epilogue,
+// used when the quantizer set enables per-tensor current scaling:
+// "NVIDIA TransformerEngine JAX LayerNorm Dense" (Description: the
+// normalised output and the kernel are quantised, then the GEMM runs) and
+// "... LayerNorm MLP" (Description: the same for GEMM1 and GEMM2). The
+// weight quantiser writes the kernel transposed; the accumulator is
+// multiplied by scale_inv(A) * scale_inv(B), derived from the two amax
+// values exactly as the quantisers did.
 //
 // A is [M, K] and B^T is [n_b, K], both K-contiguous. Each k stage holds 64
-// bytes of every tile row (64 fp8 or 32 bf16 values) for 256 rows of each
-// operand; both tiles move HBM -> LDS with buffer_load ... lds (16 bytes per
-// lane, no register staging), 16-byte chunks XOR-swizzled per row, and come
-// back with conflict-free ds_read_b128: an fp8 MFMA
-// (v_mfma_f32_32x32x64_f8f6f4, E4M3 for both operands, no block scaling)
-// takes two 16-byte chunks per lane and operand, a bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) one.
+// bytes (64 values) of every tile row for 256 rows of each operand; both
+// tiles move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+// register staging), 16-byte chunks XOR-swizzled per row, and come back with
+// conflict-free ds_read_b128: an MFMA (v_mfma_f32_32x32x64_f8f6f4, E4M3 for
+// both operands, no block scaling) takes two 16-byte chunks per lane and
+// operand.
 //
 // 256 x 256 output tile per workgroup, 8 waves of 128 x 64, 4 LDS stages
 // (128 KiB). Ping-pong schedule: waves 0-3 and 4-7 hold one wave per SIMD
@@ -55,26 +49,18 @@ struct FpArgs {
   EpiArgs ep;
 };
 
-template <bool FP8>
-struct Frags;
-template <>
-struct Frags<true> {        // one 64-k step: [row block] / [column block]
+struct Frags {        // one 64-k step: [row block] / [column block]
   i32x8_t a[4];
   i32x8_t b[kNJ];
-};
-template <>
-struct Frags<false> {       // two 16-k substeps: [substep][row block] / [substep][column block]
-  bf16x8_t a[2][4];
-  bf16x8_t b[2][kNJ];
 };
 
 __device__ __forceinline__ i32x8_t join16x2(const uint4& lo, const uint4& hi) {
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <bool FP8, int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
 __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
-  constexpr int E = FP8 ? 1 : 2;           // bytes per element
+  constexpr int E = 1;                     // bytes per element
   constexpr int KE = kRowBytes / E;        // k values per stage
   // one array per stage: distinct objects let the compiler see that the
   // LDS-DMA of a later stage cannot alias the reads of the current one
@@ -140,8 +126,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   int a_off[2], b_off[kNJ][2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    // fp8: the lane's 32 k bytes are chunks 2 lh and 2 lh + 1; bf16: substep h uses chunk 2 h + lh
-    const int c = FP8 ? 2 * lh + h : 2 * h + lh;
+    // the lane's 32 k bytes are chunks 2 lh and 2 lh + 1
+    const int c = 2 * lh + h;
     a_off[h] = (wm * 128 + lr) * kRowBytes + 16 * (c ^ sw);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j)
@@ -159,51 +145,30 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  Frags<FP8> f;
+  Frags f;
   auto read_frags = [&](int s) {
     const uint8_t* S = stage_ptr(s);
-    if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.a[i] = join16x2(*reinterpret_cast<const uint4*>(S + a_off[0] + i * 32 * kRowBytes),
-                          *reinterpret_cast<const uint4*>(S + a_off[1] + i * 32 * kRowBytes));
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = join16x2(*reinterpret_cast<const uint4*>(S + a_off[0] + i * 32 * kRowBytes),
+                        *reinterpret_cast<const uint4*>(S + a_off[1] + i * 32 * kRowBytes));
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-        f.b[j] = join16x2(*reinterpret_cast<const uint4*>(S + b_off[j][0]),
-                          *reinterpret_cast<const uint4*>(S + b_off[j][1]));
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          f.a[h][i] = *reinterpret_cast<const bf16x8_t*>(S + a_off[h] + i * 32 * kRowBytes);
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) f.b[h][j] = *reinterpret_cast<const bf16x8_t*>(S + b_off[j][h]);
-      }
-    }
+    for (int j = 0; j < kNJ; ++j)
+      f.b[j] = join16x2(*reinterpret_cast<const uint4*>(S + b_off[j][0]),
+                        *reinterpret_cast<const uint4*>(S + b_off[j][1]));
   };
   // B fragment first: each lane then holds 4 consecutive output columns
   auto mfmas = [&]() {
-    if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < kNJ; ++j)
-          // cbsz/blgp = 0: both operands E4M3. With constant zero scale operands
-          // the compiler emits the plain v_mfma_f32_32x32x64_f8f6f4 (no block
-          // scaling, checked in the generated code); with unit E8M0 scales (127)
-          // it emits the scaled form, whose scale operands cost a register and
-          // measured 0.4% slower in GEMM2 (same results).
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < kNJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[h][j], f.a[h][i], acc[i][j], 0, 0, 0);
-    }
+      for (int j = 0; j < kNJ; ++j)
+        // cbsz/blgp = 0: both operands E4M3. With constant zero scale operands
+        // the compiler emits the plain v_mfma_f32_32x32x64_f8f6f4 (no block
+        // scaling, checked in the generated code); with unit E8M0 scales (127)
+        // it emits the scaled form, whose scale operands cost a register and
+        // measured 0.4% slower in GEMM2 (same results).
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, 0, 0, 0);
   };
 
   // ---- ping-pong pipeline.
@@ -248,32 +213,28 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   if (!late) block_barrier();
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the epilogue reuses the LDS
 
-  float scale = 1.0f;
-  if constexpr (FP8) {
-    const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
-    scale = (1.0f / sa) * (1.0f / sb);
-  }
+  const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
+  const float scale = (1.0f / sa) * (1.0f / sb);
   gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, kNJ, 64 * kWaves>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
                                                                        scale, stage_ptr);
 }
 
-template <bool FP8, int ACT, bool GATED>
+template <int ACT, bool GATED>
 hipError_t launch_flags(const FpArgs& a, unsigned grid, hipStream_t s) {
   const bool out = a.ep.out != nullptr, h = a.ep.h_out != nullptr, amax = a.ep.amax != nullptr;
   constexpr int T = 64 * kWaves;
   if (amax) {
-    if (h) launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, true, true>, grid, T, 0, s, a);
-    else launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, false, true>, grid, T, 0, s, a);
+    if (h) launch_kernel(gemm_bt_kernel<ACT, GATED, false, true, true>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bt_kernel<ACT, GATED, false, false, true>, grid, T, 0, s, a);
   } else if (h) {
-    if (out) launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, true, true, false>, grid, T, 0, s, a);
-    else launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, false, true, false>, grid, T, 0, s, a);
+    if (out) launch_kernel(gemm_bt_kernel<ACT, GATED, true, true, false>, grid, T, 0, s, a);
+    else launch_kernel(gemm_bt_kernel<ACT, GATED, false, true, false>, grid, T, 0, s, a);
   } else {
-    launch_kernel(gemm_bt_kernel<FP8, ACT, GATED, true, false, false>, grid, T, 0, s, a);
+    launch_kernel(gemm_bt_kernel<ACT, GATED, true, false, false>, grid, T, 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <bool FP8>
 hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K, const float* amax_a,
                      const float* amax_b, const Epilogue& e, hipStream_t s) {
   FpArgs a;
@@ -291,21 +252,17 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
   a.ep.F = e.gated ? (int)(n_b / 2) : (int)n_b;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
-  a.ep.group = FP8 ? tile_group(tiles_n, true, e.gated) : 8;
+  a.ep.group = tile_group(tiles_n, true, e.gated);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
-  if constexpr (!FP8) {   // the bf16 data-gradient GEMMs have a plain linear epilogue
-    return launch_flags<false, kLinear, false>(a, grid, s);
-  } else {
-#define TE_G(A_) return e.gated ? launch_flags<true, A_, true>(a, grid, s) : launch_flags<true, A_, false>(a, grid, s)
-    switch (e.act) {
-      case kRelu: TE_G(kRelu);
-      case kGelu: TE_G(kGelu);
-      case kGeluErf: TE_G(kGeluErf);
-      case kSilu: TE_G(kSilu);
-      default: TE_G(kLinear);
-    }
-#undef TE_G
+#define TE_G(A_) return e.gated ? launch_flags<A_, true>(a, grid, s) : launch_flags<A_, false>(a, grid, s)
+  switch (e.act) {
+    case kRelu: TE_G(kRelu);
+    case kGelu: TE_G(kGelu);
+    case kGeluErf: TE_G(kGeluErf);
+    case kSilu: TE_G(kSilu);
+    default: TE_G(kLinear);
   }
+#undef TE_G
 }
 
 }  // namespace
@@ -313,14 +270,7 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b, int64_t K,
                            const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s) {
   LaunchScope scope(e.amax != nullptr ? "gemm_fp8_h_amax" : "gemm_fp8", s);
-  return launch_bt<true>(A, Bt, M, n_b, K, amax_a, amax_b, e, s);
-}
-
-hipError_t launch_gemm_bf16_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K, const Epilogue& e,
-                               hipStream_t s) {
-  if (e.act != kLinear || e.gated || e.h_out != nullptr || e.amax != nullptr) return hipErrorInvalidValue;
-  LaunchScope scope("gemm_bf16_dgrad", s);
-  return launch_bt<false>(A, Bt, M, n_b, K, nullptr, nullptr, e, s);
+  return launch_bt(A, Bt, M, n_b, K, amax_a, amax_b, e, s);
 }
 
 }  // namespace te

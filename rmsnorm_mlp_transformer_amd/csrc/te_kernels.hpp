@@ -144,10 +144,6 @@ struct Epilogue {
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
                             const Epilogue& ep, hipStream_t s);
 
-// bf16 with B^T [n_b, K] (both operands K-contiguous), linear epilogue
-// (optional bias): the data-gradient GEMMs of the backward.
-hipError_t launch_gemm_bf16_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K,
-                               const Epilogue& ep, hipStream_t s);
 // bf16 with A^T [K, M] and B [K, n_b] (both row-major with K the row index),
 // linear epilogue: the weight-gradient GEMMs of the backward.
 hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t n_b, int64_t K,
