@@ -272,7 +272,9 @@ size_t te_layernorm_mlp_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t
  * sums written as dparam_dtype (F32 or BF16), each optional (NULL skips it;
  * dbeta is ignored for RMSNorm). [rows, features] tensors and the kernels
  * must be smaller than 2 GiB, hidden at most 16384. Workspace:
- * te_layernorm_mlp_bwd_workspace_size(). */
+ * te_layernorm_mlp_bwd_workspace_size(); it holds xn, act, dact, dh1, dxn,
+ * a transposed copy of one kernel at a time (the data-gradient GEMMs read
+ * kernel2^T and kernel1^T from it) and the fp32 partial sums. */
 te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamma, const void* beta,
                                const void* kernel1, const void* kernel2, const float* mu,
                                const float* rsigma, const void* h1, int64_t rows, int64_t hidden,
