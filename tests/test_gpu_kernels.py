@@ -22,10 +22,11 @@ def _norm_inputs(rows, hidden, dtype, zcg, seed=0):
     return x, gamma, beta
 
 
-# the last two give every wave of the capped grid several rows (the
-# next-row prefetch) and a ragged final round
+# (4099, 1024) and (2309, 4096) give every wave of the capped grid several
+# rows (the next-row prefetch) and a ragged final round; (3, 8704) and
+# (2, 65536) take the loop for rows wider than the register budget
 NORM_SHAPES = [(1, 16), (37, 128), (64, 4096), (5, 4112), (130, 768), (3, 8192 + 512), (4099, 1024),
-               (2309, 4096)]
+               (2309, 4096), (2, 65536)]
 
 
 @pytest.mark.parametrize("rows,hidden", NORM_SHAPES)
