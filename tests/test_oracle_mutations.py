@@ -172,6 +172,59 @@ def _mlp_bwd_dkernel2_from_h(grad, x, gamma, beta, kernel1, kernel2, bias1=None,
     return out
 
 
+_orig_dense_fwd = T.layernorm_dense_fwd
+
+
+def _dense_fwd_quantizes_x(x, kernel, gamma, beta, bias=None, norm_type="layernorm", zero_centered_gamma=False,
+                           epsilon=1e-6, quant="none", round_intermediates=False):
+    if quant == "none":
+        return _orig_dense_fwd(x, kernel, gamma, beta, bias, norm_type, zero_centered_gamma, epsilon, quant,
+                               round_intermediates)
+    xn, mu, rs = T.normalize(x, gamma, beta, norm_type, epsilon, zero_centered_gamma)
+    xq, xm = T.quantize(np.asarray(x, dtype=np.float64))        # the input, not its normalised form
+    wq, wm = T.quantize(kernel)
+    return {"mu": mu, "rsigma": rs, "xn": xn, "xq": xq, "x_meta": xm, "wq": wq, "w_meta": wm,
+            "y": T.fp8_dense(xq, xm, wq, wm, bias)}
+
+
+def _dense_fwd_fp8_drops_bias(x, kernel, gamma, beta, bias=None, norm_type="layernorm", zero_centered_gamma=False,
+                              epsilon=1e-6, quant="none", round_intermediates=False):
+    return _orig_dense_fwd(x, kernel, gamma, beta, None if quant != "none" else bias, norm_type,
+                           zero_centered_gamma, epsilon, quant, round_intermediates)
+
+
+def _dense_fwd_drops_bias(x, kernel, gamma, beta, bias=None, norm_type="layernorm", zero_centered_gamma=False,
+                          epsilon=1e-6, quant="none", round_intermediates=False):
+    return _orig_dense_fwd(x, kernel, gamma, beta, None if quant == "none" else bias, norm_type,
+                           zero_centered_gamma, epsilon, quant, round_intermediates)
+
+
+def _mlp_bwd_truncating_rounds(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=None, norm_type="layernorm",
+                               zero_centered_gamma=False, epsilon=1e-6, activation_type=("relu",), h1=None,
+                               round_intermediates=False):
+    # the backward's bf16 materialisations truncate instead of rounding to nearest
+    saved = T.bf16_round
+    T.bf16_round = _bf16_truncate
+    try:
+        return _orig_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1, bias2, norm_type, zero_centered_gamma,
+                             epsilon, activation_type, h1, round_intermediates)
+    finally:
+        T.bf16_round = saved
+
+
+def _mlp_bwd_rounds_to_e4m3(grad, x, gamma, beta, kernel1, kernel2, bias1=None, bias2=None, norm_type="layernorm",
+                            zero_centered_gamma=False, epsilon=1e-6, activation_type=("relu",), h1=None,
+                            round_intermediates=False):
+    # the wrong narrow format (4 significant bits) at the materialisation points
+    saved = T.bf16_round
+    T.bf16_round = lambda a: T.round_to_bits(a, 4, -6)
+    try:
+        return _orig_mlp_bwd(grad, x, gamma, beta, kernel1, kernel2, bias1, bias2, norm_type, zero_centered_gamma,
+                             epsilon, activation_type, h1, round_intermediates)
+    finally:
+        T.bf16_round = saved
+
+
 MUTANTS = [
     ("layernorm", _ln_unbiased, [P.test_layernorm_invariants_closed_form_variance, P.test_layernorm_brute_force]),
     ("layernorm", _ln_eps_outside, [P.test_layernorm_brute_force]),
@@ -193,6 +246,12 @@ MUTANTS = [
     ("norm_bwd", _norm_bwd_dgamma_from_x, [lambda: P.test_norm_bwd_central_differences("rmsnorm", True)]),
     ("layernorm_mlp_bwd", _mlp_bwd_dkernel2_from_h,
      [lambda: P.test_mlp_bwd_central_differences("layernorm", ("gelu",))]),
+    ("layernorm_dense_fwd", _dense_fwd_quantizes_x, [P.test_layernorm_dense_fp8_identity_kernel]),
+    ("layernorm_dense_fwd", _dense_fwd_fp8_drops_bias, [P.test_layernorm_dense_fp8_identity_kernel]),
+    ("layernorm_dense_fwd", _dense_fwd_drops_bias,
+     [lambda: P.test_layernorm_dense_identity_kernel("layernorm", False)]),
+    ("layernorm_mlp_bwd", _mlp_bwd_truncating_rounds, [P.test_mlp_bwd_round_intermediates_close_to_exact]),
+    ("layernorm_mlp_bwd", _mlp_bwd_rounds_to_e4m3, [P.test_mlp_bwd_round_intermediates_close_to_exact]),
 ]
 
 

@@ -391,6 +391,60 @@ def test_round_intermediates_is_close_to_exact():
     assert 1e-4 < e < 5e-3
 
 
+def test_bf16_rounding_error_of_normal_data():
+    # the per-rounding budget the backward bounds are built from
+    from tolerances import U_BF16
+    x = RNG.standard_normal(1_000_000)
+    for scale in (1.0, 0.02, 300.0):
+        e = O.rel_l2(O.bf16_round(x * scale), x * scale)
+        assert abs(e - U_BF16) <= 0.02 * U_BF16, (scale, e)
+
+
+# ---- layernorm_dense forward: identity kernels reduce it to the (pinned) norm
+
+@pytest.mark.parametrize("norm_type,zcg", [("layernorm", False), ("rmsnorm", True)])
+def test_layernorm_dense_identity_kernel(norm_type, zcg):
+    h = 16
+    x = RNG.standard_normal((5, h)) * 2.0 + 0.5
+    g = RNG.standard_normal(h) * 0.1 + (0.0 if zcg else 1.0)
+    b = RNG.standard_normal(h) * 0.1
+    bias = RNG.standard_normal(h)
+    xn = O.normalize(x, g, b, norm_type, 1e-5, zcg)[0]
+    out = O.layernorm_dense_fwd(x, np.eye(h), g, b, bias, norm_type=norm_type, zero_centered_gamma=zcg,
+                                epsilon=1e-5)
+    assert np.array_equal(out["y"], xn + bias)
+    assert np.array_equal(out["xn"], xn)
+    r = O.layernorm_dense_fwd(x, np.eye(h), g, b, bias, norm_type=norm_type, zero_centered_gamma=zcg,
+                              epsilon=1e-5, round_intermediates=True)
+    assert np.array_equal(r["y"], O.bf16_round(xn) + bias)
+    assert np.array_equal(O.layernorm_dense_fwd(x, np.eye(h), g, b, None, norm_type=norm_type,
+                                                zero_centered_gamma=zcg, epsilon=1e-5)["y"], xn)
+
+
+def test_layernorm_dense_fp8_identity_kernel():
+    # kernel = I: amax 1, so every diagonal code is 448 and the kernel's
+    # scale_inv is fl32(1/448); y is then the normalised input after one E4M3
+    # rounding at its own scale, plus the bias. Quantising x instead of the
+    # normalised x, or dropping the bias, moves y far outside that.
+    h = 32
+    x = RNG.standard_normal((6, h)) * 3.0 + 1.0
+    g, b = 1.0 + 0.1 * RNG.standard_normal(h), 0.1 * RNG.standard_normal(h)
+    bias = RNG.standard_normal(h)
+    xn = O.layernorm(x, g, b, 1e-6)[0]
+    out = O.layernorm_dense_fwd(x, np.eye(h), g, b, bias, epsilon=1e-6, quant="fp8_e4m3_current")
+    assert out["w_meta"]["amax"] == 1.0 and out["w_meta"]["scale"] == 448.0
+    assert np.array_equal(out["wq"], np.where(np.eye(h) > 0, 0x7E, 0).astype(np.uint8))
+    assert out["x_meta"]["amax"] == float(O.fl32(np.max(np.abs(xn))))
+    # dec(code) * scale_inv: each value within half an E4M3 step (2^-4 relative,
+    # or the subnormal step 2^-10 at the tensor's scale) of the normalised input
+    deq = O.e4m3_decode(out["xq"]) * out["x_meta"]["scale_inv"]
+    assert np.all(np.abs(deq - xn) <= np.maximum(2.0 ** -4 * np.abs(xn), 2.0 ** -10 * out["x_meta"]["scale_inv"])
+                  * (1 + 1e-6))
+    # 448 * fl32(1/448) differs from 1 by about 1e-8: the difference scales with deq alone
+    assert np.all(np.abs(out["y"] - (deq + bias)) <= 1e-7 * np.abs(deq))
+    assert O.rel_l2(out["y"], xn + bias) < 2.0 ** -4
+
+
 def test_rel_l2():
     assert O.rel_l2([3.0, 4.0], [3.0, 4.0]) == 0.0
     assert abs(O.rel_l2([3.0, 5.0], [3.0, 4.0]) - 0.2) < 1e-15
@@ -502,3 +556,51 @@ def test_mlp_bwd_central_differences(norm_type, act):
             assert abs(g[out][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (arg, idx, g[out][idx], fd)
     if norm_type == "rmsnorm":
         assert g["dbeta"] is None
+
+
+def test_mlp_bwd_round_intermediates_close_to_exact():
+    # rounding xn, h1, act, dact, dh1 and dxn to bf16 moves each gradient by
+    # about sqrt(k) one-rounding errors (k = the roundings on its chain): more
+    # than nothing, less than the derived bound
+    from tolerances import bwd_roundings, rounding_bound, U_BF16
+    rows, h, f = 96, 64, 80
+    for norm_type, act in (("layernorm", ("gelu",)), ("rmsnorm", ("silu", "linear"))):
+        gated = len(act) == 2
+        x = RNG.standard_normal((rows, h))
+        gamma = 1.0 + 0.1 * RNG.standard_normal(h)
+        beta = 0.1 * RNG.standard_normal(h) if norm_type == "layernorm" else None
+        w1 = 0.1 * RNG.standard_normal((h, (2 if gated else 1) * f))
+        w2 = 0.1 * RNG.standard_normal((f, h))
+        b1 = 0.05 * RNG.standard_normal(w1.shape[1])
+        gy = RNG.standard_normal((rows, h))
+        kw = dict(norm_type=norm_type, epsilon=1e-6, activation_type=act)
+        ex = O.layernorm_mlp_bwd(gy, x, gamma, beta, w1, w2, b1, None, **kw)
+        rd = O.layernorm_mlp_bwd(gy, x, gamma, beta, w1, w2, b1, None, round_intermediates=True, **kw)
+        for name, ref in ex.items():
+            if ref is None:
+                continue
+            e = O.rel_l2(rd[name], ref)
+            k = bwd_roundings(name, gated, output_rounded=False)
+            if k == 0:
+                assert e == 0.0, name
+            else:
+                assert 0.3 * U_BF16 < e <= rounding_bound(k), (name, act, e, rounding_bound(k))
+
+
+def test_mlp_bwd_round_intermediates_keep_bf16_exact_values():
+    # rows of +-1 with zero mean and unit variance normalise to themselves at
+    # eps = 0; with dyadic kernels, biases and grad every intermediate of the
+    # chain is a short dyadic fraction (exact in bf16), so rounding changes
+    # nothing and both modes agree bit for bit
+    h, f, rows = 8, 12, 6
+    sgn = RNG.permuted(np.tile(np.array([1.0, -1.0] * (h // 2)), (rows, 1)), axis=1)
+    w1 = RNG.choice([0.0, 0.25, -0.25, 0.5, -0.5], (h, f))
+    w2 = RNG.choice([0.0, 0.25, -0.5, 0.5], (f, h))
+    b1 = RNG.choice([0.125, -0.125], f)
+    gy = RNG.choice([1.0, -1.0, 0.5, -0.5], (rows, h))
+    kw = dict(norm_type="layernorm", epsilon=0.0, activation_type=("relu",))
+    assert np.array_equal(O.layernorm(sgn, np.ones(h), np.zeros(h), 0.0)[0], sgn)
+    ex = O.layernorm_mlp_bwd(gy, sgn, np.ones(h), np.zeros(h), w1, w2, b1, None, **kw)
+    rd = O.layernorm_mlp_bwd(gy, sgn, np.ones(h), np.zeros(h), w1, w2, b1, None, round_intermediates=True, **kw)
+    for name in ex:
+        assert np.array_equal(ex[name], rd[name]), name
