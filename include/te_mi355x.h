@@ -169,10 +169,15 @@ size_t te_layernorm_bwd_workspace_size(int64_t rows, int64_t hidden, te_dtype dt
  * x: [rows, G*cols] of x_dtype (F32 or BF16), G = 2 for gated types.
  * y: [rows, cols] of y_dtype (F32, BF16 or E4M3). For E4M3, y holds the codes
  * and y_meta (required) the amax/scale/scale_inv of the whole output; the
- * page's dequantised result is te_dequantize() of it. No workspace. */
+ * page's dequantised result is te_dequantize() of it. Workspace:
+ * te_act_lu_workspace_size() bytes (0 unless y_dtype is E4M3: then it holds
+ * one partial maximum per workgroup of the amax pass; workspace may be NULL
+ * when the size is 0). */
 te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype,
                     te_act_type act_type, void* y, te_dtype y_dtype,
-                    const te_fp8_meta* y_meta, void* stream);
+                    const te_fp8_meta* y_meta, void* workspace, size_t workspace_bytes,
+                    void* stream);
+size_t te_act_lu_workspace_size(int64_t rows, int64_t cols, te_act_type act_type, te_dtype y_dtype);
 
 /* te_dact_dbias - activation backward with the bias-gradient reduction
  * ([ACT] Description: the backward rule computes the activation gradient;
@@ -215,16 +220,18 @@ size_t te_dact_dbias_quantize_workspace_size(int64_t rows, int64_t cols, te_act_
 /* te_layernorm_dense_fwd - normalisation followed by a dense layer ([DENSE]
  * Description; Outputs: LayerNorm(x) @ kernel + bias). With
  * TE_QUANT_FP8_E4M3_CURRENT the normalised input and the kernel are both
- * quantised to E4M3 before the GEMM (fp32 accumulate, bf16 output).
+ * quantised to E4M3 before the GEMM (fp32 accumulate).
  * x: [rows, hidden]; kernel: [hidden, out_features]; gamma, beta: [hidden];
- * bias: optional [out_features]; y: [rows, out_features]; all of `dtype`.
- * Workspace: te_layernorm_dense_fwd_workspace_size(). */
+ * bias: optional [out_features]; all of `dtype`. y: [rows, out_features] of
+ * y_dtype: `dtype`, or TE_F32 for TE_BF16 inputs (the fp32 accumulator plus
+ * bias written without the bf16 rounding); any other y_dtype returns
+ * TE_ERR_UNSUPPORTED. Workspace: te_layernorm_dense_fwd_workspace_size(). */
 te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* gamma,
                                  const void* beta, const void* bias,
                                  int64_t rows, int64_t hidden, int64_t out_features,
                                  te_dtype dtype, te_norm_type norm_type,
                                  int zero_centered_gamma, float epsilon, te_quant quant,
-                                 void* y, void* workspace, size_t workspace_bytes,
+                                 void* y, te_dtype y_dtype, void* workspace, size_t workspace_bytes,
                                  void* stream);
 size_t te_layernorm_dense_fwd_workspace_size(int64_t rows, int64_t hidden,
                                              int64_t out_features, te_dtype dtype,
@@ -235,7 +242,9 @@ size_t te_layernorm_dense_fwd_workspace_size(int64_t rows, int64_t hidden,
  * bias2; Outputs: LayerNorm(x) -> GEMM1 -> Activation -> GEMM2).
  * x: [rows, hidden]; gamma, beta: [hidden] (beta ignored for RMSNorm);
  * kernel1: [hidden, G*ffn]; bias1: optional [G*ffn]; kernel2: [ffn, hidden];
- * bias2: optional [hidden]; y: [rows, hidden]; all of `dtype`.
+ * bias2: optional [hidden]; all of `dtype`. y: [rows, hidden] of y_dtype:
+ * `dtype`, or TE_F32 for TE_BF16 inputs (GEMM2's fp32 accumulator plus bias2
+ * without the bf16 rounding); any other y_dtype returns TE_ERR_UNSUPPORTED.
  * With TE_QUANT_FP8_E4M3_CURRENT (dtype BF16): the normalised input, both
  * kernels and the activation output are quantised per tensor; GEMM1 plus
  * bias1 is rounded to bf16 (h1) and the activation is evaluated from that h1.
@@ -248,7 +257,7 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
                                te_dtype dtype, te_norm_type norm_type,
                                int zero_centered_gamma, float epsilon,
                                te_act_type act_type, te_quant quant,
-                               void* y, const te_mlp_saved* saved,
+                               void* y, te_dtype y_dtype, const te_mlp_saved* saved,
                                void* workspace, size_t workspace_bytes, void* stream);
 size_t te_layernorm_mlp_fwd_workspace_size(int64_t rows, int64_t hidden, int64_t ffn,
                                            te_dtype dtype, te_act_type act_type,

@@ -79,16 +79,17 @@ _SIGS = {
     "te_layernorm_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _int,
                                 _vp, _sz, _vp]),
     "te_layernorm_bwd_workspace_size": (_sz, [_i64, _i64, _int]),
-    "te_act_lu": (_int, [_vp, _i64, _i64, _int, _int, _vp, _int, _meta_p, _vp]),
+    "te_act_lu": (_int, [_vp, _i64, _i64, _int, _int, _vp, _int, _meta_p, _vp, _sz, _vp]),
+    "te_act_lu_workspace_size": (_sz, [_i64, _i64, _int, _int]),
     "te_dact_dbias": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_workspace_size": (_sz, [_i64, _i64, _int]),
     "te_dact_dbias_quantize": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _meta_p, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_quantize_workspace_size": (_sz, [_i64, _i64, _int]),
     "te_layernorm_dense_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f,
-                                      _int, _vp, _vp, _sz, _vp]),
+                                      _int, _vp, _int, _vp, _sz, _vp]),
     "te_layernorm_dense_fwd_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int]),
     "te_layernorm_mlp_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
-                                    _int, _f, _int, _int, _vp, _saved_p, _vp, _sz, _vp]),
+                                    _int, _f, _int, _int, _vp, _int, _saved_p, _vp, _sz, _vp]),
     "te_layernorm_mlp_fwd_workspace_size": (_sz, [_i64, _i64, _i64, _int, _int, _int]),
     "te_layernorm_mlp_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int,
                                     _int, _f, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp, _sz, _vp]),
@@ -210,9 +211,15 @@ def te_layernorm_bwd(dy, x, mu, rsigma, gamma, rows, hidden, dtype, norm_type, z
                                  dparam_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def te_act_lu(x, rows, cols, x_dtype, act_type, y, y_dtype, y_meta=None, stream=None):
+def te_act_lu_workspace_size(rows, cols, act_type, y_dtype) -> int:
+    return _lib.te_act_lu_workspace_size(rows, cols, act_type, y_dtype)
+
+
+def te_act_lu(x, rows, cols, x_dtype, act_type, y, y_dtype, y_meta=None, workspace=None, workspace_bytes=0,
+              stream=None):
     _check(_lib.te_act_lu(_ptr(x), rows, cols, x_dtype, act_type, _ptr(y), y_dtype,
-                          ctypes.byref(y_meta.c()) if y_meta is not None else None, _stream(stream)))
+                          ctypes.byref(y_meta.c()) if y_meta is not None else None, _ptr(workspace),
+                          workspace_bytes, _stream(stream)))
 
 
 def te_dact_dbias_workspace_size(rows, cols, act_type) -> int:
@@ -241,10 +248,10 @@ def te_layernorm_dense_fwd_workspace_size(rows, hidden, out_features, dtype, qua
 
 
 def te_layernorm_dense_fwd(x, kernel, gamma, beta, bias, rows, hidden, out_features, dtype, norm_type,
-                           zero_centered_gamma, epsilon, quant, y, workspace, workspace_bytes, stream=None):
+                           zero_centered_gamma, epsilon, quant, y, y_dtype, workspace, workspace_bytes, stream=None):
     _check(_lib.te_layernorm_dense_fwd(_ptr(x), _ptr(kernel), _ptr(gamma), _ptr(beta), _ptr(bias), rows,
                                        hidden, out_features, dtype, norm_type, int(zero_centered_gamma),
-                                       float(epsilon), quant, _ptr(y), _ptr(workspace), workspace_bytes,
+                                       float(epsilon), quant, _ptr(y), y_dtype, _ptr(workspace), workspace_bytes,
                                        _stream(stream)))
 
 
@@ -263,11 +270,11 @@ def make_saved(h1=None, mu=None, rsigma=None, qset: Optional[QuantizerSet] = Non
 
 
 def te_layernorm_mlp_fwd(x, gamma, beta, kernel1, bias1, kernel2, bias2, rows, hidden, ffn, dtype,
-                         norm_type, zero_centered_gamma, epsilon, act_type, quant, y, saved=None,
+                         norm_type, zero_centered_gamma, epsilon, act_type, quant, y, y_dtype, saved=None,
                          workspace=None, workspace_bytes=0, stream=None):
     _check(_lib.te_layernorm_mlp_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(kernel1), _ptr(bias1),
                                      _ptr(kernel2), _ptr(bias2), rows, hidden, ffn, dtype, norm_type,
-                                     int(zero_centered_gamma), float(epsilon), act_type, quant, _ptr(y),
+                                     int(zero_centered_gamma), float(epsilon), act_type, quant, _ptr(y), y_dtype,
                                      ctypes.byref(saved) if saved is not None else None,
                                      _ptr(workspace), workspace_bytes, _stream(stream)))
 
@@ -378,7 +385,8 @@ def activation(x, activation_type, quantizer: Optional[Fp8Meta] = None, act_para
         te_act_lu(x2, rows, cols, _dtype(x2), act, y, _dtype(y))
         return y.reshape(out_shape)
     codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
-    te_act_lu(x2, rows, cols, _dtype(x2), act, codes, TE_E4M3, quantizer)
+    ws = _workspace(te_act_lu_workspace_size(rows, cols, act, TE_E4M3), x.device)
+    te_act_lu(x2, rows, cols, _dtype(x2), act, codes, TE_E4M3, quantizer, ws, ws.numel())
     y = torch.empty(rows, cols, dtype=x.dtype, device=x.device)
     te_dequantize(codes, rows * cols, quantizer, y, _dtype(y))
     return y.reshape(out_shape)
@@ -391,7 +399,8 @@ def activation_codes(x, activation_type, quantizer: Fp8Meta):
     rows = x2.shape[0]
     cols = x2.shape[1] // (2 if is_gated(act) else 1)
     codes = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
-    te_act_lu(x2, rows, cols, _dtype(x2), act, codes, TE_E4M3, quantizer)
+    ws = _workspace(te_act_lu_workspace_size(rows, cols, act, TE_E4M3), x.device)
+    te_act_lu(x2, rows, cols, _dtype(x2), act, codes, TE_E4M3, quantizer, ws, ws.numel())
     return codes
 
 
@@ -429,10 +438,12 @@ def dact_dbias_quantize(grad, x, activation_type, quantizer: "Fp8Meta", dbias_dt
 def layernorm_dense(x, kernel, gamma, beta, bias=None, norm_type="layernorm", zero_centered_gamma=False,
                     epsilon=1e-6, transpose_batch_sequence=False, layernorm_input_axes=None,
                     dot_input_axes=None, kernel_axes=None, quantizer_set: Optional[QuantizerSet] = None,
-                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None):
     """"... JAX LayerNorm Dense" signature: LayerNorm(x) @ kernel + bias.
     Sharding axes and transpose_batch_sequence do not change the math of a
-    single-device call and are accepted for signature compatibility."""
+    single-device call and are accepted for signature compatibility.
+    ``out_dtype`` (default x's dtype, or out's) may be float32 for bf16 x."""
     x2 = _flat(x)
     rows, hidden = x2.shape
     outf = kernel.shape[1]
@@ -440,9 +451,9 @@ def layernorm_dense(x, kernel, gamma, beta, bias=None, norm_type="layernorm", ze
     quant = TE_QUANT_FP8_E4M3_CURRENT if quantizer_set is not None else TE_QUANT_NONE
     nbytes = te_layernorm_dense_fwd_workspace_size(rows, hidden, outf, dt, quant)
     ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, x.device)
-    y = out if out is not None else torch.empty(rows, outf, dtype=x.dtype, device=x.device)
+    y = out if out is not None else torch.empty(rows, outf, dtype=out_dtype or x.dtype, device=x.device)
     te_layernorm_dense_fwd(x2, kernel, gamma, beta, bias, rows, hidden, outf, dt, _NORM[norm_type],
-                           zero_centered_gamma, epsilon, quant, y, ws, ws.numel())
+                           zero_centered_gamma, epsilon, quant, y, _dtype(y), ws, ws.numel())
     return y.reshape(*x.shape[:-1], outf)
 
 
@@ -452,14 +463,16 @@ def layernorm_mlp(x, gamma, beta, kernels, biases, norm_type, zero_centered_gamm
                   ffn2_ckpt_name="ffn2", activation_type=("relu",),
                   quantizer_set: Optional[QuantizerSet] = None, act_params=None,
                   workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                  save_h1: bool = False, return_saved: bool = False, save_codes: bool = False):
+                  save_h1: bool = False, return_saved: bool = False, save_codes: bool = False,
+                  out_dtype: Optional[torch.dtype] = None):
     """"... JAX LayerNorm MLP" signature: LayerNorm(x) -> GEMM1 + bias1 ->
     activation -> GEMM2 + bias2. ``biases`` may contain None. Sharding axes,
     checkpoint names and transpose_batch_sequence do not change the math of
     a single-device call and are accepted for signature compatibility.
     With ``return_saved`` the result is (y, saved) where saved holds h1 (the
     GEMM1 output plus bias1), mu and rsigma; with ``save_codes`` (fp8) also
-    the E4M3 codes xq, w1q_t, w2q_t and actq."""
+    the E4M3 codes xq, w1q_t, w2q_t and actq. ``out_dtype`` (default x's
+    dtype, or out's) may be float32 for bf16 x."""
     if act_params is not None:
         raise NotImplementedError("act_params (clamped SwiGLU) is not supported")
     act = act_type_of(activation_type)
@@ -473,7 +486,7 @@ def layernorm_mlp(x, gamma, beta, kernels, biases, norm_type, zero_centered_gamm
     quant = TE_QUANT_FP8_E4M3_CURRENT if quantizer_set is not None else TE_QUANT_NONE
     nbytes = te_layernorm_mlp_fwd_workspace_size(rows, hidden, ffn, dt, act, quant)
     ws = workspace if workspace is not None and workspace.numel() >= nbytes else _workspace(nbytes, x.device)
-    y = out if out is not None else torch.empty(rows, hidden, dtype=x.dtype, device=x.device)
+    y = out if out is not None else torch.empty(rows, hidden, dtype=out_dtype or x.dtype, device=x.device)
     saved_t = {}
     if save_h1 or return_saved:
         saved_t["h1"] = torch.empty(rows, g * ffn, dtype=x.dtype, device=x.device)
@@ -491,7 +504,7 @@ def layernorm_mlp(x, gamma, beta, kernels, biases, norm_type, zero_centered_gamm
                            saved_t.get("xq"), saved_t.get("w1q_t"), saved_t.get("w2q_t"),
                            saved_t.get("actq"))
     te_layernorm_mlp_fwd(x2, gamma, beta, k1, b1, k2, b2, rows, hidden, ffn, dt, _NORM[norm_type],
-                         zero_centered_gamma, epsilon, act, quant, y, saved, ws, ws.numel())
+                         zero_centered_gamma, epsilon, act, quant, y, _dtype(y), saved, ws, ws.numel())
     y = y.reshape(*x.shape[:-1], hidden)
     return (y, saved_t) if return_saved else y
 

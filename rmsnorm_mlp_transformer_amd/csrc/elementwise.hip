@@ -634,9 +634,9 @@ int64_t dact_rows_per_chunk(int64_t rows, int64_t cols, bool gated) {
 // The same layout as dact: 512-column strips, W waves over short row chunks
 // read through per-chunk buffer descriptors, U rows per step with all loads
 // in flight before the first use. MODE 0 stores y (OUT bf16 / fp32), 1 the
-// amax of y only (workgroup max + one atomic; the grid is capped and a
-// workgroup loops over chunks), 2 the E4M3 codes of y * scale with the scale
-// from the finished amax.
+// amax of y only (one partial maximum per workgroup into amax[block index];
+// the grid is capped and a workgroup loops over chunks), 2 the E4M3 codes of
+// y * scale with the scale from the finished amax.
 template <bool BF16, int ACT, bool GATED, int MODE, int OUT>
 __global__ void __launch_bounds__(64 * kActWaves) act_kernel(const void* x, int64_t rows, int64_t cols,
                                                               int64_t rows_per_chunk, void* y, float* amax,
@@ -705,8 +705,17 @@ __global__ void __launch_bounds__(64 * kActWaves) act_kernel(const void* x, int6
   }
   if constexpr (MODE == 1) {
     __shared__ float red[W];
-    block_max_atomic(m, amax, red);
+    block_max_store(m, amax + (blockIdx.y * gridDim.x + blockIdx.x), red);
   }
+}
+
+// The capped grid of the amax mode: its workgroup count is the number of
+// partial maxima.
+dim3 act_amax_grid(int64_t rows, int64_t cols, bool gated) {
+  const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
+  const int64_t chunks = (rows + rpc - 1) / rpc;
+  const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
+  return dim3((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, (int64_t)kAmaxBlocks / strips)));
 }
 
 template <bool BF16>
@@ -717,8 +726,8 @@ hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool
   const int64_t chunks = (rows + rpc - 1) / rpc;
   const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
   const dim3 grid((unsigned)strips, (unsigned)chunks);
-  // amax pass: at most kAmaxBlocks workgroups (one atomic each on a single address)
-  const dim3 grid_amax((unsigned)strips, (unsigned)min(chunks, max((int64_t)1, (int64_t)kAmaxBlocks / strips)));
+  // amax pass: at most kAmaxBlocks workgroups (one partial maximum each)
+  const dim3 grid_amax = act_amax_grid(rows, cols, gated);
   constexpr int T = 64 * kActWaves;
 #define TE_ACT_CASE(A, G)                                                                                      \
   if (mode == 1) launch_kernel(act_kernel<BF16, A, G, 1, kF32>, grid_amax, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);   \
@@ -823,6 +832,19 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale
   const unsigned grid = grid_for(n / 8, 4);
   if (y_dtype == kBF16) launch_kernel(dequantize_kernel<true>, grid, kThreads, 0, s, codes, n / 8, scale_inv, y);
   else launch_kernel(dequantize_kernel<false>, grid, kThreads, 0, s, codes, n / 8, scale_inv, y);
+  return hipGetLastError();
+}
+
+int64_t act_amax_blocks(int64_t rows, int64_t cols, bool gated) {
+  if (rows <= 0) return 0;
+  const dim3 g = act_amax_grid(rows, cols, gated);
+  return (int64_t)g.x * g.y;
+}
+
+hipError_t launch_amax_finalize(const float* part, int64_t n, float* amax, float* scale, float* scale_inv,
+                                hipStream_t s) {
+  LaunchScope scope("amax_finalize", s);
+  launch_kernel(amax_finalize_kernel, 1, kFinThreads, 0, s, part, n, amax, scale, scale_inv);
   return hipGetLastError();
 }
 

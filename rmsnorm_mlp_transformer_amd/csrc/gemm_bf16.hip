@@ -50,7 +50,7 @@ struct Stage {
 __device__ __forceinline__ int swz_b(int kr) { return (kr & 3) << 2; }
 
 template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int WAVES, int BK, int STAGES, bool PP,
-          bool AT>
+          bool AT, bool OUT_F32 = false>
 __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   using St = Stage<BK>;
   constexpr int NJ = 16 / WAVES;                      // 32-column blocks per wave
@@ -300,7 +300,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid, 1.0f, stage_ptr);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES, OUT_F32>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
+                                                                             1.0f, stage_ptr);
 }
 
 constexpr int kWaves = TE_GEMM_WAVES;
@@ -367,6 +368,13 @@ hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
   a.ep.group = tile_group(tiles_n, false, e.gated);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
+  if (e.out_f32) {
+    if (e.act != kLinear || e.gated || e.h_out != nullptr || e.amax != nullptr || e.out == nullptr)
+      return hipErrorInvalidValue;
+    launch_kernel(gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, false, true>,
+                  grid, 64 * kWaves, 0, s, a);
+    return hipGetLastError();
+  }
 #define TE_G(A_) return e.gated ? launch_flags<A_, true>(a, grid, s) : launch_flags<A_, false>(a, grid, s)
   switch (e.act) {
     case kRelu: TE_G(kRelu);

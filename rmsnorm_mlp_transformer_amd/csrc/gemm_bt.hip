@@ -58,7 +58,7 @@ __device__ __forceinline__ i32x8_t join16x2(const uint4& lo, const uint4& hi) {
   return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX>
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, bool OUT_F32 = false>
 __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   constexpr int E = 1;                     // bytes per element
   constexpr int KE = kRowBytes / E;        // k values per stage
@@ -215,8 +215,8 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
 
   const float sa = fp8_scale_from_amax(*a.amax_a), sb = fp8_scale_from_amax(*a.amax_b);
   const float scale = (1.0f / sa) * (1.0f / sb);
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, kNJ, 64 * kWaves>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
-                                                                       scale, stage_ptr);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, kNJ, 64 * kWaves, OUT_F32>(acc, bv, a.ep, m0, n0, wm, wn, lane,
+                                                                                tid, scale, stage_ptr);
 }
 
 template <int ACT, bool GATED>
@@ -254,6 +254,12 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
   a.ep.group = tile_group(tiles_n, true, e.gated);
   const unsigned grid = (unsigned)(tiles_m * tiles_n);
+  if (e.out_f32) {
+    if (e.act != kLinear || e.gated || e.h_out != nullptr || e.amax != nullptr || e.out == nullptr)
+      return hipErrorInvalidValue;
+    launch_kernel(gemm_bt_kernel<kLinear, false, true, false, false, true>, grid, 64 * kWaves, 0, s, a);
+    return hipGetLastError();
+  }
 #define TE_G(A_) return e.gated ? launch_flags<A_, true>(a, grid, s) : launch_flags<A_, false>(a, grid, s)
   switch (e.act) {
     case kRelu: TE_G(kRelu);

@@ -44,7 +44,7 @@ constexpr int kTileN = 256;
 
 struct EpiArgs {
   const uint16_t* bias;   // bf16 [n_b] or NULL
-  uint16_t* out;          // bf16 [M, n_out] or NULL
+  uint16_t* out;          // bf16 [M, n_out] or NULL (fp32 [M, n_out] with OUT_F32)
   uint16_t* h_out;        // bf16 [M, n_b] or NULL
   float* amax;            // or NULL
   int M, n_b, F;          // F = n_b / 2 when gated, else n_b
@@ -201,15 +201,45 @@ constexpr float amax_exact_from() {
 }
 
 // h = acc * scale + bias; then the stores / amax selected by the flags. Both
-// stores go through the LDS staging tile (the main loop's LDS is free here).
-// AMAX evaluates the activation from h rounded to bf16, exactly as a later
-// pass reading the stored h would. bv: load_bias_frag() of the same lane.
-template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ, int NT, typename St>
+// bf16 stores go through the LDS staging tile (the main loop's LDS is free
+// here). AMAX evaluates the activation from h rounded to bf16, exactly as a
+// later pass reading the stored h would. bv: load_bias_frag() of the same
+// lane. OUT_F32 (plain, ungated output only) writes the output as fp32 with
+// direct 16-byte stores: a lane's four consecutive columns of one row; the
+// four register groups of a block cover 128 contiguous bytes of each row.
+template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ, int NT, bool OUT_F32 = false,
+          typename St>
 __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const uint2 (&bv)[NJ][4],
                                               const EpiArgs& ep, int m0, int n0, int wm, int wn, int lane,
                                               int tid, float scale, St st) {
   const int lm = lane & 31, lh = lane >> 5;
   const int rows_valid = min(ep.M - m0, kTileM);
+  if constexpr (OUT_F32) {
+    static_assert(STORE_OUT && !STORE_H && !AMAX && !GATED, "fp32 output: plain epilogue only");
+    float* out = reinterpret_cast<float*>(ep.out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + lm;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int tc = b_block_row<false, NJ>(wn, j) + g * 8 + lh * 4;
+          float b[4];
+          unpack_bias4(bv[j][g], b);
+          float4 o;
+          o.x = act_fwd<ACT>(acc[i][j][4 * g + 0] * scale + b[0]);
+          o.y = act_fwd<ACT>(acc[i][j][4 * g + 1] * scale + b[1]);
+          o.z = act_fwd<ACT>(acc[i][j][4 * g + 2] * scale + b[2]);
+          o.w = act_fwd<ACT>(acc[i][j][4 * g + 3] * scale + b[3]);
+          // n_b is a multiple of 16 and tc of 4: the four columns are all in or all out
+          if (r < rows_valid && n0 + tc < ep.n_b)
+            *reinterpret_cast<float4*>(out + (int64_t)(m0 + r) * ep.n_b + n0 + tc) = o;
+        }
+      }
+    }
+    return;
+  }
   float lmax = 0.0f;
   float hmax = -INFINITY, hmin = INFINITY;   // range of the lane's rounded h (plain amax)
   // every wave's LDS reads of the main loop are done before the staging writes

@@ -182,6 +182,14 @@ te_status check_dtype_quant(te_dtype dtype, te_quant quant) {
   return TE_SUCCESS;
 }
 
+// Output dtypes of the forwards: the input dtype, or fp32 from bf16 inputs.
+te_status check_y_dtype(te_dtype dtype, te_dtype y_dtype) {
+  TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype %d", (int)y_dtype);
+  TE_REQUIRE(y_dtype == dtype || (dtype == TE_BF16 && y_dtype == TE_F32), TE_ERR_UNSUPPORTED,
+             "y_dtype must be the input dtype or, for TE_BF16 inputs, TE_F32");
+  return TE_SUCCESS;
+}
+
 te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                      int64_t hidden, te_norm_type nt, float eps) {
   TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows must be in [0, 2^31], got %lld", (long long)rows);
@@ -308,8 +316,16 @@ te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta, i
 }
 
 // ---------------------------------------------------------------- activation
+size_t te_act_lu_workspace_size(int64_t rows, int64_t cols, te_act_type act_type, te_dtype y_dtype) {
+  if (rows <= 0 || cols <= 0 || y_dtype != TE_E4M3) return 0;
+  Carver c(nullptr);
+  c.floats((size_t)te::act_amax_blocks(rows, cols, is_gated(act_type)));
+  return c.off;
+}
+
 te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype, te_act_type act_type,
-                    void* y, te_dtype y_dtype, const te_fp8_meta* y_meta, void* stream) {
+                    void* y, te_dtype y_dtype, const te_fp8_meta* y_meta, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
   TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
   TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
@@ -318,6 +334,10 @@ te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype,
   TE_ARG(((x != nullptr && y != nullptr) || rows == 0) && aligned16(x) && aligned16(y),
          "x and y are required, 16-byte aligned");
   TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
+  const size_t need = te_act_lu_workspace_size(rows, cols, act_type, y_dtype);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
   hipStream_t s = as_stream(stream);
   if (rows == 0) {
     if (y_dtype == TE_E4M3) TE_HIP(te::launch_empty_meta(y_meta->amax, y_meta->scale, y_meta->scale_inv, s), "meta");
@@ -329,9 +349,14 @@ te_status te_act_lu(const void* x, int64_t rows, int64_t cols, te_dtype x_dtype,
     TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 0, y, y_dtype, nullptr, nullptr, nullptr, s), "act");
     return ok();
   }
-  TE_HIP(te::launch_fill_zero(y_meta->amax, 1, s), "fill");
-  TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 1, nullptr, y_dtype, y_meta->amax, nullptr, nullptr, s),
-         "act amax");
+  // current scaling: per-workgroup maxima of |act(x)| into the workspace, their
+  // max (and the scale) into y_meta, then the codes
+  Carver c(workspace);
+  float* part = c.floats((size_t)te::act_amax_blocks(rows, cols, g));
+  TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 1, nullptr, y_dtype, part, nullptr, nullptr, s), "act amax");
+  TE_HIP(te::launch_amax_finalize(part, te::act_amax_blocks(rows, cols, g), y_meta->amax, y_meta->scale,
+                                  y_meta->scale_inv, s),
+         "amax");
   TE_HIP(te::launch_act(x, rows, cols, x_dtype, k, g, 2, y, y_dtype, y_meta->amax, y_meta->scale,
                         y_meta->scale_inv, s),
          "act quantise");
@@ -625,8 +650,11 @@ size_t te_layernorm_dense_fwd_workspace_size(int64_t rows, int64_t hidden, int64
 te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* gamma, const void* beta,
                                  const void* bias, int64_t rows, int64_t hidden, int64_t out_features,
                                  te_dtype dtype, te_norm_type norm_type, int zero_centered_gamma, float epsilon,
-                                 te_quant quant, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+                                 te_quant quant, void* y, te_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   te_status st = check_dtype_quant(dtype, quant);
+  if (st != TE_SUCCESS) return st;
+  st = check_y_dtype(dtype, y_dtype);
   if (st != TE_SUCCESS) return st;
   st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
@@ -645,6 +673,7 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   DenseWs w = dense_ws(c, rows, hidden, out_features, dtype, quant);
   const bool rms = norm_type == TE_RMSNORM, zcg = zero_centered_gamma != 0;
   te::Epilogue ep{bias, y, nullptr, nullptr, te::kLinear, false};
+  ep.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
   if (quant == TE_QUANT_NONE) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn,
                            nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
@@ -683,9 +712,11 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
                                const void* bias1, const void* kernel2, const void* bias2, int64_t rows,
                                int64_t hidden, int64_t ffn, te_dtype dtype, te_norm_type norm_type,
                                int zero_centered_gamma, float epsilon, te_act_type act_type, te_quant quant,
-                               void* y, const te_mlp_saved* saved, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               void* y, te_dtype y_dtype, const te_mlp_saved* saved, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   te_status st = check_dtype_quant(dtype, quant);
+  if (st != TE_SUCCESS) return st;
+  st = check_y_dtype(dtype, y_dtype);
   if (st != TE_SUCCESS) return st;
   st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
@@ -724,6 +755,7 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
                            rsigma, nullptr, nullptr, nullptr, s), "norm");
     te::Epilogue e1{bias1, w.act, h1_user, nullptr, k, gated};
     te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
+    e2.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
     if (dtype == TE_F32) {
       TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.xn), static_cast<const float*>(kernel1), rows, nb1,
                                  hidden, e1, s), "gemm1");
@@ -764,6 +796,7 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
   TE_HIP(te::launch_act(h1, rows, ffn, TE_BF16, k, gated, 2, w.act, TE_E4M3, ma.amax, ma.scale, ma.scale_inv, s),
          "act quantise");
   te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
+  e2.out_f32 = y_dtype == TE_F32;
   TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.act), w.w2t, rows, hidden, ffn, ma.amax, m2.amax, e2, s),
          "fp8 gemm2");
   return ok();

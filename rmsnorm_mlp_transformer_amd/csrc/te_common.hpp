@@ -205,4 +205,18 @@ __device__ __forceinline__ void block_max_atomic(float v, float* amax, float* re
   }
 }
 
+// Workgroup max of v (v >= 0) written to *out by thread 0: one partial per
+// workgroup, reduced by a later launch (no atomics, no zeroed slot needed).
+__device__ __forceinline__ void block_max_store(float v, float* out, float* red) {
+  v = wave_max(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+    for (int i = 1; i < nw; ++i) m = fmaxf(m, red[i]);
+    *out = m;
+  }
+}
+
 }  // namespace te

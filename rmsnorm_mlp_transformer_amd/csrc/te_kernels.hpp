@@ -89,10 +89,15 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale
                              int y_dtype, hipStream_t s);
 
 // Activation forward: x [rows, G*cols] -> y [rows, cols].
-// mode 0: store y (F32/BF16); 1: amax only; 2: E4M3 codes using *amax.
+// mode 0: store y (F32/BF16); 1: amax only, one partial maximum per workgroup
+// into amax[0 .. act_amax_blocks()); 2: E4M3 codes using *amax.
 hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, int act,
                       bool gated, int mode, void* y, int y_dtype, float* amax,
                       float* scale_out, float* scale_inv_out, hipStream_t s);
+int64_t act_amax_blocks(int64_t rows, int64_t cols, bool gated);
+// Max of n partial maxima -> amax; scale = 448 / amax (1 if 0), scale_inv.
+hipError_t launch_amax_finalize(const float* part, int64_t n, float* amax, float* scale, float* scale_inv,
+                                hipStream_t s);
 
 // dact + dbias. partials: fp32 workspace of dact_partials_floats() floats.
 int64_t dact_row_chunks(int64_t rows, int64_t cols, bool gated);
@@ -138,6 +143,7 @@ struct Epilogue {
   int act;                // ActKind
   bool gated;
   const char* name = nullptr;   // timing-scope name (default: from act / gated)
+  bool out_f32 = false;   // out is fp32 (plain ungated epilogue without h_out / amax only)
 };
 
 // bf16: C[M, n_out] from A [M, K] (row-major) and B [K, n_b] (row-major).

@@ -50,13 +50,14 @@ def test_struct_layouts_match_header():
 def _mlp(**kw):
     args = dict(x=P, gamma=P, beta=P, k1=P, b1=None, k2=P, b2=None, rows=8, hidden=64, ffn=128,
                 dtype=B.TE_BF16, norm=B.TE_LAYERNORM, zcg=0, eps=1e-6, act=B.TE_ACT_GELU,
-                quant=B.TE_QUANT_NONE, y=P, saved=None, ws=P, ws_bytes=1 << 30)
+                quant=B.TE_QUANT_NONE, y=P, y_dtype=None, saved=None, ws=P, ws_bytes=1 << 30)
     args.update(kw)
+    y_dtype = args["dtype"] if args["y_dtype"] is None else args["y_dtype"]
     return B._lib.te_layernorm_mlp_fwd(args["x"], args["gamma"], args["beta"], args["k1"], args["b1"],
                                        args["k2"], args["b2"], args["rows"], args["hidden"], args["ffn"],
                                        args["dtype"], args["norm"], args["zcg"], args["eps"], args["act"],
-                                       args["quant"], args["y"], args["saved"], args["ws"], args["ws_bytes"],
-                                       None)
+                                       args["quant"], args["y"], y_dtype, args["saved"], args["ws"],
+                                       args["ws_bytes"], None)
 
 
 @no_gpu
@@ -82,6 +83,9 @@ def _mlp(**kw):
     (dict(dtype=B.TE_E4M3), B.TE_ERR_UNSUPPORTED),
     (dict(ws_bytes=100), B.TE_ERR_WORKSPACE_TOO_SMALL),
     (dict(ws=None), B.TE_ERR_INVALID_ARGUMENT),
+    (dict(y_dtype=7), B.TE_ERR_INVALID_ARGUMENT),
+    (dict(y_dtype=B.TE_E4M3), B.TE_ERR_UNSUPPORTED),
+    (dict(dtype=B.TE_F32, y_dtype=B.TE_BF16), B.TE_ERR_UNSUPPORTED),
 ])
 def test_mlp_validation(kw, status):
     assert _mlp(**kw) == status
@@ -105,23 +109,31 @@ def test_valid_call_without_gpu_maps_to_hip_error():
     st = _mlp()
     assert st == B.TE_ERR_HIP
     assert te.te_last_error() != ""
+    # fp32 output from bf16 inputs is a supported combination (plain and fp8)
+    assert _mlp(y_dtype=B.TE_F32) == B.TE_ERR_HIP
+    assert _mlp(y_dtype=B.TE_F32, quant=B.TE_QUANT_FP8_E4M3_CURRENT) == B.TE_ERR_HIP
 
 
 @no_gpu
 def test_dense_validation():
     def call(**kw):
         a = dict(x=P, k=P, g=P, b=P, bias=None, rows=4, hidden=32, out=48, dtype=B.TE_BF16,
-                 norm=B.TE_LAYERNORM, quant=B.TE_QUANT_NONE, y=P, ws=P, wsb=1 << 30)
+                 norm=B.TE_LAYERNORM, quant=B.TE_QUANT_NONE, y=P, y_dtype=None, ws=P, wsb=1 << 30)
         a.update(kw)
         return B._lib.te_layernorm_dense_fwd(a["x"], a["k"], a["g"], a["b"], a["bias"], a["rows"],
                                              a["hidden"], a["out"], a["dtype"], a["norm"], 0, 1e-5,
-                                             a["quant"], a["y"], a["ws"], a["wsb"], None)
+                                             a["quant"], a["y"], a["dtype"] if a["y_dtype"] is None else a["y_dtype"],
+                                             a["ws"], a["wsb"], None)
     assert call(out=40) == B.TE_ERR_INVALID_ARGUMENT
     assert call(k=None) == B.TE_ERR_INVALID_ARGUMENT
     assert call(b=None) == B.TE_ERR_INVALID_ARGUMENT
     assert call(dtype=B.TE_F32, quant=B.TE_QUANT_FP8_E4M3_CURRENT) == B.TE_ERR_UNSUPPORTED
     assert call(wsb=0) == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert call(y_dtype=B.TE_E4M3) == B.TE_ERR_UNSUPPORTED
+    assert call(dtype=B.TE_F32, y_dtype=B.TE_BF16) == B.TE_ERR_UNSUPPORTED
+    assert call(y_dtype=-1) == B.TE_ERR_INVALID_ARGUMENT
     assert call(rows=0) == B.TE_SUCCESS
+    assert call(rows=0, y_dtype=B.TE_F32) == B.TE_SUCCESS
 
 
 @no_gpu
@@ -139,10 +151,21 @@ def test_norm_act_dact_quant_validation():
     assert lib.te_layernorm_fwd(P, P, None, 0, 64, B.TE_BF16, B.TE_RMSNORM, 0, 1e-6, P, B.TE_BF16,
                                 None, None, None, None, 0, None) == B.TE_SUCCESS
     # act
-    assert lib.te_act_lu(P, 4, 24, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None) == B.TE_ERR_INVALID_ARGUMENT
-    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, 8, P, B.TE_BF16, None, None) == B.TE_ERR_INVALID_ARGUMENT
-    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_E4M3, None, None) == B.TE_ERR_INVALID_ARGUMENT
-    assert lib.te_act_lu(None, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_act_lu(P, 4, 24, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None, 0, None) \
+        == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, 8, P, B.TE_BF16, None, None, 0, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_E4M3, None, P, 1 << 20, None) \
+        == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_act_lu(None, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None, 0, None) \
+        == B.TE_ERR_INVALID_ARGUMENT
+    # E4M3 output needs the partial-maximum workspace; other outputs need none
+    assert lib.te_act_lu_workspace_size(64, 32, B.TE_ACT_GELU, B.TE_BF16) == 0
+    need_a = lib.te_act_lu_workspace_size(64, 32, B.TE_ACT_GELU, B.TE_E4M3)
+    assert need_a >= 4
+    assert lib.te_act_lu(P, 64, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_E4M3, ctypes.byref(m), P, need_a - 1, None) \
+        == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.te_act_lu(P, 64, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_E4M3, ctypes.byref(m), None, need_a, None) \
+        == B.TE_ERR_INVALID_ARGUMENT
     # dact
     need = lib.te_dact_dbias_workspace_size(64, 32, B.TE_ACT_GELU)
     assert need > 0

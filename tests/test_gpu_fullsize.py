@@ -1,8 +1,11 @@
 """GPU parity at the full workload sizes, launched as bench.py launches them
-(same entry points and tensor shapes). The GPU computes every row; the oracle
-computes a sample of rows spread over tiles (first/last rows of 256-row tiles
-and of the whole tensor). Rows are independent once the whole-tensor fp8
-amaxes are known, and those the oracle computes over every row."""
+(same entry points and tensor shapes), against the fp64 oracle on every
+element: rel-L2 over the whole tensor plus the per-element guard of
+gpu_util.check_elementwise, whose error model for the bf16 forwards is k
+bf16 roundings between the inputs and the output (tolerances.rounding_bound).
+
+The fp8 forward and the backward of its activation (dact + dbias on the
+saved GEMM1 pre-activation) share one GPU run and one oracle run."""
 
 import numpy as np
 import pytest
@@ -11,19 +14,15 @@ import torch
 import oracle as O
 import rmsnorm_mlp_transformer_amd as te
 import workloads as W
-from gpu_util import (ACT_CODE_ONE_STEP_MAX, CODE_ONE_STEP_MAX, TOL, assert_rel, check_codes,
-                      check_codes_combined, codes_np, dev, f64, to_dev)
+from gpu_util import TOL, assert_rel, bf16_ulp, check_codes, check_elementwise, check_fp8_forward, codes_np, dev, f64, to_dev
+from tolerances import rounding_bound
 
 pytestmark = pytest.mark.gpu
 
-
-def sample_rows(n):
-    r = [0, 1, 2, 127, 255, 256, 511, 1023, 1024, 2047, 3000, 4095, 4096, 5555, 6143, 8190, 8191]
-    return np.array(sorted({x for x in r if x < n} | {n - 1}))
-
-
-def _f64_rows(t, rows):
-    return f64(t[torch.as_tensor(rows)])
+# dact: the kernel evaluates act' in fp32 (exp2, reciprocal); near a zero of
+# act' the terms cancel and the error is a few fp32 ulps of the largest term,
+# not of the result. 4e-6 of the tensor's rms bounds it for |grad| up to ~25.
+DACT_FP32_REL = 4e-6
 
 
 def test_full_ln_dense_bf16():
@@ -33,12 +32,12 @@ def test_full_ln_dense_bf16():
     g = to_dev(t)
     y = te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g["bias"], epsilon=w.epsilon)
     torch.cuda.synchronize()
-    rows = sample_rows(w.rows)
-    ref = O.layernorm_dense_fwd(_f64_rows(t["x"], rows), f64(t["kernel"]), f64(t["gamma"]), f64(t["beta"]),
-                                f64(t["bias"]), epsilon=w.epsilon)["y"]
-    got = f64(y[torch.as_tensor(rows, device=dev())])
-    assert_rel(got, ref, TOL["bf16"], "y")
-    assert torch.isfinite(y).all()
+    f = {k: f64(v) for k, v in t.items()}
+    ref = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f["beta"], f["bias"], epsilon=w.epsilon)["y"]
+    got = f64(y)
+    e = assert_rel(got, ref, TOL["bf16"], "y")
+    m = check_elementwise(got, ref, rounding_bound(1), "y")     # one rounding: the normalised input
+    print(f"  rel_l2 {e:.3e}, max |err| / rms {m:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["ln_mlp_gelu_bf16", "rms_swiglu_bf16"])
@@ -52,20 +51,27 @@ def test_full_mlp_bf16(name):
                          zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
                          activation_type=w.activation_type)
     torch.cuda.synchronize()
-    rows = sample_rows(w.rows)
-    f = {k: f64(v) for k, v in t.items() if k != "x"}
-    ref = O.layernorm_mlp_fwd(_f64_rows(t["x"], rows), f["gamma"], f.get("beta"), f["kernel1"], f["kernel2"],
-                              f.get("bias1"), f.get("bias2"), norm_type=w.norm_type,
-                              zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
-                              activation_type=w.activation_type)["y"]
-    got = f64(y[torch.as_tensor(rows, device=dev())])
-    assert_rel(got, ref, TOL["bf16"], "y")
-    assert torch.isfinite(y).all()
+    got = f64(y)
+    del y, g
+    f = {k: f64(v) for k, v in t.items()}
+    # row blocks bound the oracle's memory (the SwiGLU h is 8192 x 28672)
+    ref = np.empty_like(got)
+    for r0 in range(0, w.rows, 2048):
+        ref[r0:r0 + 2048] = O.layernorm_mlp_fwd(
+            f["x"][r0:r0 + 2048], f["gamma"], f.get("beta"), f["kernel1"], f["kernel2"], f.get("bias1"),
+            f.get("bias2"), norm_type=w.norm_type, zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
+            activation_type=w.activation_type)["y"]
+    e = assert_rel(got, ref, TOL["bf16"], "y")
+    m = check_elementwise(got, ref, rounding_bound(2), "y")     # the normalised input and the activation output
+    print(f"  rel_l2 {e:.3e}, max |err| / rms {m:.3e}", flush=True)
 
 
-def test_full_mlp_fp8_forward():
+@pytest.fixture(scope="module")
+def fp8_run():
+    """The 8192 x 4096 -> 16384 -> 4096 fp8 forward (codes and h1 saved) and
+    the activation backward on its saved h1, with the oracle of both."""
     w = W.WORKLOADS["ln_mlp_gelu_fp8"]
-    print(f"full {w.name} forward", flush=True)
+    print(f"full {w.name} forward + dact_dbias on the saved h1", flush=True)
     t = W.make_inputs(w)
     g = to_dev(t)
     q = te.QuantizerSet()
@@ -73,70 +79,88 @@ def test_full_mlp_fp8_forward():
                                 [g["bias1"], g["bias2"]], w.norm_type, epsilon=w.epsilon,
                                 activation_type=w.activation_type, quantizer_set=q, return_saved=True,
                                 save_codes=True)
+    dx, db = te.dact_dbias(g["grad"], saved["h1"], w.activation_type, dbias_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = sample_rows(w.rows)
-    rt = torch.as_tensor(rows, device=dev())
-    f = {k: f64(v) for k, v in t.items() if k != "grad"}
+    f = {k: f64(v) for k, v in t.items()}
     o = O.layernorm_mlp_fwd(f["x"], f["gamma"], f["beta"], f["kernel1"], f["kernel2"], f["bias1"], f["bias2"],
-                            epsilon=w.epsilon, activation_type=w.activation_type, quant="fp8_e4m3_current",
-                            rows=rows)
-    for key, meta in (("x_meta", q.x), ("w1_meta", q.w1), ("w2_meta", q.w2), ("act_meta", q.act)):
-        got, ref = meta.values(), o[key]
-        assert abs(got["amax"] - ref["amax"]) <= 1e-5 * ref["amax"], key
-        assert got["scale"] == float(np.float32(448.0) / np.float32(got["amax"])), key
-    w1q = codes_np(saved["w1q_t"]).T
-    w2q = codes_np(saved["w2q_t"]).T
-    assert np.array_equal(w1q, o["w1q"]) and np.array_equal(w2q, o["w2q"])
-    check_codes_combined([("xq", codes_np(saved["xq"]), o["xq"], CODE_ONE_STEP_MAX),
-                          ("w1q", w1q, o["w1q"], CODE_ONE_STEP_MAX),
-                          ("w2q", w2q, o["w2q"], CODE_ONE_STEP_MAX),
-                          ("actq (sampled rows)", codes_np(saved["actq"][rt]), o["actq"], ACT_CODE_ONE_STEP_MAX)])
-    assert_rel(f64(saved["h1"][rt]), o["h1"], TOL["bf16"], "h1")
-    assert_rel(f64(y[rt]), o["y"], TOL["fp8"], "y")
-    assert torch.isfinite(y).all()
+                            epsilon=w.epsilon, activation_type=w.activation_type, quant="fp8_e4m3_current")
+    rdx, rdb = O.dact_dbias(f["grad"], o["h1"], w.activation_type)
+    return dict(w=w, q=q, y=y, saved=saved, dx=dx, db=db, o=o, rdx=rdx, rdb=rdb, grad=f["grad"])
+
+
+def test_full_mlp_fp8_forward(fp8_run):
+    r = fp8_run
+    print("full fp8 forward: every code, h1 and y element", flush=True)
+    check_fp8_forward(r["q"], r["saved"], r["y"], r["o"], r["w"].activation_type, label="ln_mlp_gelu_fp8")
+
+
+def test_full_dact_dbias_on_fp8_saved_h1(fp8_run):
+    """The backward half of the fp8 workload: te_dact_dbias on grad and the
+    forward's own saved bf16 h1 (dx_act and a bf16 dbias1). Where the GPU's h1
+    equals the oracle's, dx is the correctly rounded value (within one bf16
+    step); where h1 is one bf16 step away, dx may move by |grad| x max|gelu''|
+    (0.8) x that step."""
+    r = fp8_run
+    print("full dact_dbias on the fp8 forward's saved h1", flush=True)
+    got, ref = f64(r["dx"]), r["rdx"]
+    e = assert_rel(got, ref, TOL["bf16"], "dx")
+    h_gpu = f64(r["saved"]["h1"])
+    dh = np.abs(h_gpu - r["o"]["h1"])
+    allowance = np.abs(r["grad"]) * 0.8 * dh
+    check_elementwise(got, ref, DACT_FP32_REL, "dx", extra=allowance)
+    # dbias: the fp32 column sums of dx (moved by the same allowance), rounded to bf16
+    gdb = f64(r["db"])
+    eb = assert_rel(gdb, r["rdb"], TOL["bf16"], "dbias")
+    lim = bf16_ulp(r["rdb"]) + allowance.sum(axis=0) + 1e-5 * np.sqrt(np.mean(r["rdb"] ** 2))
+    assert np.all(np.abs(gdb - r["rdb"]) <= lim), "dbias beyond one bf16 step plus the h1 allowance"
+    print(f"  dx rel_l2 {e:.3e}, dbias rel_l2 {eb:.3e}, h1 values differing {np.count_nonzero(dh)}", flush=True)
 
 
 def test_full_dact_dbias():
-    """grad [8192, 16384] ~ N(0, 1) and a pre-activation of GEMM1's spread."""
+    """grad [8192, 16384] ~ N(0, 1) and a pre-activation of GEMM1's spread
+    (N(0, 1.3^2)): dx is the correctly rounded bf16 of the fp32 value (one
+    bf16 step of the oracle), dbias in fp32."""
     w = W.WORKLOADS["ln_mlp_gelu_fp8"]
     print("full dact_dbias 8192x16384 gelu", flush=True)
     a = W.make_act_inputs(w.rows, w.ffn, gated=False, dtype="bf16", seed=0, std=1.3)
     gd, xd = a["grad"].to(dev()), a["x"].to(dev())
     dx, db = te.dact_dbias(gd, xd, ("gelu",))
     torch.cuda.synchronize()
-    rows = sample_rows(w.rows)
     rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), ("gelu",))
-    assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx[rows], TOL["bf16"], "dx")
+    got = f64(dx)
+    assert_rel(got, rdx, TOL["bf16"], "dx")
+    check_elementwise(got, rdx, DACT_FP32_REL, "dx")
     assert_rel(f64(db), rdb, 1e-5, "dbias")
 
 
 def test_full_dact_dbias_swiglu():
     """Gated (silu, linear) at the RMSNorm-SwiGLU shape: grad [8192, 14336],
-    pre-activation [8192, 2 x 14336]."""
+    pre-activation [8192, 2 x 14336]; every element of dx, dbias in fp32."""
     w = W.WORKLOADS["rms_swiglu_bf16"]
     print("full dact_dbias 8192x2x14336 swiglu", flush=True)
     a = W.make_act_inputs(w.rows, w.ffn, gated=True, dtype="bf16", seed=0, std=1.3)
     gd, xd = a["grad"].to(dev()), a["x"].to(dev())
     dx, db = te.dact_dbias(gd, xd, ("silu", "linear"))
     torch.cuda.synchronize()
-    rows = sample_rows(w.rows)
-    rdx, rdb = O.dact_dbias(_f64_rows(a["grad"], rows), _f64_rows(a["x"], rows), ("silu", "linear"))
-    assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx, TOL["bf16"], "dx")
-    # dbias over all rows, in column blocks (the same columns of both halves)
-    # to bound the oracle's memory
+    got, gdb = f64(dx), f64(db)
+    del dx, db
     F = w.ffn
+    # column blocks (the same columns of both halves) bound the oracle's memory
     for c0 in range(0, F, 2048):
         c1 = min(c0 + 2048, F)
         n = c1 - c0
         xab = np.concatenate([f64(a["x"][:, c0:c1]), f64(a["x"][:, F + c0:F + c1])], axis=1)
-        ref = O.dact_dbias(f64(a["grad"][:, c0:c1]), xab, ("silu", "linear"))[1]
-        assert_rel(f64(db[c0:c1]), ref[:n], 1e-5, f"dbias a[{c0}:{c1}]")
-        assert_rel(f64(db[F + c0:F + c1]), ref[n:], 1e-5, f"dbias b[{c0}:{c1}]")
+        rdx, rdb = O.dact_dbias(f64(a["grad"][:, c0:c1]), xab, ("silu", "linear"))
+        gblk = np.concatenate([got[:, c0:c1], got[:, F + c0:F + c1]], axis=1)
+        assert_rel(gblk, rdx, TOL["bf16"], f"dx [{c0}:{c1}]")
+        check_elementwise(gblk, rdx, DACT_FP32_REL, f"dx [{c0}:{c1}]")
+        assert_rel(gdb[c0:c1], rdb[:n], 1e-5, f"dbias a[{c0}:{c1}]")
+        assert_rel(gdb[F + c0:F + c1], rdb[n:], 1e-5, f"dbias b[{c0}:{c1}]")
 
 
 def test_full_dact_dbias_quantize():
-    """quantize_dact_dbias at 8192 x 16384 (GELU): amax over the whole dx, codes
-    of sampled rows, dbias over all rows."""
+    """quantize_dact_dbias at 8192 x 16384 (GELU): amax over the whole dx, every
+    code, dbias over all rows."""
     w = W.WORKLOADS["ln_mlp_gelu_fp8"]
     print("full dact_dbias_quantize 8192x16384 gelu", flush=True)
     a = W.make_act_inputs(w.rows, w.ffn, gated=False, dtype="bf16", seed=0, std=1.3)
@@ -148,14 +172,17 @@ def test_full_dact_dbias_quantize():
     meta = O.current_scaling(rdx)
     m = q.values()
     assert abs(m["amax"] - meta["amax"]) <= 1e-5 * meta["amax"]
-    rows = sample_rows(w.rows)
-    rq, _ = O.quantize(rdx[rows], meta)
-    check_codes(codes_np(codes[torch.as_tensor(rows, device=dev())]), rq, "dx codes (sampled rows)")
+    rq, _ = O.quantize(rdx, meta)
+    n1, n = check_codes(codes_np(codes), rq, "dx codes")
+    print(f"  dx codes one step away: {n1} of {n}", flush=True)
     assert_rel(f64(db), rdb, 1e-5, "dbias")
 
 
 def test_full_norm_bwd_ln_bf16():
-    """LayerNorm backward at 8192 x 4096 bf16 from the forward's saved statistics."""
+    """LayerNorm backward at 8192 x 4096 bf16 from the forward's saved
+    statistics: every element of dx (the correctly rounded bf16 of an fp32
+    value: one bf16 step of the oracle plus the fp32 statistics' error),
+    dgamma and dbeta in fp32."""
     w = W.WORKLOADS["ln_mlp_gelu_bf16"]
     print("full norm_bwd 8192x4096 layernorm bf16", flush=True)
     t = W.make_inputs(w)
@@ -166,7 +193,8 @@ def test_full_norm_bwd_ln_bf16():
     dx, dg, db = te.layernorm_bwd(dy.to(dev()), x, mu, rs, gamma, "layernorm")
     torch.cuda.synchronize()
     rdx, rdg, rdb = O.norm_bwd(f64(dy), f64(t["x"]), f64(t["gamma"]), "layernorm", w.epsilon)
-    rows = sample_rows(w.rows)
-    assert_rel(f64(dx[torch.as_tensor(rows, device=dev())]), rdx[rows], TOL["bf16"], "dx")
+    got = f64(dx)
+    assert_rel(got, rdx, TOL["bf16"], "dx")
+    check_elementwise(got, rdx, 1e-5, "dx")
     assert_rel(f64(dg), rdg, 1e-5, "dgamma")
     assert_rel(f64(db), rdb, 1e-5, "dbeta")

@@ -9,8 +9,9 @@ import torch
 import oracle as O
 import rmsnorm_mlp_transformer_amd as te
 import workloads as W
-from gpu_util import (ACT_CODE_ONE_STEP_MAX, CODE_ONE_STEP_MAX, TOL, assert_rel, check_codes,
-                      check_codes_combined, codes_np, dev, f64, to_dev)
+from gpu_util import (TOL, assert_rel, check_codes, check_elementwise, check_fp8_forward, codes_np, dev, f64,
+                      to_dev)
+from tolerances import rounding_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +36,7 @@ def test_layernorm_dense(rows, hidden, out, dtype):
     ref = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f["beta"], f["bias"], epsilon=1e-5)["y"]
     assert_rel(f64(y), ref, TOL[dtype], "y")
     if dtype == "bf16":
+        check_elementwise(f64(y), ref, rounding_bound(1), "y")
         # against the oracle with the normalised input rounded to bf16 as the GPU stores it
         refr = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f["beta"], f["bias"], epsilon=1e-5,
                                      round_intermediates=True)["y"]
@@ -57,6 +59,9 @@ def test_layernorm_dense_fp8(rows, hidden, out, norm):
     exact = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f.get("beta"), f["bias"], norm_type=norm,
                                   epsilon=1e-5)["y"]
     assert_rel(f64(y), o["y"], TOL["fp8"], "y vs fp8 oracle")
+    # y depends on the codes alone; at most 0.1% of the normalised input's codes
+    # may sit one E4M3 step (2^-3 of the value) away
+    check_elementwise(f64(y), o["y"], 1.5 * np.sqrt(rounding_bound(1) ** 2 + 1e-3 * 2.0 ** -6), "y")
     assert_rel(f64(y), exact, 0.1, "y vs unquantised")
 
 
@@ -102,6 +107,9 @@ def test_mlp_activations(act, dtype, rows):
     o = _mlp_oracle(w, t)
     assert_rel(f64(y), o["y"], TOL[dtype], "y")
     assert_rel(f64(saved["h1"]), o["h"], TOL[dtype], "h1")
+    if dtype == "bf16":
+        check_elementwise(f64(y), o["y"], rounding_bound(2), "y")
+        check_elementwise(f64(saved["h1"]), o["h"], rounding_bound(1), "h1")
 
 
 @pytest.mark.parametrize("name,rows,hidden,ffn", [
@@ -122,6 +130,7 @@ def test_mlp_bf16_workload_recipes(name, rows, hidden, ffn):
     torch.cuda.synchronize()
     o = _mlp_oracle(w, t)
     assert_rel(f64(y), o["y"], TOL["bf16"], "y")
+    check_elementwise(f64(y), o["y"], rounding_bound(2), "y")
     orr = _mlp_oracle(w, t, round_intermediates=True)
     assert_rel(f64(y), orr["y"], 3e-3, "y (bf16 intermediates)")
     assert torch.equal(y, y2), "not bitwise reproducible"
@@ -147,19 +156,7 @@ def test_mlp_fp8(name, rows, hidden, ffn, gated):
     y, saved = _mlp_gpu(w, g, quantizer_set=q, return_saved=True, save_codes=True)
     torch.cuda.synchronize()
     o = _mlp_oracle(w, t, quant="fp8_e4m3_current")
-    for key, meta in (("x_meta", q.x), ("w1_meta", q.w1), ("w2_meta", q.w2), ("act_meta", q.act)):
-        got, ref = meta.values(), o[key]
-        assert abs(got["amax"] - ref["amax"]) <= 1e-5 * ref["amax"], key
-        assert got["scale"] == float(np.float32(448.0) / np.float32(got["amax"])), key
-    # the kernels' codes are computed from exact inputs: bit-exact
-    assert np.array_equal(codes_np(saved["w1q_t"]), o["w1q"].T)
-    assert np.array_equal(codes_np(saved["w2q_t"]), o["w2q"].T)
-    check_codes_combined([("xq", codes_np(saved["xq"]), o["xq"], CODE_ONE_STEP_MAX),
-                          ("w1q", codes_np(saved["w1q_t"]).T, o["w1q"], CODE_ONE_STEP_MAX),
-                          ("w2q", codes_np(saved["w2q_t"]).T, o["w2q"], CODE_ONE_STEP_MAX),
-                          ("actq", codes_np(saved["actq"]), o["actq"], ACT_CODE_ONE_STEP_MAX)])
-    assert_rel(f64(saved["h1"]), o["h1"], TOL["bf16"], "h1")
-    assert_rel(f64(y), o["y"], TOL["fp8"], "y")
+    check_fp8_forward(q, saved, y, o, w.activation_type, w.name)
 
 
 @pytest.mark.parametrize("act", ["gelu", "gelu_erf", "silu", "relu", "linear"])
@@ -198,3 +195,48 @@ def test_mlp_zero_rows():
                          "layernorm", activation_type=("gelu",))
     torch.cuda.synchronize()
     assert y.shape == (0, 64)
+
+
+@pytest.mark.parametrize("quant", ["none", "fp8_e4m3_current"])
+@pytest.mark.parametrize("rows,hidden,out", [(300, 272, 400), (513, 1024, 784)])
+def test_layernorm_dense_f32_output(rows, hidden, out, quant):
+    """y_dtype fp32 from bf16 inputs: the fp32 accumulator plus bias without
+    the final bf16 rounding. Rounding it to bf16 must give the bf16-output
+    call bit for bit (same kernel, same summation order)."""
+    print(f"layernorm_dense {quant} f32 output {rows}x{hidden}->{out}", flush=True)
+    w, t = _dense_case(rows, hidden, out, "bf16", quant, seed=rows + 1)
+    g = to_dev(t)
+    q = (lambda: te.QuantizerSet()) if quant != "none" else (lambda: None)
+    y32 = te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g["bias"], epsilon=1e-5,
+                             quantizer_set=q(), out_dtype=torch.float32)
+    y16 = te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g["bias"], epsilon=1e-5,
+                             quantizer_set=q())
+    torch.cuda.synchronize()
+    assert y32.dtype == torch.float32 and y16.dtype == torch.bfloat16
+    assert torch.equal(y32.to(torch.bfloat16), y16), "fp32 output does not round to the bf16 output"
+    f = {k: f64(v) for k, v in t.items()}
+    if quant == "none":
+        ref = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f["beta"], f["bias"], epsilon=1e-5,
+                                    round_intermediates=True)["y"]
+        # the normalised input is the bf16 A operand; the rest is fp32 accumulation
+        assert_rel(f64(y32), ref, 1e-4, "y (fp32 output)")
+    else:
+        ref = O.layernorm_dense_fwd(f["x"], f["kernel"], f["gamma"], f["beta"], f["bias"], epsilon=1e-5,
+                                    quant=quant)["y"]
+        assert_rel(f64(y32), ref, TOL["fp8"], "y (fp32 output)")
+
+
+@pytest.mark.parametrize("quant", ["none", "fp8_e4m3_current"])
+def test_mlp_f32_output(quant):
+    w = W.WORKLOADS["ln_mlp_gelu_bf16"].scaled(300, 272, 400)
+    print(f"layernorm_mlp {quant} f32 output {w.name}", flush=True)
+    t = W.make_inputs(w)
+    g = to_dev(t)
+    q = (lambda: te.QuantizerSet()) if quant != "none" else (lambda: None)
+    y32 = _mlp_gpu(w, g, quantizer_set=q(), out_dtype=torch.float32)
+    y16 = _mlp_gpu(w, g, quantizer_set=q())
+    torch.cuda.synchronize()
+    assert y32.dtype == torch.float32
+    assert torch.equal(y32.to(torch.bfloat16), y16), "fp32 output does not round to the bf16 output"
+    o = _mlp_oracle(w, t, quant=quant) if quant != "none" else _mlp_oracle(w, t)
+    assert_rel(f64(y32), o["y"], TOL["fp8" if quant != "none" else "bf16"], "y (fp32 output)")
