@@ -83,66 +83,103 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# working sets under twice the 256 MB memory-side cache can still partly hit in it across
+# steps: those rotate input sets
+ROTATE_BELOW = 512 << 20
+ROTATE_SETS = 4
+
+
 class Case:
-    """Inputs on the device plus a closure running one step."""
+    """Inputs on the device plus a closure running one step. When the step's
+    working set (inputs, output and workspace) is under ROTATE_BELOW, the
+    memory-side cache could hold much of it across steps, so ROTATE_SETS independent input sets
+    (seeds 0, 1, ...) are cycled through, one per step."""
 
     def __init__(self, w: W.Workload, te, dev):
         self.w = w
-        t = W.make_inputs(w)
-        self.g = {k: v.to(dev) for k, v in t.items()}
-        g = self.g
+        sets = [{k: v.to(dev) for k, v in W.make_inputs(w).items()}]
+        g0 = sets[0]
         self.qset = te.QuantizerSet(dev) if w.quant != "none" else None
         if w.kind == "dense":
             ws_n = te.te_layernorm_dense_fwd_workspace_size(w.rows, w.hidden, w.ffn, 1,
                                                             1 if self.qset else 0)
-            self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-            self.y = torch.empty(w.rows, w.ffn, dtype=g["x"].dtype, device=dev)
-            self.fn = lambda: te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g.get("bias"),
-                                                 epsilon=w.epsilon, quantizer_set=self.qset,
-                                                 workspace=self.ws, out=self.y)
+            out_shape = (w.rows, w.ffn)
         else:
             act = te.act_type_of(w.activation_type)
             ws_n = te.te_layernorm_mlp_fwd_workspace_size(w.rows, w.hidden, w.ffn,
                                                           0 if w.dtype == "fp32" else 1, act,
                                                           1 if self.qset else 0)
-            self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
-            self.y = torch.empty(w.rows, w.hidden, dtype=g["x"].dtype, device=dev)
-            self.fn = lambda: te.layernorm_mlp(
+            out_shape = (w.rows, w.hidden)
+        self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(*out_shape, dtype=g0["x"].dtype, device=dev)
+        working = sum(v.numel() * v.element_size() for v in g0.values()) + ws_n + \
+            self.y.numel() * self.y.element_size()
+        self.rotated = working < ROTATE_BELOW
+        if self.rotated:
+            sets += [{k: v.to(dev) for k, v in W.make_inputs(w, seed=i).items()} for i in range(1, ROTATE_SETS)]
+        self.working_set = working
+        self.i = 0
+
+        def fn():
+            g = sets[self.i % len(sets)]
+            self.i += 1
+            if w.kind == "dense":
+                return te.layernorm_dense(g["x"], g["kernel"], g["gamma"], g["beta"], g.get("bias"),
+                                          epsilon=w.epsilon, quantizer_set=self.qset, workspace=self.ws, out=self.y)
+            return te.layernorm_mlp(
                 g["x"], g["gamma"], g.get("beta"), [g["kernel1"], g["kernel2"]], [g.get("bias1"), g.get("bias2")],
                 w.norm_type, zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
                 activation_type=w.activation_type, quantizer_set=self.qset, workspace=self.ws, out=self.y)
+        self.fn = fn
 
     def flops(self):
         return self.w.gemm_flops()
 
 
 class DactCase:
-    """dact + dbias on grad [M, F] ~ N(0, 1) and a pre-activation h1 [M, G*F]
-    with the spread of GEMM1's output (N(0, 1.3^2)), both bf16 (G = 2 for a
-    gated activation)."""
+    """dact + dbias on the pre-activation h1 [M, G*F] that the workload's own
+    forward saved (bf16) and grad [M, F]: for the fp8 workload its grad tensor
+    (~N(0, 1), bf16) and the fp8 forward's h1, with dbias written in bf16 as
+    the workload states; for the others grad ~ N(0, 1) drawn after the
+    forward's inputs and dbias in fp32."""
 
     def __init__(self, w: W.Workload, te, dev):
         self.w = w
         g = 2 if w.gated else 1
-        a = W.make_act_inputs(w.rows, w.ffn, gated=w.gated, dtype="bf16", seed=0, std=1.3)
-        self.grad = a["grad"].to(dev)
-        self.h1 = a["x"].to(dev)
+        t = {k: v.to(dev) for k, v in W.make_inputs(w).items()}
+        qset = te.QuantizerSet(dev) if w.quant != "none" else None
+        _, saved = te.layernorm_mlp(t["x"], t["gamma"], t.get("beta"), [t["kernel1"], t["kernel2"]],
+                                    [t.get("bias1"), t.get("bias2")], w.norm_type,
+                                    zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
+                                    activation_type=w.activation_type, quantizer_set=qset, return_saved=True)
+        self.h1 = saved["h1"]
+        del saved
+        if "grad" in t:
+            self.grad = t["grad"]
+        else:
+            gen = torch.Generator(device="cpu").manual_seed(7)
+            self.grad = torch.randn(w.rows, w.ffn, generator=gen).to(torch.bfloat16).to(dev)
+        del t
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         self.dx = torch.empty_like(self.h1)
-        self.dbias = torch.empty(g * w.ffn, dtype=torch.float32, device=dev)
+        dbias_bf16 = w.quant != "none"
+        self.dbias = torch.empty(g * w.ffn, dtype=torch.bfloat16 if dbias_bf16 else torch.float32, device=dev)
         act = te.act_type_of(w.activation_type)
         n = te.te_dact_dbias_workspace_size(w.rows, w.ffn, act)
         self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
         B = te._binding
+        ddt = B.TE_BF16 if dbias_bf16 else B.TE_F32
 
         def fn():
-            B.te_dact_dbias(self.grad, self.h1, w.rows, w.ffn, B.TE_BF16, act, self.dx, self.dbias, B.TE_F32,
+            B.te_dact_dbias(self.grad, self.h1, w.rows, w.ffn, B.TE_BF16, act, self.dx, self.dbias, ddt,
                             self.ws, self.ws.numel())
         self.fn = fn
 
     def bytes(self):
-        # grad + h1 read, dx written (bf16), dbias written (fp32)
+        # grad + h1 read, dx written (bf16), dbias written
         g = 2 if self.w.gated else 1
-        return (1 + 2 * g) * self.w.rows * self.w.ffn * 2 + g * self.w.ffn * 4
+        return (1 + 2 * g) * self.w.rows * self.w.ffn * 2 + g * self.w.ffn * self.dbias.element_size()
 
 
 class DactQuantCase(DactCase):
@@ -172,26 +209,33 @@ class DactQuantCase(DactCase):
 
 class NormBwdCase:
     """LayerNorm backward at the bench workload's normalisation shape: dy, x
-    (bf16) and the forward's saved mu / rsigma -> dx, dgamma, dbeta (fp32)."""
+    (bf16) and the forward's saved mu / rsigma -> dx, dgamma, dbeta (fp32).
+    The working set (dy, x, dx: 192 MB) is under the 256 MB memory-side
+    cache, so ROTATE_SETS input sets (x from seeds 0.., dy from seeds 5..)
+    are cycled through."""
 
     def __init__(self, w: W.Workload, te, dev):
         self.w = w
-        t = W.make_inputs(w)
-        gen = torch.Generator(device="cpu").manual_seed(5)
-        self.dy = torch.randn(w.rows, w.hidden, generator=gen).to(torch.bfloat16).to(dev)
-        self.x, self.gamma = t["x"].to(dev), t["gamma"].to(dev)
-        beta = t["beta"].to(dev)
-        _, self.mu, self.rs = te.layernorm(self.x, self.gamma, beta, "layernorm", False, w.epsilon, return_stats=True)
-        self.dx = torch.empty_like(self.x)
+        B = te._binding
+        sets = []
+        for i in range(ROTATE_SETS):
+            t = W.make_inputs(w, seed=i)
+            gen = torch.Generator(device="cpu").manual_seed(5 + i)
+            dy = torch.randn(w.rows, w.hidden, generator=gen).to(torch.bfloat16).to(dev)
+            x, gamma = t["x"].to(dev), t["gamma"].to(dev)
+            _, mu, rs = te.layernorm(x, gamma, t["beta"].to(dev), "layernorm", False, w.epsilon, return_stats=True)
+            sets.append((dy, x, gamma, mu, rs, torch.empty_like(x)))
         self.dg = torch.empty(w.hidden, dtype=torch.float32, device=dev)
         self.db = torch.empty(w.hidden, dtype=torch.float32, device=dev)
-        B = te._binding
         n = B.te_layernorm_bwd_workspace_size(w.rows, w.hidden, B.TE_BF16)
         self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+        self.i = 0
 
         def fn():
-            B.te_layernorm_bwd(self.dy, self.x, self.mu, self.rs, self.gamma, w.rows, w.hidden, B.TE_BF16,
-                               B.TE_LAYERNORM, 0, self.dx, self.dg, self.db, B.TE_F32, self.ws, self.ws.numel())
+            dy, x, gamma, mu, rs, dx = sets[self.i % len(sets)]
+            self.i += 1
+            B.te_layernorm_bwd(dy, x, mu, rs, gamma, w.rows, w.hidden, B.TE_BF16, B.TE_LAYERNORM, 0, dx, self.dg,
+                               self.db, B.TE_F32, self.ws, self.ws.numel())
         self.fn = fn
 
     def bytes(self):
@@ -340,16 +384,20 @@ def roofline(w, kernels, dtype_key, wname=None):
             "launches": cnt}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        return os.cpu_count()
+
+
 def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
     """Times the fp64 oracle forward on a bounded row sample of workload w:
     blocks of consecutive rows (16, 32, ... up to 1024), taken from the start
     of the input and wrapping round, until about budget_s of CPU work."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        threads = os.cpu_count()
+    threads = _blas_threads()
     t = W.make_inputs(w)
     f = {k: W.to_f64(v) for k, v in t.items()}
     rows = 16
@@ -368,6 +416,32 @@ def cpu_baseline(w: W.Workload, budget_s: float = 15.0):
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle forward of {done_rows} rows in blocks of the {w.rows}-row input "
                       f"({elapsed:.1f} s of CPU work)"}
+
+
+def cpu_baseline_fp8(w: W.Workload, rows: int = 512):
+    """The oracle's fp8 forward (x-hat, both kernels and the activation
+    quantised with current scaling, the E4M3 GEMMs in fp64) on the first
+    `rows` rows of the workload (its scales taken over that sample), then its
+    dact + dbias on those rows' h1 and grad: seconds, TFLOP/s and GB/s at the
+    workload's own work per row."""
+    import oracle as O
+    t = W.make_inputs(w)
+    f = {k: W.to_f64(v) for k, v in t.items()}
+    t0 = time.perf_counter()
+    o = O.layernorm_mlp_fwd(f["x"][:rows], f["gamma"], f["beta"], f["kernel1"], f["kernel2"], f["bias1"], f["bias2"],
+                            epsilon=w.epsilon, activation_type=w.activation_type, quant="fp8_e4m3_current")
+    fwd_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.dact_dbias(f["grad"][:rows], o["h1"], w.activation_type)
+    bwd_s = time.perf_counter() - t0
+    g = 2 if w.gated else 1
+    return {"fwd": {"value": round(w.scaled(rows=rows).gemm_flops() / fwd_s / 1e12, 6), "unit": "TFLOP/s",
+                    "seconds": round(fwd_s, 2)},
+            "dact_dbias": {"value": round((1 + 2 * g) * rows * w.ffn * 2 / bwd_s / 1e9, 3), "unit": "GB/s",
+                           "seconds": round(bwd_s, 3)},
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle fp8 forward of the first {rows} rows (scales over the sample, both kernels "
+                      f"quantised in full), then its dact + dbias on those rows"}
 
 
 def main():
@@ -430,10 +504,29 @@ def main():
                            "frac_of_peak": round(pv / PEAK[pkey], 4),
                            "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in pk.items()},
                            "roofline": roofline(pw, pk, pkey)}
+            if c.rotated:
+                parts[name]["input_sets"] = ROTATE_SETS
+            if pw.quant != "none" and pk:
+                # the same step with the kernels' amax and quantise-transpose
+                # passes taken out (weights quantised once, ahead of the
+                # steps), and the two fp8 GEMMs alone, from the measured
+                # per-kernel durations of the instrumented region
+                per = {k: v[1] / v[0] for k, v in pk.items()}
+                wq_ms = per.get("amax", 0.0) + per.get("quantize_transpose", 0.0)
+                gemm_ms = sum(v for k, v in per.items() if k.startswith("gemm"))
+                parts[name]["prequantised_weights"] = {
+                    "ms_per_step": round(pms - wq_ms, 4),
+                    "TFLOP/s": round(c.flops() / ((pms - wq_ms) / 1e3) / 1e12, 2),
+                    "frac_of_peak": round(c.flops() / ((pms - wq_ms) / 1e3) / 1e12 / PEAK[pkey], 4)}
+                parts[name]["gemm_only"] = {
+                    "ms": round(gemm_ms, 4), "TFLOP/s": round(c.flops() / (gemm_ms / 1e3) / 1e12, 2),
+                    "frac_of_peak": round(c.flops() / (gemm_ms / 1e3) / 1e12 / PEAK[pkey], 4)}
             log(f"bench part {name}: {pms:.4f} ms, {pv:.1f} TFLOP/s")
             del c
             torch.cuda.empty_cache()
-        # activation backward at the GELU workload's shape and (gated) at the SwiGLU one
+        # activation backward: the fp8 workload's backward half (its grad and the
+        # h1 its fp8 forward saved, bf16 dbias) and, gated, at the SwiGLU
+        # workload's shape on the h1 its bf16 forward saved
         for pname, wname in (("dact_dbias_gelu_bf16", "ln_mlp_gelu_fp8"), ("dact_dbias_swiglu_bf16", "rms_swiglu_bf16")):
             dw = W.WORKLOADS[wname]
             d = DactCase(dw, te, dev)
@@ -441,6 +534,7 @@ def main():
             gbs = d.bytes() / (dms / 1e3) / 1e9
             parts[pname] = {"shape": [dw.rows, (2 if dw.gated else 1) * dw.ffn],
                             "activation": list(dw.activation_type),
+                            "h1": f"saved by the {wname} forward", "dbias_dtype": str(d.dbias.dtype)[6:],
                             "ms_per_step": round(dms, 4), "GB/s": round(gbs, 1),
                             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                             "kernels_ms": {k: round(v[1] / v[0], 4) for k, v in dk.items()},
@@ -493,6 +587,9 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
         log(f"bench cpu baseline: {result['cpu_baseline']}")
+        if not args.no_parts:
+            result["cpu_baseline_fp8"] = cpu_baseline_fp8(W.WORKLOADS["ln_mlp_gelu_fp8"])
+            log(f"bench cpu baseline fp8: {result['cpu_baseline_fp8']}")
     print(json.dumps(result), flush=True)
 
 
