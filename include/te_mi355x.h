@@ -198,6 +198,23 @@ te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t c
                         void* workspace, size_t workspace_bytes, void* stream);
 size_t te_dact_dbias_workspace_size(int64_t rows, int64_t cols, te_act_type act_type);
 
+/* te_dact_dbias_noalloc - te_dact_dbias for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, results
+ * and errors as te_dact_dbias without the workspace: the fp32 column partials
+ * of dbias live in a static device buffer of the library,
+ * te_dact_dbias_noalloc_scratch_bytes() (32 MiB) per GPU, held from the first
+ * call on a device until the process ends; shapes whose partials would not
+ * fit return TE_ERR_UNSUPPORTED (no valid shape exceeds it with the shipped
+ * kernel configuration). The call allocates nothing. Every call on one GPU
+ * shares that GPU's buffer: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * The results are bitwise equal to te_dact_dbias's. */
+te_status te_dact_dbias_noalloc(const void* grad, const void* x, int64_t rows, int64_t cols,
+                                te_dtype dtype, te_act_type act_type, void* dx,
+                                void* dbias, te_dtype dbias_dtype, void* stream);
+size_t te_dact_dbias_noalloc_scratch_bytes(void);
+
 /* te_dact_dbias_quantize - the activation backward with the bias reduction
  * and the activation gradient quantised for the fp8 backward GEMMs ([MLP]
  * Description: the fused backward's quantize_dact_dbias step returns the

@@ -83,6 +83,8 @@ _SIGS = {
     "te_act_lu_workspace_size": (_sz, [_i64, _i64, _int, _int]),
     "te_dact_dbias": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_workspace_size": (_sz, [_i64, _i64, _int]),
+    "te_dact_dbias_noalloc": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _vp, _int, _vp]),
+    "te_dact_dbias_noalloc_scratch_bytes": (_sz, []),
     "te_dact_dbias_quantize": (_int, [_vp, _vp, _i64, _i64, _int, _int, _vp, _meta_p, _vp, _int, _vp, _sz, _vp]),
     "te_dact_dbias_quantize_workspace_size": (_sz, [_i64, _i64, _int]),
     "te_layernorm_dense_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _f,
@@ -230,6 +232,11 @@ def te_dact_dbias(grad, x, rows, cols, dtype, act_type, dx, dbias, dbias_dtype, 
                   workspace_bytes, stream=None):
     _check(_lib.te_dact_dbias(_ptr(grad), _ptr(x), rows, cols, dtype, act_type, _ptr(dx), _ptr(dbias),
                               dbias_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def te_dact_dbias_noalloc(grad, x, rows, cols, dtype, act_type, dx, dbias, dbias_dtype, stream=None):
+    _check(_lib.te_dact_dbias_noalloc(_ptr(grad), _ptr(x), rows, cols, dtype, act_type, _ptr(dx), _ptr(dbias),
+                                      dbias_dtype, _stream(stream)))
 
 
 def te_dact_dbias_quantize_workspace_size(rows, cols, act_type) -> int:

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -396,6 +397,73 @@ te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t c
   }
   Carver c(workspace);
   float* partials = dbias != nullptr ? c.floats((size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols) : nullptr;
+  TE_HIP(te::launch_dact_dbias(grad, x, rows, cols, dtype, act_kind(act_type), g, dx, dbias, dbias_dtype,
+                               partials, s),
+         "dact_dbias");
+  return ok();
+}
+
+// ---------------------------------------------------------------- dact + dbias without allocation
+// The fp32 column partials of te_dact_dbias_noalloc live in this static device
+// array (one copy per GPU, held until the process ends). Its device address is
+// looked up once per device with hipGetSymbolAddress; in host code the array's
+// name is only a host-side stand-in and is never passed to a kernel.
+}  // extern "C"
+namespace {
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+te_status scratch_address(float** out) {
+  int dev = -1;
+  TE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  TE_REQUIRE(dev >= 0 && dev < kMaxDevices, TE_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    TE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    TE_REQUIRE(p != nullptr, TE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return TE_SUCCESS;
+}
+}  // namespace
+extern "C" {
+
+size_t te_dact_dbias_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+te_status te_dact_dbias_noalloc(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
+                                te_act_type act_type, void* dx, void* dbias, te_dtype dbias_dtype, void* stream) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
+  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
+  TE_ARG((grad != nullptr && x != nullptr && dx != nullptr) || rows == 0, "grad, x and dx are required");
+  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
+         "pointers must be 16-byte aligned");
+  const bool g = is_gated(act_type);
+  const size_t need = rows > 0 ? (size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols * sizeof(float) : 0;
+  TE_REQUIRE(need <= kNoallocScratchBytes, TE_ERR_UNSUPPORTED,
+             "the bias partials of %lld x %lld need %zu bytes; the static scratch holds %zu", (long long)rows,
+             (long long)cols, need, kNoallocScratchBytes);
+  hipStream_t s = as_stream(stream);
+  if (rows == 0) {   // the bias gradient of an empty batch is zero
+    if (dbias != nullptr) TE_HIP(te::launch_fill_zero_bytes(dbias, (g ? 2 : 1) * cols * (int64_t)esize(dbias_dtype), s), "fill");
+    return ok();
+  }
+  float* partials = nullptr;
+  if (dbias != nullptr) {
+    te_status st = scratch_address(&partials);
+    if (st != TE_SUCCESS) return st;
+  }
+  // every partial the finalize pass reads is written by the dact pass first:
+  // nothing in the scratch has to start at zero
   TE_HIP(te::launch_dact_dbias(grad, x, rows, cols, dtype, act_kind(act_type), g, dx, dbias, dbias_dtype,
                                partials, s),
          "dact_dbias");
