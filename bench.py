@@ -56,14 +56,24 @@ KERNEL_SOURCES = {
     "gemm_bf16_act": _GEMM_NC, "gemm_bf16": _GEMM_NC, "gemm_bf16_gated": _GEMM_NC, "gemm_bf16_wgrad": _GEMM_NC,
     "gemm_bf16_dgrad": _GEMM_NC, "gemm_fp8_h_amax": _GEMM_KC, "gemm_fp8": _GEMM_KC,
     "dact_dbias": ["elementwise.hip", "te_common.hpp"],
+    "dact_quant": ["elementwise.hip", "te_common.hpp"], "dact_dbias_amax": ["elementwise.hip", "te_common.hpp"],
     "norm_bwd": ["norm_bwd.hip", "te_common.hpp"],
 }
 # Counter-measured HBM bytes per launch: {(workload, kernel): (bytes, source hash)}.
-# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summaries are
-# profiles/gemm_bf16_act_ln_mlp_gelu_bf16.md and profiles/dact_dbias_8192x16384_gelu.md.
+# FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summary is
+# profiles/counters_all_kernels_bench.md. The backward's entry is the mean of
+# its two data-gradient GEMMs (dY.kernel2^T and dh1.kernel1^T), one launch each per step.
 TRAFFIC = {
-    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879501139, "86903035431b075e"),
-    ("dact_dbias_gelu_bf16", "dact_dbias"): (822149715, "aca40937c0da79e2"),
+    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879571502, "c28be1a4f8e854ea"),
+    ("ln_dense_bf16", "gemm_bf16"): (704913102, "c28be1a4f8e854ea"),
+    ("rms_swiglu_bf16", "gemm_bf16_gated"): (3155270959, "c28be1a4f8e854ea"),
+    ("ln_mlp_gelu_fp8", "gemm_fp8_h_amax"): (1477733938, "ec0c46db7023bc00"),
+    ("dact_dbias_gelu_bf16", "dact_dbias"): (822159747, "60869412733196b5"),
+    ("dact_dbias_swiglu_bf16", "dact_dbias"): (1207970954, "60869412733196b5"),
+    ("ln_mlp_gelu_bf16_backward", "gemm_bf16_dgrad"): (1759455479, "c28be1a4f8e854ea"),
+    ("norm_bwd_ln_bf16", "norm_bwd"): (210068243, "11bb4c1cbbbfb221"),
+    ("dact_dbias_quantize_gelu_bf16", "dact_quant"): (671158965, "60869412733196b5"),
+    ("dact_dbias_quantize_gelu_bf16", "dact_dbias_amax"): (553991694, "60869412733196b5"),
 }
 
 
