@@ -131,7 +131,10 @@ typedef struct te_mlp_saved {
  * x_dtype. y: [rows, hidden] of y_dtype: F32, BF16 or E4M3. For E4M3 the
  * whole tensor is quantised with current scaling and y_meta (required) gets
  * amax/scale/scale_inv. mu, rsigma: optional [rows] fp32 outputs (mu is not
- * written for RMSNorm). Workspace: te_layernorm_fwd_workspace_size(). */
+ * written for RMSNorm). Workspace: te_layernorm_fwd_workspace_size() bytes,
+ * 16-byte aligned; empty unless y_dtype is E4M3, when it holds one partial
+ * maximum per workgroup of the amax pass (TE_ERR_WORKSPACE_TOO_SMALL if
+ * smaller). */
 te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta,
                            int64_t rows, int64_t hidden, te_dtype x_dtype,
                            te_norm_type norm_type, int zero_centered_gamma, float epsilon,

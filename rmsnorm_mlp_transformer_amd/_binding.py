@@ -202,6 +202,10 @@ def te_layernorm_fwd(x, gamma, beta, rows, hidden, x_dtype, norm_type, zero_cent
                                  _ptr(mu), _ptr(rsigma), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def te_layernorm_fwd_workspace_size(rows, hidden, x_dtype, y_dtype) -> int:
+    return _lib.te_layernorm_fwd_workspace_size(rows, hidden, x_dtype, y_dtype)
+
+
 def te_layernorm_bwd_workspace_size(rows, hidden, dtype) -> int:
     return _lib.te_layernorm_bwd_workspace_size(rows, hidden, dtype)
 
@@ -354,8 +358,10 @@ def layernorm(x, gamma, beta=None, norm_type="layernorm", zero_centered_gamma=Fa
         yd = _dtype(y)
     mu = torch.empty(rows, dtype=torch.float32, device=x.device) if return_stats else None
     rs = torch.empty(rows, dtype=torch.float32, device=x.device) if return_stats else None
+    nbytes = te_layernorm_fwd_workspace_size(rows, hidden, _dtype(x2), yd)
+    ws = _workspace(nbytes, x.device) if nbytes else None
     te_layernorm_fwd(x2, gamma, beta, rows, hidden, _dtype(x2), _NORM[norm_type], zero_centered_gamma,
-                     epsilon, y, yd, quantizer, mu, rs)
+                     epsilon, y, yd, quantizer, mu, rs, ws, nbytes)
     y = y.reshape(x.shape)
     return (y, mu, rs) if return_stats else y
 

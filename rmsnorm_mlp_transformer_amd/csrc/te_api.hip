@@ -135,11 +135,13 @@ struct DenseWs {
   void* xn;        // normalised input (F32/BF16) or codes
   uint8_t* wt;     // fp8: kernel codes, transposed
   float* metas;    // fp8: 6 floats
+  float* npart;    // fp8: the norm amax pass's partial maxima
 };
 DenseWs dense_ws(Carver& c, int64_t rows, int64_t hidden, int64_t out, int dtype, int quant) {
   DenseWs w{};
   if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
     w.metas = c.floats(6);
+    w.npart = c.floats((size_t)te::norm_amax_parts(rows));
     w.xn = c.take((size_t)rows * hidden);
     w.wt = static_cast<uint8_t*>(c.take((size_t)out * hidden));
   } else {
@@ -155,6 +157,7 @@ struct MlpWs {
   uint8_t* w2t;    // fp8: kernel2 codes transposed [hidden, ffn]
   void* h1;        // fp8: GEMM1 output + bias1, bf16 [rows, G*ffn] (when not saved)
   float* metas;    // fp8: 12 floats
+  float* npart;    // fp8: the norm amax pass's partial maxima
 };
 MlpWs mlp_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int dtype, int act, int quant,
              bool need_h1) {
@@ -162,6 +165,7 @@ MlpWs mlp_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int dtype, in
   const int64_t g = is_gated(act) ? 2 : 1;
   if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
     w.metas = c.floats(12);
+    w.npart = c.floats((size_t)te::norm_amax_parts(rows));
     w.xn = c.take((size_t)rows * hidden);
     w.w1t = static_cast<uint8_t*>(c.take((size_t)g * ffn * hidden));
     w.w2t = static_cast<uint8_t*>(c.take((size_t)hidden * ffn));
@@ -278,21 +282,30 @@ void te_timing_reset(void) {
 }
 
 // ---------------------------------------------------------------- norm
-size_t te_layernorm_fwd_workspace_size(int64_t, int64_t, te_dtype, te_dtype) { return 0; }
+size_t te_layernorm_fwd_workspace_size(int64_t rows, int64_t hidden, te_dtype x_dtype, te_dtype y_dtype) {
+  (void)hidden;
+  (void)x_dtype;
+  if (rows <= 0 || y_dtype != TE_E4M3) return 0;
+  Carver c(nullptr);
+  c.floats((size_t)te::norm_amax_parts(rows));
+  return c.off;
+}
 
 te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta, int64_t rows,
                            int64_t hidden, te_dtype x_dtype, te_norm_type norm_type,
                            int zero_centered_gamma, float epsilon, void* y, te_dtype y_dtype,
                            const te_fp8_meta* y_meta, float* mu, float* rsigma, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   te_status st = check_norm(x, gamma, beta, rows, hidden, norm_type, epsilon);
   if (st != TE_SUCCESS) return st;
   TE_ARG(x_dtype == TE_F32 || x_dtype == TE_BF16, "x_dtype must be TE_F32 or TE_BF16");
   TE_ARG(y_dtype == TE_F32 || y_dtype == TE_BF16 || y_dtype == TE_E4M3, "invalid y_dtype");
   TE_ARG((y != nullptr || rows == 0) && aligned16(y), "y is required and must be 16-byte aligned");
   TE_ARG(y_dtype != TE_E4M3 || meta_ok(y_meta), "E4M3 output needs y_meta with amax, scale, scale_inv");
+  const size_t need = te_layernorm_fwd_workspace_size(rows, hidden, x_dtype, y_dtype);
+  TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
+             workspace_bytes, need);
+  TE_ARG(need == 0 || (workspace != nullptr && aligned16(workspace)), "workspace is required (16-byte aligned)");
   hipStream_t s = as_stream(stream);
   if (rows == 0) {
     if (y_dtype == TE_E4M3) TE_HIP(te::launch_empty_meta(y_meta->amax, y_meta->scale, y_meta->scale_inv, s), "meta");
@@ -301,17 +314,18 @@ te_status te_layernorm_fwd(const void* x, const void* gamma, const void* beta, i
   const bool rms = norm_type == TE_RMSNORM;
   if (y_dtype != TE_E4M3) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
-                           te::kNormStore, y_dtype, y, mu, rsigma, nullptr, nullptr, nullptr, s),
+                           te::kNormStore, y_dtype, y, mu, rsigma, nullptr, nullptr, nullptr, nullptr, s),
            "norm");
     return ok();
   }
-  TE_HIP(te::launch_fill_zero(y_meta->amax, 1, s), "fill");
+  Carver c(workspace);
+  float* part = c.floats((size_t)te::norm_amax_parts(rows));
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
-                         te::kNormAmax, y_dtype, nullptr, mu, rsigma, y_meta->amax, nullptr, nullptr, s),
+                         te::kNormAmax, y_dtype, nullptr, mu, rsigma, nullptr, nullptr, nullptr, part, s),
          "norm amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, x_dtype, rms, zero_centered_gamma != 0, epsilon,
                          te::kNormQuant, y_dtype, y, nullptr, nullptr, y_meta->amax, y_meta->scale,
-                         y_meta->scale_inv, s),
+                         y_meta->scale_inv, part, s),
          "norm quantise");
   return ok();
 }
@@ -592,7 +606,7 @@ te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamm
   const te::Epilogue lin{nullptr, nullptr, nullptr, nullptr, te::kLinear, false};
   // the normalised input (GEMM1's A operand) and the activation output, recomputed
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zero_centered_gamma != 0, epsilon, te::kNormStore,
-                         dtype, w.xn, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
+                         dtype, w.xn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
   TE_HIP(te::launch_act(h1, rows, ffn, dtype, k, gated, 0, w.act, dtype, nullptr, nullptr, nullptr, s), "act");
   // GEMM2: dact = grad @ kernel2^T, dkernel2 = act^T @ grad, dbias2 = sum of grad.
   // The data-gradient GEMMs run on the N-contiguous kernel with a transposed
@@ -744,7 +758,7 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   ep.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
   if (quant == TE_QUANT_NONE) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn,
-                           nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
+                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
     if (dtype == TE_F32)
       TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.xn), static_cast<const float*>(kernel), rows,
                                  out_features, hidden, ep, s), "gemm");
@@ -756,10 +770,10 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   float* mw = w.metas + 3;  // ... of the kernel
   TE_HIP(te::launch_fill_zero(w.metas, 6, s), "fill");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr,
-                         nullptr, nullptr, mx, nullptr, nullptr, s), "norm amax");
+                         nullptr, nullptr, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
   TE_HIP(te::launch_amax(kernel, hidden * out_features, dtype, mw, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
-                         nullptr, nullptr, mx, mx + 1, mx + 2, s), "norm quantise");
+                         nullptr, nullptr, mx, mx + 1, mx + 2, w.npart, s), "norm quantise");
   TE_HIP(te::launch_quantize_transpose(kernel, hidden, out_features, dtype, w.wt, mw, mw + 1, mw + 2, s),
          "kernel quantise");
   TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.wt, rows, out_features, hidden, mx, mw, ep, s),
@@ -820,7 +834,7 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
 
   if (quant == TE_QUANT_NONE) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn, mu,
-                           rsigma, nullptr, nullptr, nullptr, s), "norm");
+                           rsigma, nullptr, nullptr, nullptr, nullptr, s), "norm");
     te::Epilogue e1{bias1, w.act, h1_user, nullptr, k, gated};
     te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
     e2.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
@@ -848,13 +862,13 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
     if (saved->actq != nullptr) w.act = saved->actq;
   }
   TE_HIP(te::launch_fill_zero(w.metas, 12, s), "fill");
-  for (const Meta* m : {&mx, &m1, &ma, &m2})
+  for (const Meta* m : {&m1, &ma, &m2})   // (x's amax is written, not accumulated)
     if (m->amax < w.metas || m->amax >= w.metas + 12) TE_HIP(te::launch_fill_zero(m->amax, 1, s), "fill");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr, mu,
-                         rsigma, mx.amax, nullptr, nullptr, s), "norm amax");
+                         rsigma, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
   TE_HIP(te::launch_amax2(kernel1, hidden * nb1, m1.amax, kernel2, ffn * hidden, m2.amax, dtype, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
-                         nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, s), "norm quantise");
+                         nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, w.npart, s), "norm quantise");
   TE_HIP(te::launch_quantize_transpose2(kernel1, hidden, nb1, w.w1t, m1.amax, m1.scale, m1.scale_inv, kernel2, ffn,
                                         hidden, w.w2t, m2.amax, m2.scale, m2.scale_inv, dtype, s),
          "kernel quantise");

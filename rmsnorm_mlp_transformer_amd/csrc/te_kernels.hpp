@@ -46,13 +46,16 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
 // ---------------------------------------------------------------- norm
 enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
 // kNormStore: y (F32/BF16) and optional mu/rsigma.
-// kNormAmax : no y; amax of the normalised tensor into *amax (must start at 0),
-//             optional mu/rsigma.
-// kNormQuant: y = E4M3 codes with scale from *amax; writes scale/scale_inv.
+// kNormAmax : no y; one partial maximum of |normalised value| per workgroup
+//             into part[0, norm_amax_parts(rows)), optional mu/rsigma.
+// kNormQuant: y = E4M3 codes with the scale from the maximum of those
+//             partials; writes *amax, *scale_out and *scale_inv_out.
+// part is required by the two fp8 modes (norm_amax_parts(rows) floats).
 hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                        int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
                        int y_dtype, void* y, float* mu, float* rsigma, float* amax,
-                       float* scale_out, float* scale_inv_out, hipStream_t s);
+                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s);
+int64_t norm_amax_parts(int64_t rows);
 
 // ---------------------------------------------------------------- elementwise
 hipError_t launch_fill_zero(float* p, int n, hipStream_t s);

@@ -150,6 +150,17 @@ def test_norm_act_dact_quant_validation():
                                 None, None, None, None, 0, None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_layernorm_fwd(P, P, None, 0, 64, B.TE_BF16, B.TE_RMSNORM, 0, 1e-6, P, B.TE_BF16,
                                 None, None, None, None, 0, None) == B.TE_SUCCESS
+    # an E4M3 output needs the amax pass's partials: one float per workgroup
+    # (a workgroup takes 4 rows; at most 512 partials)
+    assert lib.te_layernorm_fwd_workspace_size(64, 4096, B.TE_BF16, B.TE_BF16) == 0
+    assert lib.te_layernorm_fwd_workspace_size(0, 4096, B.TE_BF16, B.TE_E4M3) == 0
+    assert lib.te_layernorm_fwd_workspace_size(64, 4096, B.TE_BF16, B.TE_E4M3) == 16 * 4
+    assert lib.te_layernorm_fwd_workspace_size(63, 4096, B.TE_BF16, B.TE_E4M3) == 16 * 4
+    assert lib.te_layernorm_fwd_workspace_size(1 << 20, 4096, B.TE_BF16, B.TE_E4M3) == 512 * 4
+    assert lib.te_layernorm_fwd(P, P, P, 64, 64, B.TE_BF16, B.TE_LAYERNORM, 0, 1e-6, P, B.TE_E4M3,
+                                ctypes.byref(m), None, None, P, 63, None) == B.TE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.te_layernorm_fwd(P, P, P, 64, 64, B.TE_BF16, B.TE_LAYERNORM, 0, 1e-6, P, B.TE_E4M3,
+                                ctypes.byref(m), None, None, None, 64, None) == B.TE_ERR_INVALID_ARGUMENT
     # act
     assert lib.te_act_lu(P, 4, 24, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None, 0, None) \
         == B.TE_ERR_INVALID_ARGUMENT
@@ -232,7 +243,8 @@ def test_workspace_sizes_cover_the_buffers():
                                                      B.TE_QUANT_FP8_E4M3_CURRENT)
     assert gated > fp8
     d = lib.te_layernorm_dense_fwd_workspace_size(4096, 4096, 12288, B.TE_BF16, B.TE_QUANT_FP8_E4M3_CURRENT)
-    assert d >= 4096 * 4096 + 4096 * 12288
+    assert d >= 4096 * 4096 + 4096 * 12288 + 512 * 4
+    assert fp8 >= r * h + 2 * h * f + r * f * 2 + r * f + 512 * 4
     assert lib.te_layernorm_mlp_fwd_workspace_size(100, 64, 128, B.TE_F32, B.TE_ACT_RELU, B.TE_QUANT_NONE) \
         < lib.te_layernorm_mlp_fwd_workspace_size(200, 64, 128, B.TE_F32, B.TE_ACT_RELU, B.TE_QUANT_NONE)
 
