@@ -239,7 +239,7 @@ def _norm_bwd_case(rows, hidden, dtype, norm_type, zcg, seed):
 
 @pytest.mark.parametrize("norm_type", ["layernorm", "rmsnorm"])
 @pytest.mark.parametrize("zcg", [False, True])
-@pytest.mark.parametrize("rows,hidden", [(1, 16), (37, 272), (300, 4096), (2049, 1040), (65, 16384)])
+@pytest.mark.parametrize("rows,hidden", [(1, 16), (37, 272), (300, 4096), (2049, 1040), (33, 8192), (65, 16384)])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_norm_bwd_matches_oracle(norm_type, zcg, rows, hidden, dtype):
     if dtype == "fp32" and hidden > 8192:
