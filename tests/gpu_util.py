@@ -174,7 +174,11 @@ ACT_CODE_DIFF_MAX = 3e-3
 # products it adds, sum_k |a_k b_k|: measured at most 1.9e-6 at K = 4096
 # (GEMM1 at 2048 x 4096 -> 16384, against the exact fp64 sum of the same
 # codes) and about 4.5e-6 at K = 272..512 (values near zero in the small
-# parity shapes); bound about 2x the larger.
+# parity shapes); bound about 2x the larger. Each matrix instruction's error
+# scales with the largest of its 64 products, so this form holds for GEMM1's
+# operands (normalised input and kernel codes, no heavy tail); with the
+# activation's skewed codes as an operand (GEMM2) it reached 2.2e-5 at K = 400
+# (test_fp8_gemm_summation_error measures both forms).
 H1_ACC_REL = 8e-6
 
 

@@ -9,8 +9,8 @@ import torch
 import oracle as O
 import rmsnorm_mlp_transformer_amd as te
 import workloads as W
-from gpu_util import (TOL, assert_rel, check_codes, check_elementwise, check_fp8_forward, codes_np, dev, f64,
-                      to_dev)
+from gpu_util import (H1_ACC_REL, TOL, assert_rel, check_codes, check_elementwise, check_fp8_forward, codes_np,
+                      dev, f64, to_dev)
 from tolerances import rounding_bound
 
 pytestmark = pytest.mark.gpu
@@ -240,3 +240,51 @@ def test_mlp_f32_output(quant):
     assert torch.equal(y32.to(torch.bfloat16), y16), "fp32 output does not round to the bf16 output"
     o = _mlp_oracle(w, t, quant=quant) if quant != "none" else _mlp_oracle(w, t)
     assert_rel(f64(y32), o["y"], TOL["fp8" if quant != "none" else "bf16"], "y (fp32 output)")
+
+
+# Summation error of one fp8 matrix instruction (64 products) relative to the
+# largest of its products, as an upper bound: the per-64-block maxima of |a| and
+# |b| multiplied. Measured at most 6.2e-5 (K = 400) and 1.4e-5 (K = 4096) of
+# the sum over blocks of those bounds; twice the larger.
+FP8_BLOCK_REL = 1.25e-4
+
+
+@pytest.mark.parametrize("rows,hidden,ffn", [(512, 1024, 4096), (300, 272, 400)])
+def test_fp8_gemm_summation_error(rows, hidden, ffn):
+    """The fp8 GEMM's accumulator against the exact sum of its own operand
+    codes. GEMM2 of the fp8 MLP with an fp32 output returns acc * s + bias2,
+    s = fl32(scale_inv(act) * scale_inv(kernel2)); the saved act and kernel2
+    codes give the exact sum in fp64 (E4M3 products span fewer than 53 bits).
+    The difference is the summation error of the fp8 matrix instruction. Each
+    instruction's error scales with the largest of its 64 products (the test
+    holds the error to FP8_BLOCK_REL of the sum over k blocks of max|a| max|b|
+    in the block); over a long K it is also within H1_ACC_REL of
+    sum_k |a_k b_k|, the form the h1 rule of the fp8 parity checks uses."""
+    w = W.WORKLOADS["ln_mlp_gelu_bf16"].scaled(rows, hidden, ffn)
+    print(f"fp8 GEMM summation error {rows}x{hidden}x{ffn}", flush=True)
+    t = W.make_inputs(w, seed=5)
+    q = te.QuantizerSet()
+    y, s = _mlp_gpu(w, to_dev(t), quantizer_set=q, out_dtype=torch.float32, return_saved=True, save_codes=True)
+    torch.cuda.synchronize()
+    a = O.e4m3_decode(codes_np(s["actq"]))
+    b = O.e4m3_decode(codes_np(s["w2q_t"]))
+    sc = float(np.float32(q.act.values()["scale_inv"]) * np.float32(q.w2.values()["scale_inv"]))
+    exact = (a @ b.T) * sc + f64(t["bias2"])[None, :]
+    yv = f64(y)
+    # the epilogue's own roundings (acc * s and + bias2 in fp32), at most one ulp of y each
+    ulp = np.spacing(np.abs(yv).astype(np.float32)).astype(np.float64)
+    excess = np.maximum(np.abs(yv - exact) - 2 * ulp, 0)
+    nb = (ffn + 63) // 64
+    ma = np.stack([np.abs(a[:, 64 * j:64 * j + 64]).max(1) for j in range(nb)], 1)
+    mb = np.stack([np.abs(b[:, 64 * j:64 * j + 64]).max(1) for j in range(nb)], 1)
+    blk = (ma @ mb.T) * sc
+    mag = (np.abs(a) @ np.abs(b).T) * sc
+    r_blk = (excess / np.where(blk > 0, blk, 1)).max()
+    r_mag = (excess / np.where(mag > 0, mag, 1)).max()
+    print(f"  K = {ffn}: max error / sum of block max products {r_blk:.3g} (bound {FP8_BLOCK_REL:g}); "
+          f"/ sum|a b| {r_mag:.3g}", flush=True)
+    assert r_blk <= FP8_BLOCK_REL, f"fp8 GEMM summation error {r_blk:.3g} of the block bound"
+    if ffn >= 4096:
+        assert r_mag <= H1_ACC_REL, f"fp8 GEMM summation error {r_mag:.3g} of sum|a b| beyond {H1_ACC_REL:g}"
+    # an error of the sum, not of the operands: a wrong code or element would be far larger
+    assert np.abs(yv - exact).max() < 1e-3 * np.abs(exact).max()
