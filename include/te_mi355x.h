@@ -77,7 +77,8 @@ typedef enum te_act_type {
   TE_ACT_LINEAR = 4,
   TE_ACT_REGLU = 5,  /* ("relu", "linear") */
   TE_ACT_GEGLU = 6,  /* ("gelu", "linear") */
-  TE_ACT_SWIGLU = 7  /* ("silu", "linear") */
+  TE_ACT_SWIGLU = 7,  /* ("silu", "linear") */
+  TE_ACT_GEGLU_ERF = 8  /* ("gelu_erf", "linear") */
 } te_act_type;
 
 /* [MLP]/[DENSE] Inputs: quantizer_set. NONE is the no-op quantizer set. */

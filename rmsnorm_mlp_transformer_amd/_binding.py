@@ -35,7 +35,7 @@ TE_SUCCESS, TE_ERR_INVALID_ARGUMENT, TE_ERR_UNSUPPORTED, TE_ERR_WORKSPACE_TOO_SM
 TE_F32, TE_BF16, TE_E4M3 = 0, 1, 2
 TE_LAYERNORM, TE_RMSNORM = 0, 1
 (TE_ACT_RELU, TE_ACT_GELU, TE_ACT_GELU_ERF, TE_ACT_SILU, TE_ACT_LINEAR,
- TE_ACT_REGLU, TE_ACT_GEGLU, TE_ACT_SWIGLU) = range(8)
+ TE_ACT_REGLU, TE_ACT_GEGLU, TE_ACT_SWIGLU, TE_ACT_GEGLU_ERF) = range(9)
 TE_QUANT_NONE, TE_QUANT_FP8_E4M3_CURRENT = 0, 1
 
 _NORM = {"layernorm": TE_LAYERNORM, "rmsnorm": TE_RMSNORM}
@@ -43,7 +43,7 @@ _ACT = {
     ("relu",): TE_ACT_RELU, ("gelu",): TE_ACT_GELU, ("gelu_erf",): TE_ACT_GELU_ERF,
     ("silu",): TE_ACT_SILU, ("linear",): TE_ACT_LINEAR,
     ("relu", "linear"): TE_ACT_REGLU, ("gelu", "linear"): TE_ACT_GEGLU,
-    ("silu", "linear"): TE_ACT_SWIGLU,
+    ("silu", "linear"): TE_ACT_SWIGLU, ("gelu_erf", "linear"): TE_ACT_GEGLU_ERF,
 }
 _DTYPE = {torch.float32: TE_F32, torch.bfloat16: TE_BF16, torch.uint8: TE_E4M3,
           torch.float8_e4m3fn: TE_E4M3}

@@ -56,13 +56,13 @@ bool feature_ok(int64_t n) { return n > 0 && n % 16 == 0 && n <= (int64_t)1 << 2
 // The GEMMs address a weight matrix through one buffer descriptor with 32-bit
 // byte offsets: it must stay below 2 GiB.
 bool weight_ok(int64_t rows, int64_t cols, int dtype) { return rows * cols * (int64_t)esize(dtype) < ((int64_t)1 << 31); }
-bool valid_act(int a) { return a >= TE_ACT_RELU && a <= TE_ACT_SWIGLU; }
+bool valid_act(int a) { return a >= TE_ACT_RELU && a <= TE_ACT_GEGLU_ERF; }
 bool is_gated(int a) { return a >= TE_ACT_REGLU; }
 int act_kind(int a) {
   switch (a) {
     case TE_ACT_RELU: case TE_ACT_REGLU: return te::kRelu;
     case TE_ACT_GELU: case TE_ACT_GEGLU: return te::kGelu;
-    case TE_ACT_GELU_ERF: return te::kGeluErf;
+    case TE_ACT_GELU_ERF: case TE_ACT_GEGLU_ERF: return te::kGeluErf;
     case TE_ACT_SILU: case TE_ACT_SWIGLU: return te::kSilu;
     default: return te::kLinear;
   }

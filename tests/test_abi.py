@@ -164,7 +164,7 @@ def test_norm_act_dact_quant_validation():
     # act
     assert lib.te_act_lu(P, 4, 24, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None, 0, None) \
         == B.TE_ERR_INVALID_ARGUMENT
-    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, 8, P, B.TE_BF16, None, None, 0, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_act_lu(P, 4, 32, B.TE_BF16, 9, P, B.TE_BF16, None, None, 0, None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_act_lu(P, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_E4M3, None, P, 1 << 20, None) \
         == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_act_lu(None, 4, 32, B.TE_BF16, B.TE_ACT_GELU, P, B.TE_BF16, None, None, 0, None) \
@@ -260,6 +260,8 @@ def test_timing_api_without_launches():
 
 def test_act_type_names():
     assert te.act_type_of(("silu", "linear")) == B.TE_ACT_SWIGLU
+    assert te.act_type_of(("gelu_erf", "linear")) == B.TE_ACT_GEGLU_ERF
+    assert B.is_gated(B.TE_ACT_GEGLU_ERF) and not B.is_gated(B.TE_ACT_GELU_ERF)
     assert te.act_type_of("gelu") == B.TE_ACT_GELU
     with pytest.raises(ValueError):
         te.act_type_of(("tanh",))

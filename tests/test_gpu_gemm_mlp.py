@@ -66,7 +66,7 @@ def test_layernorm_dense_fp8(rows, hidden, out, norm):
 
 
 MLP_ACTS = [("gelu",), ("relu",), ("silu",), ("gelu_erf",), ("linear",),
-            ("silu", "linear"), ("gelu", "linear"), ("relu", "linear")]
+            ("silu", "linear"), ("gelu", "linear"), ("relu", "linear"), ("gelu_erf", "linear")]
 
 
 def _mlp_oracle(w, t, **kw):

@@ -124,7 +124,7 @@ def test_quantize_all_zero_tensor():
 
 
 ACTS = [("relu",), ("gelu",), ("gelu_erf",), ("silu",), ("linear",),
-        ("relu", "linear"), ("gelu", "linear"), ("silu", "linear")]
+        ("relu", "linear"), ("gelu", "linear"), ("silu", "linear"), ("gelu_erf", "linear")]
 
 
 @pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])

@@ -77,7 +77,7 @@ def test_mlp_bwd_workload_recipes(name, rows, hidden, ffn):
 
 
 @pytest.mark.parametrize("act", [("relu",), ("silu",), ("gelu_erf",), ("linear",), ("gelu", "linear"),
-                                 ("relu", "linear")], ids=lambda a: "-".join(a))
+                                 ("relu", "linear"), ("gelu_erf", "linear")], ids=lambda a: "-".join(a))
 def test_mlp_bwd_activations(act):
     w = W.Workload("mlpb", "mlp", 384, 272, 528, "bf16", "none", "layernorm", False, 1e-6, act, True)
     print(f"layernorm_mlp_bwd {act} 384x272x528", flush=True)
