@@ -208,6 +208,21 @@ te_status check_norm(const void* x, const void* gamma, const void* beta, int64_t
   return TE_SUCCESS;
 }
 
+// Arguments shared by the dact + dbias entry points; dx is the output (dx, or
+// the codes of the quantising variant), named dx_name in the messages.
+te_status check_dact(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype, te_act_type act_type,
+                     const void* dx, const char* dx_name, const void* dbias, te_dtype dbias_dtype) {
+  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
+  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
+  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
+  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
+  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
+  TE_ARG((grad != nullptr && x != nullptr && dx != nullptr) || rows == 0, "grad, x and %s are required", dx_name);
+  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
+         "pointers must be 16-byte aligned");
+  return TE_SUCCESS;
+}
+
 }  // namespace
 
 namespace te {
@@ -389,14 +404,8 @@ size_t te_dact_dbias_workspace_size(int64_t rows, int64_t cols, te_act_type act_
 te_status te_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
                         te_act_type act_type, void* dx, void* dbias, te_dtype dbias_dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
-  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
-  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
-  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
-  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
-  TE_ARG((grad != nullptr && x != nullptr && dx != nullptr) || rows == 0, "grad, x and dx are required");
-  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
-         "pointers must be 16-byte aligned");
+  te_status st = check_dact(grad, x, rows, cols, dtype, act_type, dx, "dx", dbias, dbias_dtype);
+  if (st != TE_SUCCESS) return st;
   const size_t need = te_dact_dbias_workspace_size(rows, cols, act_type);
   if (dbias != nullptr) {
     TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL,
@@ -453,14 +462,8 @@ size_t te_dact_dbias_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; 
 
 te_status te_dact_dbias_noalloc(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
                                 te_act_type act_type, void* dx, void* dbias, te_dtype dbias_dtype, void* stream) {
-  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
-  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
-  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
-  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
-  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
-  TE_ARG((grad != nullptr && x != nullptr && dx != nullptr) || rows == 0, "grad, x and dx are required");
-  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx) && (dbias == nullptr || aligned16(dbias)),
-         "pointers must be 16-byte aligned");
+  te_status st = check_dact(grad, x, rows, cols, dtype, act_type, dx, "dx", dbias, dbias_dtype);
+  if (st != TE_SUCCESS) return st;
   const bool g = is_gated(act_type);
   const size_t need = rows > 0 ? (size_t)te::dact_row_chunks(rows, cols, g) * (g ? 2 : 1) * cols * sizeof(float) : 0;
   TE_REQUIRE(need <= kNoallocScratchBytes, TE_ERR_UNSUPPORTED,
@@ -496,15 +499,9 @@ size_t te_dact_dbias_quantize_workspace_size(int64_t rows, int64_t cols, te_act_
 te_status te_dact_dbias_quantize(const void* grad, const void* x, int64_t rows, int64_t cols, te_dtype dtype,
                                  te_act_type act_type, uint8_t* dx_codes, const te_fp8_meta* dx_meta, void* dbias,
                                  te_dtype dbias_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  TE_ARG(rows >= 0 && rows <= (int64_t)1 << 31, "rows out of range");
-  TE_ARG(feature_ok(cols), "cols must be a positive multiple of 16, got %lld", (long long)cols);
-  TE_ARG(valid_act(act_type), "invalid act_type %d", (int)act_type);
-  TE_ARG(dtype == TE_F32 || dtype == TE_BF16, "dtype must be TE_F32 or TE_BF16");
-  TE_ARG(dbias == nullptr || dbias_dtype == TE_F32 || dbias_dtype == TE_BF16, "dbias_dtype must be TE_F32 or TE_BF16");
+  te_status st = check_dact(grad, x, rows, cols, dtype, act_type, dx_codes, "dx_codes", dbias, dbias_dtype);
+  if (st != TE_SUCCESS) return st;
   TE_ARG(meta_ok(dx_meta), "dx_meta with amax, scale and scale_inv is required");
-  TE_ARG((grad != nullptr && x != nullptr && dx_codes != nullptr) || rows == 0, "grad, x and dx_codes are required");
-  TE_ARG(aligned16(grad) && aligned16(x) && aligned16(dx_codes) && (dbias == nullptr || aligned16(dbias)),
-         "pointers must be 16-byte aligned");
   const size_t need = te_dact_dbias_quantize_workspace_size(rows, cols, act_type);
   TE_REQUIRE(workspace_bytes >= need, TE_ERR_WORKSPACE_TOO_SMALL, "workspace too small: %zu < %zu bytes",
              workspace_bytes, need);
