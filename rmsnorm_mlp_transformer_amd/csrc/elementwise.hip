@@ -11,6 +11,7 @@
 // backward gives the activation gradient with the bias reduction);
 // "... LayerNorm Dense" (Description: the normalised input and the kernel
 // are quantised before the GEMM).
+#include "gemm_lds.hpp"
 #include "te_common.hpp"
 #include "te_kernels.hpp"
 
@@ -244,6 +245,7 @@ struct QtJob {
   const float* amax;
   float* scale_out;        // nullable
   float* scale_inv_out;
+  int64_t nks, split;      // nks > 0: codes_t in the tiled GEMM operand layout (k stages, split row)
 };
 
 // Workgroups [0, tiles0) take the tiles of job 0, the rest those of job 1.
@@ -309,7 +311,8 @@ __global__ void __launch_bounds__(kThreads) quantize_transpose_kernel(QtJob j0, 
     const int oc = idx >> 3, orr = (idx & 7) * 16;
     if (c0 + oc < cols && r0 + orr < rows) {
       const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + oc * kQtPitch + orr);
-      *reinterpret_cast<uint4*>(codes_t + (c0 + oc) * rows + r0 + orr) = make_uint4(src[0], src[1], src[2], src[3]);
+      const int64_t off = job.nks > 0 ? tiled_offset(c0 + oc, r0 + orr, job.nks, job.split) : (c0 + oc) * rows + r0 + orr;
+      *reinterpret_cast<uint4*>(codes_t + off) = make_uint4(src[0], src[1], src[2], src[3]);
     }
   }
 }
@@ -645,7 +648,8 @@ int64_t dact_rows_per_chunk(int64_t rows, int64_t cols, bool gated) {
 template <bool BF16, int ACT, bool GATED, int MODE, int OUT>
 __global__ void __launch_bounds__(64 * kActWaves) act_kernel(const void* x, int64_t rows, int64_t cols,
                                                               int64_t rows_per_chunk, void* y, float* amax,
-                                                              float* scale_out, float* scale_inv_out) {
+                                                              float* scale_out, float* scale_inv_out,
+                                                              int64_t y_nks) {
   constexpr int G = GATED ? 2 : 1;
   constexpr int W = kActWaves, U = kActUnroll;
   constexpr int64_t ES = BF16 ? 2 : 4;
@@ -701,6 +705,13 @@ __global__ void __launch_bounds__(64 * kActWaves) act_kernel(const void* x, int6
           } else if constexpr (MODE == 1) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(o[i]));
+          } else if (y_nks > 0) {
+            // tiled codes (the next GEMM's A): 8 codes, half of one 16-byte slot; rows past
+            // the chunk (read as zero) belong to the next chunk and are not written
+            const int64_t rc = r0 + (int64_t)u * W + w;
+            if (rc < nr)
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(y) + tiled_offset(r_begin + rc, col, y_nks, 0)) =
+                  encode8(o, qscale);
           } else {
             store8_codes_buf(ry, vy, so, encode8(o, qscale));
           }
@@ -725,8 +736,10 @@ dim3 act_amax_grid(int64_t rows, int64_t cols, bool gated) {
 
 template <bool BF16>
 hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool gated, int mode,
-                        void* y, int y_dtype, float* amax, float* so, float* sio, hipStream_t s) {
+                        void* y, int y_dtype, float* amax, float* so, float* sio, hipStream_t s, bool y_tiled) {
   if (rows <= 0) return hipSuccess;
+  if (y_tiled && (mode != 2 || cols > kTiledMaxRowBytes)) return hipErrorInvalidValue;
+  const int64_t nks = y_tiled ? tiled_stages(cols) : 0;   // E4M3 codes: one byte per column
   const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
   const int64_t chunks = (rows + rpc - 1) / rpc;
   const int64_t strips = (cols + kDactStrip - 1) / kDactStrip;
@@ -735,10 +748,10 @@ hipError_t act_dispatch(const void* x, int64_t rows, int64_t cols, int act, bool
   const dim3 grid_amax = act_amax_grid(rows, cols, gated);
   constexpr int T = 64 * kActWaves;
 #define TE_ACT_CASE(A, G)                                                                                      \
-  if (mode == 1) launch_kernel(act_kernel<BF16, A, G, 1, kF32>, grid_amax, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);   \
-  else if (mode == 2) launch_kernel(act_kernel<BF16, A, G, 2, kE4M3>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio); \
-  else if (y_dtype == kBF16) launch_kernel(act_kernel<BF16, A, G, 0, kBF16>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio); \
-  else launch_kernel(act_kernel<BF16, A, G, 0, kF32>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio);
+  if (mode == 1) launch_kernel(act_kernel<BF16, A, G, 1, kF32>, grid_amax, T, 0, s, x, rows, cols, rpc, y, amax, so, sio, nks);   \
+  else if (mode == 2) launch_kernel(act_kernel<BF16, A, G, 2, kE4M3>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio, nks); \
+  else if (y_dtype == kBF16) launch_kernel(act_kernel<BF16, A, G, 0, kBF16>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio, nks); \
+  else launch_kernel(act_kernel<BF16, A, G, 0, kF32>, grid, T, 0, s, x, rows, cols, rpc, y, amax, so, sio, nks);
 #define TE_ACT_G(A) if (gated) { TE_ACT_CASE(A, true) } else { TE_ACT_CASE(A, false) }
   switch (act) {
     case kRelu: TE_ACT_G(kRelu) break;
@@ -802,22 +815,27 @@ hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes
 
 hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
                                      uint8_t* codes_t, const float* amax, float* scale_out,
-                                     float* scale_inv_out, hipStream_t s) {
+                                     float* scale_inv_out, hipStream_t s, bool tiled) {
   return launch_quantize_transpose2(x, rows, cols, codes_t, amax, scale_out, scale_inv_out, nullptr, 0, 0, nullptr,
-                                    nullptr, nullptr, nullptr, x_dtype, s);
+                                    nullptr, nullptr, nullptr, x_dtype, s, tiled, false, 0);
 }
 
 hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes_t0,
                                       const float* amax0, float* scale0, float* scale_inv0, const void* x1,
                                       int64_t rows1, int64_t cols1, uint8_t* codes_t1, const float* amax1,
-                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s) {
+                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s, bool tiled0,
+                                      bool tiled1, int64_t split0) {
   LaunchScope scope("quantize_transpose", s);
+  // codes_t rows are K = rows of x long
+  if ((tiled0 && rows0 > kTiledMaxRowBytes) || (tiled1 && rows1 > kTiledMaxRowBytes) ||
+      (split0 > 0 && (!tiled0 || 2 * split0 != cols0)))
+    return hipErrorInvalidValue;
   auto tiles = [](int64_t r, int64_t c) {   // < 2^17 for weights < 2 GiB
     return (unsigned)(((c + kQtCols - 1) / kQtCols) * ((r + kQtRows - 1) / kQtRows));
   };
   const unsigned t0 = tiles(rows0, cols0), t1 = rows1 > 0 ? tiles(rows1, cols1) : 0u;
-  const QtJob j0{x0, rows0, cols0, codes_t0, amax0, scale0, scale_inv0};
-  const QtJob j1{x1, rows1, cols1, codes_t1, amax1, scale1, scale_inv1};
+  const QtJob j0{x0, rows0, cols0, codes_t0, amax0, scale0, scale_inv0, tiled0 ? tiled_stages(rows0) : 0, split0};
+  const QtJob j1{x1, rows1, cols1, codes_t1, amax1, scale1, scale_inv1, tiled1 ? tiled_stages(rows1) : 0, 0};
   if (x_dtype == kBF16) launch_kernel(quantize_transpose_kernel<true>, t0 + t1, kThreads, 0, s, j0, j1, t0);
   else launch_kernel(quantize_transpose_kernel<false>, t0 + t1, kThreads, 0, s, j0, j1, t0);
   return hipGetLastError();
@@ -855,12 +873,14 @@ hipError_t launch_amax_finalize(const float* part, int64_t n, float* amax, float
 
 hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, int act, bool gated,
                       int mode, void* y, int y_dtype, float* amax, float* scale_out,
-                      float* scale_inv_out, hipStream_t s) {
+                      float* scale_inv_out, hipStream_t s, bool y_tiled) {
   static const char* names[3] = {"act_lu", "act_amax", "act_quant"};
   LaunchScope scope(names[mode], s);
   if (x_dtype == kBF16)
-    return act_dispatch<true>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
-  return act_dispatch<false>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s);
+    return act_dispatch<true>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s,
+                              y_tiled);
+  return act_dispatch<false>(x, rows, cols, act, gated, mode, y, y_dtype, amax, scale_out, scale_inv_out, s,
+                             y_tiled);
 }
 
 

@@ -19,6 +19,11 @@
 // weight-gradient GEMMs of the backward, x^T @ dY, whose operands are both
 // stored token-major. The A tile is then loaded and read exactly like the B
 // tile (k-rows of 256 values, transposing reads).
+//
+// A tiled A (the tiled GEMM operand layout of te_kernels.hpp, written by the
+// library's own normalisation or the previous GEMM's epilogue) holds every
+// stage's A tile as one 16 KiB block in its LDS image: each wave's loads of
+// a stage read one contiguous KiB each, at the block's offset.
 #include "gemm_common.hpp"
 #include "gemm_lds.hpp"
 #include "te_kernels.hpp"
@@ -30,6 +35,7 @@ struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
   int K;
+  int a_tiled;     // A in the tiled operand layout (not with AT)
   EpiArgs ep;
 };
 
@@ -82,8 +88,17 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   // ---- loaders: wave w fills A rows [w RA, (w + 1) RA) (AT: A k-rows [w RB,
   // (w + 1) RB)) and B k-rows [w RB, (w + 1) RB)
   const int rows_a = min(M - m0, kTileM);
+  // tiled A: the tile's blocks, one per k stage (a stage is one block: 256 rows of 2 BK = 64 bytes)
+  static_assert(AT || BK * 2 == 64, "the tiled layout's stages are 64 bytes per row");
+  const bool a_tiled = !AT && a.a_tiled != 0;
+  const uint32_t nks_a = (uint32_t)(K + BK - 1) / BK;
   const __amdgpu_buffer_rsrc_t rsrc_a =
-      AT ? make_rsrc(a.A, (uint32_t)K * M * 2) : make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K * 2);
+      AT ? make_rsrc(a.A, (uint32_t)K * M * 2)
+         : a_tiled ? make_rsrc(reinterpret_cast<const uint8_t*>(a.A) + ((int64_t)tm * nks_a << kTiledBlockShift),
+                               nks_a << kTiledBlockShift)
+                   : make_rsrc(a.A + (int64_t)m0 * K, (uint32_t)rows_a * K * 2);
+  // soffset bytes per k value: a whole block per stage when tiled
+  const uint32_t kstride_a = a_tiled ? (uint32_t)kTileM * 2 : 2u;
   uint32_t off_a[LA];
   int kc_a[LA];
 #pragma unroll
@@ -97,7 +112,9 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     } else {
       const int r = wave * RA + j * (64 / St::CPR) + lane / St::CPR;
       const int c = (lane % St::CPR) ^ chunk_swizzle<St::CPR>(r);
-      off_a[j] = (uint32_t)r * K * 2 + c * 16;
+      // tiled: the block holds slot lane % CPR of row r at 64 r + 16 (lane % CPR) (rows past M read zero)
+      off_a[j] = a_tiled ? (r < rows_a ? (uint32_t)(r * 64 + (lane % St::CPR) * 16) : kOffNone)
+                         : (uint32_t)r * K * 2 + c * 16;
       kc_a[j] = c * 8;
     }
   }
@@ -127,7 +144,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
         load_lds16(rsrc_a, As + wave * RB * 512 + j * 1024, v, (uint32_t)k0 * M * 2);
       } else {
         const uint32_t v = (tail && k0 + kc_a[j] >= K) ? kOffNone : off_a[j];
-        load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * 2);
+        load_lds16(rsrc_a, As + wave * RA * BK * 2 + j * 1024, v, (uint32_t)k0 * kstride_a);
       }
     }
     // k-rows at or past K (including whole stages past the end) read as zero:
@@ -335,6 +352,7 @@ hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t
   a.A = reinterpret_cast<const uint16_t*>(At);
   a.B = reinterpret_cast<const uint16_t*>(B);
   a.K = (int)K;
+  a.a_tiled = 0;
   a.ep.bias = reinterpret_cast<const uint16_t*>(e.bias);
   a.ep.out = reinterpret_cast<uint16_t*>(e.out);
   a.ep.h_out = nullptr;
@@ -343,13 +361,14 @@ hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t
   a.ep.n_b = (int)n_b;
   a.ep.F = (int)n_b;
   a.ep.group = 8;
+  a.ep.out_nks = 0;
   const unsigned grid = (unsigned)(((M + kTileM - 1) / kTileM) * ((n_b + kTileN - 1) / kTileN));
   launch_kernel(gemm_bf16_kernel<kLinear, false, true, false, false, kWaves, kBK, kStages, kPingPong, true>, grid, 64 * kWaves, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
-                            const Epilogue& e, hipStream_t s) {
+                            const Epilogue& e, hipStream_t s, bool a_tiled) {
   LaunchScope scope(e.name != nullptr ? e.name
                                       : e.gated ? "gemm_bf16_gated" : (e.act == kLinear ? "gemm_bf16" : "gemm_bf16_act"),
                     s);
@@ -357,6 +376,7 @@ hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b
   a.A = reinterpret_cast<const uint16_t*>(A);
   a.B = reinterpret_cast<const uint16_t*>(B);
   a.K = (int)K;
+  a.a_tiled = a_tiled ? 1 : 0;
   a.ep.bias = reinterpret_cast<const uint16_t*>(e.bias);
   a.ep.out = reinterpret_cast<uint16_t*>(e.out);
   a.ep.h_out = reinterpret_cast<uint16_t*>(e.h_out);
@@ -364,6 +384,10 @@ hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b
   a.ep.M = (int)M;
   a.ep.n_b = (int)n_b;
   a.ep.F = e.gated ? (int)(n_b / 2) : (int)n_b;
+  a.ep.out_nks = e.out_tiled ? (int)tiled_stages((int64_t)a.ep.F * 2) : 0;
+  if (e.out_tiled && (e.out_f32 || e.out == nullptr || (int64_t)a.ep.F * 2 > kTiledMaxRowBytes))
+    return hipErrorInvalidValue;
+  if (a_tiled && K * 2 > kTiledMaxRowBytes) return hipErrorInvalidValue;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
   a.ep.group = tile_group(tiles_n, false, e.gated);

@@ -16,6 +16,11 @@
 // both operands, no block scaling) takes two 16-byte chunks per lane and
 // operand.
 //
+// Either operand may be tiled (the tiled GEMM operand layout of
+// te_kernels.hpp, written by the library's own quantisers): a stage's tile
+// of that operand is then one 16 KiB block in its LDS image, and each wave's
+// loads read one contiguous KiB each.
+//
 // 256 x 256 output tile per workgroup, 8 waves of 128 x 64, 4 LDS stages
 // (128 KiB). Ping-pong schedule: waves 0-3 and 4-7 hold one wave per SIMD
 // each and alternate, one phase apart, between a memory phase (their share
@@ -44,6 +49,7 @@ struct FpArgs {
   const uint8_t* A;
   const uint8_t* Bt;
   int K;
+  int a_tiled, b_tiled;     // operand in the tiled layout (B^T gated: split F)
   const float* amax_a;      // amaxes of the two quantised operands
   const float* amax_b;
   EpiArgs ep;
@@ -82,8 +88,12 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   const uint32_t pitch = (uint32_t)K * E;  // bytes per operand row (< 2^31, checked by the caller)
 
   // ---- loaders: wave w fills tile rows [w R, (w + 1) R) of both operands
+  static_assert(kRowBytes == 64, "the tiled layout's stages are 64 bytes per row");
   const int rows_a = min(M - m0, kTileM);
-  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(a.A + (int64_t)m0 * pitch, (uint32_t)rows_a * pitch);
+  const uint32_t nks = (uint32_t)(K * E + kRowBytes - 1) / kRowBytes;   // k stages per tiled row tile
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      a.a_tiled ? make_rsrc(a.A + ((int64_t)tm * nks << kTiledBlockShift), nks << kTiledBlockShift)
+                : make_rsrc(a.A + (int64_t)m0 * pitch, (uint32_t)rows_a * pitch);
   // B^T rows of this tile: [n0, n0 + 256), or for gated the first-half rows
   // [n0, n0 + 128) (waves 0-3) and the second-half rows [F + n0, F + n0 + 128) (waves 4-7)
   int b_row0, b_rows;
@@ -94,7 +104,13 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
     b_row0 = n0;
     b_rows = min(NB - n0, kTileN);
   }
-  const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(a.Bt + (int64_t)b_row0 * pitch, (uint32_t)b_rows * pitch);
+  // tiled B^T: block tn holds this tile's rows (gated: the split layout's 128 + 128 rows)
+  const __amdgpu_buffer_rsrc_t rsrc_b =
+      a.b_tiled ? make_rsrc(a.Bt + ((int64_t)tn * nks << kTiledBlockShift), nks << kTiledBlockShift)
+                : make_rsrc(a.Bt + (int64_t)b_row0 * pitch, (uint32_t)b_rows * pitch);
+  // soffset bytes per k value: a whole block per stage when tiled
+  const uint32_t kstride_a = a.a_tiled ? (uint32_t)kTileM : (uint32_t)E;
+  const uint32_t kstride_b = a.b_tiled ? (uint32_t)kTileM : (uint32_t)E;
   const int b_first = GATED ? (wave % (kWaves / 2)) * kRowsPerWave : wave * kRowsPerWave;
   uint32_t off_a[kLJ], off_b[kLJ];
   int kc[kLJ];
@@ -102,8 +118,12 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   for (int j = 0; j < kLJ; ++j) {
     const int r = wave * kRowsPerWave + j * (64 / kCpr) + lane / kCpr;   // row inside the LDS tile
     const int c = (lane % kCpr) ^ chunk_swizzle<kCpr>(r);
-    off_a[j] = (uint32_t)r * pitch + c * 16;
-    off_b[j] = (uint32_t)(b_first + j * (64 / kCpr) + lane / kCpr) * pitch + c * 16;
+    const int rb = b_first + j * (64 / kCpr) + lane / kCpr;              // row of B^T (of its half when gated)
+    // tiled: LDS row r's slot lane % kCpr sits at 64 r + 16 (lane % kCpr) of the block; rows
+    // past the operand read zero
+    const uint32_t tile_off = (uint32_t)(r * kRowBytes + (lane % kCpr) * 16);
+    off_a[j] = a.a_tiled ? (r < rows_a ? tile_off : kOffNone) : (uint32_t)r * pitch + c * 16;
+    off_b[j] = a.b_tiled ? (rb < b_rows ? tile_off : kOffNone) : (uint32_t)rb * pitch + c * 16;
     kc[j] = c * (16 / E);
   }
   auto issue_stage = [&](int kt, int s) {
@@ -114,8 +134,10 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
 #pragma unroll
     for (int j = 0; j < kLJ; ++j) {
       const bool out = k0 + kc[j] >= K;
-      load_lds16(rsrc_a, As + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_a[j], (uint32_t)k0 * E);
-      load_lds16(rsrc_b, Bs + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_b[j], (uint32_t)k0 * E);
+      load_lds16(rsrc_a, As + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_a[j],
+                 (uint32_t)k0 * kstride_a);
+      load_lds16(rsrc_b, Bs + wave * kRowsPerWave * kRowBytes + j * 1024, out ? kOffNone : off_b[j],
+                 (uint32_t)k0 * kstride_b);
     }
   };
 
@@ -236,11 +258,15 @@ hipError_t launch_flags(const FpArgs& a, unsigned grid, hipStream_t s) {
 }
 
 hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int64_t K, const float* amax_a,
-                     const float* amax_b, const Epilogue& e, hipStream_t s) {
+                     const float* amax_b, const Epilogue& e, hipStream_t s, bool a_tiled, bool b_tiled) {
+  if (e.out_tiled) return hipErrorInvalidValue;
+  if ((a_tiled || b_tiled) && K > kTiledMaxRowBytes) return hipErrorInvalidValue;
   FpArgs a;
   a.A = static_cast<const uint8_t*>(A);
   a.Bt = static_cast<const uint8_t*>(Bt);
   a.K = (int)K;
+  a.a_tiled = a_tiled ? 1 : 0;
+  a.b_tiled = b_tiled ? 1 : 0;
   a.amax_a = amax_a;
   a.amax_b = amax_b;
   a.ep.bias = static_cast<const uint16_t*>(e.bias);
@@ -250,6 +276,7 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
   a.ep.M = (int)M;
   a.ep.n_b = (int)n_b;
   a.ep.F = e.gated ? (int)(n_b / 2) : (int)n_b;
+  a.ep.out_nks = 0;
   const int64_t tiles_m = (M + kTileM - 1) / kTileM;
   const int64_t tiles_n = e.gated ? (n_b / 2 + 127) / 128 : (n_b + kTileN - 1) / kTileN;
   a.ep.group = tile_group(tiles_n, true, e.gated);
@@ -274,9 +301,10 @@ hipError_t launch_bt(const void* A, const void* Bt, int64_t M, int64_t n_b, int6
 }  // namespace
 
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b, int64_t K,
-                           const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s) {
+                           const float* amax_a, const float* amax_b, const Epilogue& e, hipStream_t s,
+                           bool a_tiled, bool b_tiled) {
   LaunchScope scope(e.amax != nullptr ? "gemm_fp8_h_amax" : "gemm_fp8", s);
-  return launch_bt(A, Bt, M, n_b, K, amax_a, amax_b, e, s);
+  return launch_bt(A, Bt, M, n_b, K, amax_a, amax_b, e, s, a_tiled, b_tiled);
 }
 
 }  // namespace te

@@ -17,6 +17,7 @@
 // j + NJ / 2, so the gate product f(a) * b happens in registers.
 #pragma once
 
+#include "gemm_lds.hpp"
 #include "te_common.hpp"
 
 namespace te {
@@ -49,6 +50,7 @@ struct EpiArgs {
   float* amax;            // or NULL
   int M, n_b, F;          // F = n_b / 2 when gated, else n_b
   int group;              // row-tiles per group of the tile walk (tile_group())
+  int out_nks;            // > 0: out is a tiled operand with that many k stages per row tile
 };
 
 // LDS row (0..255) of B-fragment block j (of NJ) for wave column wn.
@@ -177,6 +179,47 @@ __device__ __forceinline__ void stage_copy_out(St st, int tid, int rows_valid, D
           const uint4 w = (r & 1) ? make_uint4(v[k].z, v[k].w, v[k].x, v[k].y) : v[k];  // odd rows swap 8-byte units
           *reinterpret_cast<uint4*>(d) = w;
         }
+      }
+    }
+  }
+}
+
+// Copies the staged tile (C bf16 columns) to a tiled operand whose block 0
+// for this tile starts at dst: tile columns [32 s, 32 s + 32) of the 256 rows
+// form block s (16 KiB, dst + s * 16 KiB), row r at 64 r with its chunks at
+// the swizzled slots. Each wave store covers four runs of four rows (256
+// contiguous bytes each); the 16 lanes of each quarter-wave read rows that
+// differ in bits 3-4, which the staging swizzle maps to four disjoint bank
+// quarters. Rows past rows_valid and columns past cols_valid are not written.
+template <int C, int NT, int BATCH, typename St>
+__device__ __forceinline__ void stage_copy_out_tiled(St st, int tid, int rows_valid, int cols_valid, uint8_t* dst) {
+  constexpr int N = kTileM * (C / 8) / NT;   // 16-byte chunks per thread
+  static_assert(kTileM * (C / 8) % NT == 0 && C % 32 == 0, "whole blocks");
+  static_assert(N % BATCH == 0, "whole batches");
+  // chunk u: slot p of row r of block s; the staged chunk q holds its 8 columns
+  auto place = [&](int u, int& r, int& p, int& q, int& s) {
+    p = u & 3;
+    const int i = (u >> 2) & 15, g = (u >> 6) & 15;
+    s = u >> 10;
+    r = (g >> 1) * 32 + (g & 1) * 4 + (i & 3) * 8 + (i >> 2);
+    q = s * 4 + (p ^ chunk_swizzle<4>(r));
+  };
+#pragma unroll
+  for (int k0 = 0; k0 < N; k0 += BATCH) {
+    uint4 v[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      int r, p, q, s;
+      place(tid + (k0 + k) * NT, r, p, q, s);
+      v[k] = *reinterpret_cast<const uint4*>(st(r >> 6) + (r & 63) * (C * 2) + 16 * (q ^ ((r & 31) >> 1)));
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      int r, p, q, s;
+      place(tid + (k0 + k) * NT, r, p, q, s);
+      if (r < rows_valid && 8 * q < cols_valid) {
+        const uint4 w = (r & 1) ? make_uint4(v[k].z, v[k].w, v[k].x, v[k].y) : v[k];  // odd rows swap 8-byte units
+        *reinterpret_cast<uint4*>(dst + ((int64_t)s << kTiledBlockShift) + r * 64 + p * 16) = w;
       }
     }
   }
@@ -352,9 +395,16 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     }
     __syncthreads();
     const int n_out = GATED ? ep.F : ep.n_b;
-    stage_copy_out<C, NT, kTileM * (C / 8) / NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
-      return n0 + c < n_out ? ep.out + (int64_t)(m0 + r) * n_out + n0 + c : nullptr;
-    });
+    if (ep.out_nks > 0) {
+      // m0 / 256 is the row tile; n0 is a multiple of 128 columns (256 bytes), i.e. of 4 k stages
+      uint8_t* dst = reinterpret_cast<uint8_t*>(ep.out) +
+                     (((int64_t)(m0 / kTileM) * ep.out_nks + n0 / 32) << kTiledBlockShift);
+      stage_copy_out_tiled<C, NT, 8>(st, tid, rows_valid, n_out - n0, dst);
+    } else {
+      stage_copy_out<C, NT, kTileM * (C / 8) / NT>(st, tid, rows_valid, [&](int r, int c) -> uint16_t* {
+        return n0 + c < n_out ? ep.out + (int64_t)(m0 + r) * n_out + n0 + c : nullptr;
+      });
+    }
   }
 
   if constexpr (AMAX && !GATED) {

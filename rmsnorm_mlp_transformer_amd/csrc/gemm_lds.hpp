@@ -77,4 +77,22 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
   return (r / (16 / CPR)) & (CPR - 1);
 }
 
+// Byte offset of byte kb of row `row` of a tiled GEMM operand (te_kernels.hpp)
+// with nks k stages per row tile and the given split (0: plain).
+__device__ __forceinline__ int64_t tiled_offset(int64_t row, int64_t kb, int64_t nks, int64_t split) {
+  int64_t t;
+  int r;
+  if (split > 0) {
+    const bool hi = row >= split;
+    const int64_t q = hi ? row - split : row;
+    t = q >> 7;
+    r = (int)(q & 127) + (hi ? 128 : 0);
+  } else {
+    t = row >> 8;
+    r = (int)(row & 255);
+  }
+  const int c = (int)(kb >> 4) & 3;
+  return ((t * nks + (kb >> 6)) << kTiledBlockShift) + r * 64 + ((c ^ chunk_swizzle<4>(r)) << 4) + (kb & 15);
+}
+
 }  // namespace te

@@ -18,6 +18,7 @@
 // * g; g = 1 + gamma for a zero-centred gamma.
 #include <type_traits>
 
+#include "gemm_lds.hpp"
 #include "te_common.hpp"
 #include "te_kernels.hpp"
 
@@ -61,18 +62,20 @@ __device__ __forceinline__ float norm_value(float v, float mean, float rs, float
   return __builtin_fmaf((v - mean) * rs, g, b);
 }
 
-// Store VEC output values of chunk `c` of row `row`.
+// Store VEC output values of chunk `c` of row `row`: row-major, or (nks > 0,
+// BF16 and E4M3 outputs) in the tiled GEMM operand layout with nks k stages
+// per row tile. A chunk's 8 or 16 output bytes never straddle a 16-byte slot.
 template <int OUT, int VEC>
 __device__ __forceinline__ void store_chunk(void* y, int64_t row, int64_t hidden, int64_t c,
-                                            const float* v, float qscale) {
-  const int64_t e = row * hidden + c * VEC;
+                                            const float* v, float qscale, int64_t nks) {
+  constexpr int OB = OUT == kF32 ? 4 : OUT == kBF16 ? 2 : 1;   // output bytes per value
+  const int64_t off = OUT != kF32 && nks > 0 ? tiled_offset(row, c * VEC * OB, nks, 0) : (row * hidden + c * VEC) * OB;
+  uint8_t* p = reinterpret_cast<uint8_t*>(y) + off;
   if constexpr (OUT == kF32) {
-    float* p = reinterpret_cast<float*>(y) + e;
 #pragma unroll
     for (int i = 0; i < VEC; i += 4)
-      *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+      *reinterpret_cast<float4*>(p + 4 * i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
   } else if constexpr (OUT == kBF16) {
-    uint16_t* p = reinterpret_cast<uint16_t*>(y) + e;
     if constexpr (VEC == 8) {
       *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                                 pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
@@ -80,7 +83,6 @@ __device__ __forceinline__ void store_chunk(void* y, int64_t row, int64_t hidden
       *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   } else {
-    uint8_t* p = reinterpret_cast<uint8_t*>(y) + e;
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < VEC; i += 4)
@@ -95,6 +97,7 @@ struct NormArgs {
   int64_t rows, hidden; float eps; int zcg;
   void* y; float* mu; float* rsigma; float* amax; float* scale_out; float* scale_inv_out;
   float* part; int nparts;   // the amax pass's per-workgroup maxima
+  int64_t y_nks;             // > 0: y in the tiled GEMM operand layout with that many k stages
 };
 
 // Maximum of the amax pass's partial maxima, returned to every thread of the
@@ -209,7 +212,7 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
           y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
           lmax = fmaxf(lmax, fabsf(y[i]));
         }
-        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale, a.y_nks);
       }
     }
   };
@@ -284,7 +287,7 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
           y[i] = norm_value(v[i], mean, rs, gi, RMS ? 0.0f : b[i]);
           lmax = fmaxf(lmax, fabsf(y[i]));
         }
-        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale);
+        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale, a.y_nks);
       }
     }
   }
@@ -335,12 +338,14 @@ int64_t norm_amax_parts(int64_t rows) {
 hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                        int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
                        int y_dtype, void* y, float* mu, float* rsigma, float* amax,
-                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s) {
+                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s, bool y_tiled) {
   static const char* names[3] = {"norm_fwd", "norm_amax", "norm_quant"};
   LaunchScope scope(names[mode], s);
   if (mode != kNormStore && part == nullptr) return hipErrorInvalidValue;
+  const int64_t out_bytes = mode == kNormQuant ? 1 : y_dtype == kBF16 ? 2 : 4;
+  if (y_tiled && (out_bytes == 4 || hidden * out_bytes > kTiledMaxRowBytes)) return hipErrorInvalidValue;
   NormArgs a{x, gamma, beta, rows, hidden, eps, zcg ? 1 : 0, y, mu, rsigma, amax, scale_out,
-             scale_inv_out, part, (int)norm_amax_parts(rows)};
+             scale_inv_out, part, (int)norm_amax_parts(rows), y_tiled ? tiled_stages(hidden * out_bytes) : 0};
   if (x_dtype == kBF16) {
     return rms ? dispatch_nch<true, true>(a, mode, y_dtype, s)
                : dispatch_nch<true, false>(a, mode, y_dtype, s);

@@ -131,21 +131,34 @@ hipEvent_t pooled_event() {
 }
 
 // ---------------------------------------------------------------- layouts
+// The library's own GEMM operands (normalised input, activation, transposed
+// kernel codes) are written in the tiled GEMM operand layout whenever their
+// rows are short enough for it; a caller's buffer (the saved codes) stays
+// row-major.
+bool tiled_ok(int64_t row_bytes) { return row_bytes <= te::kTiledMaxRowBytes; }
+// Bytes of a [rows, row_bytes] operand, tiled (split: see te_kernels.hpp) or row-major.
+size_t operand_bytes(bool tiled, int64_t rows, int64_t row_bytes, int64_t split = 0) {
+  return tiled ? te::tiled_bytes(rows, row_bytes, split) : (size_t)rows * row_bytes;
+}
+
 struct DenseWs {
   void* xn;        // normalised input (F32/BF16) or codes
   uint8_t* wt;     // fp8: kernel codes, transposed
   float* metas;    // fp8: 6 floats
   float* npart;    // fp8: the norm amax pass's partial maxima
+  bool tiled;      // xn (and wt) in the tiled operand layout
 };
 DenseWs dense_ws(Carver& c, int64_t rows, int64_t hidden, int64_t out, int dtype, int quant) {
   DenseWs w{};
   if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
+    w.tiled = tiled_ok(hidden);
     w.metas = c.floats(6);
     w.npart = c.floats((size_t)te::norm_amax_parts(rows));
-    w.xn = c.take((size_t)rows * hidden);
-    w.wt = static_cast<uint8_t*>(c.take((size_t)out * hidden));
+    w.xn = c.take(operand_bytes(w.tiled, rows, hidden));
+    w.wt = static_cast<uint8_t*>(c.take(operand_bytes(w.tiled, out, hidden)));
   } else {
-    w.xn = c.take((size_t)rows * hidden * esize(dtype));
+    w.tiled = dtype == TE_BF16 && tiled_ok(hidden * 2);
+    w.xn = c.take(operand_bytes(w.tiled, rows, hidden * esize(dtype)));
   }
   return w;
 }
@@ -158,22 +171,28 @@ struct MlpWs {
   void* h1;        // fp8: GEMM1 output + bias1, bf16 [rows, G*ffn] (when not saved)
   float* metas;    // fp8: 12 floats
   float* npart;    // fp8: the norm amax pass's partial maxima
+  bool t1, t2;     // the workspace operands of GEMM1 (xn, w1t) / GEMM2 (act, w2t) are tiled
 };
 MlpWs mlp_ws(Carver& c, int64_t rows, int64_t hidden, int64_t ffn, int dtype, int act, int quant,
              bool need_h1) {
   MlpWs w{};
   const int64_t g = is_gated(act) ? 2 : 1;
   if (quant == TE_QUANT_FP8_E4M3_CURRENT) {
+    w.t1 = tiled_ok(hidden);
+    w.t2 = tiled_ok(ffn);
     w.metas = c.floats(12);
     w.npart = c.floats((size_t)te::norm_amax_parts(rows));
-    w.xn = c.take((size_t)rows * hidden);
-    w.w1t = static_cast<uint8_t*>(c.take((size_t)g * ffn * hidden));
-    w.w2t = static_cast<uint8_t*>(c.take((size_t)hidden * ffn));
+    w.xn = c.take(operand_bytes(w.t1, rows, hidden));
+    w.w1t = static_cast<uint8_t*>(c.take(operand_bytes(w.t1, g * ffn, hidden, g == 2 ? ffn : 0)));
+    w.w2t = static_cast<uint8_t*>(c.take(operand_bytes(w.t2, hidden, ffn)));
     if (need_h1) w.h1 = c.take((size_t)rows * g * ffn * 2);
-    w.act = c.take((size_t)rows * ffn);
+    w.act = c.take(operand_bytes(w.t2, rows, ffn));
   } else {
-    w.xn = c.take((size_t)rows * hidden * esize(dtype));
-    w.act = c.take((size_t)rows * ffn * esize(dtype));
+    const int64_t es = esize(dtype);
+    w.t1 = dtype == TE_BF16 && tiled_ok(hidden * 2);
+    w.t2 = dtype == TE_BF16 && tiled_ok(ffn * 2);
+    w.xn = c.take(operand_bytes(w.t1, rows, hidden * es));
+    w.act = c.take(operand_bytes(w.t2, rows, ffn * es));
   }
   return w;
 }
@@ -755,12 +774,12 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   ep.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
   if (quant == TE_QUANT_NONE) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn,
-                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
+                           nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s, w.tiled), "norm");
     if (dtype == TE_F32)
       TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.xn), static_cast<const float*>(kernel), rows,
                                  out_features, hidden, ep, s), "gemm");
     else
-      TE_HIP(te::launch_gemm_bf16(w.xn, kernel, rows, out_features, hidden, ep, s), "gemm");
+      TE_HIP(te::launch_gemm_bf16(w.xn, kernel, rows, out_features, hidden, ep, s, w.tiled), "gemm");
     return ok();
   }
   float* mx = w.metas;      // amax, scale, scale_inv of the normalised input
@@ -770,10 +789,11 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
                          nullptr, nullptr, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
   TE_HIP(te::launch_amax(kernel, hidden * out_features, dtype, mw, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
-                         nullptr, nullptr, mx, mx + 1, mx + 2, w.npart, s), "norm quantise");
-  TE_HIP(te::launch_quantize_transpose(kernel, hidden, out_features, dtype, w.wt, mw, mw + 1, mw + 2, s),
+                         nullptr, nullptr, mx, mx + 1, mx + 2, w.npart, s, w.tiled), "norm quantise");
+  TE_HIP(te::launch_quantize_transpose(kernel, hidden, out_features, dtype, w.wt, mw, mw + 1, mw + 2, s, w.tiled),
          "kernel quantise");
-  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.wt, rows, out_features, hidden, mx, mw, ep, s),
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.wt, rows, out_features, hidden, mx, mw, ep, s,
+                             w.tiled, w.tiled),
          "fp8 gemm");
   return ok();
 }
@@ -831,8 +851,9 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
 
   if (quant == TE_QUANT_NONE) {
     TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormStore, dtype, w.xn, mu,
-                           rsigma, nullptr, nullptr, nullptr, nullptr, s), "norm");
+                           rsigma, nullptr, nullptr, nullptr, nullptr, s, w.t1), "norm");
     te::Epilogue e1{bias1, w.act, h1_user, nullptr, k, gated};
+    e1.out_tiled = w.t2;
     te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
     e2.out_f32 = dtype == TE_BF16 && y_dtype == TE_F32;
     if (dtype == TE_F32) {
@@ -841,8 +862,8 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
       TE_HIP(te::launch_gemm_f32(static_cast<const float*>(w.act), static_cast<const float*>(kernel2), rows,
                                  hidden, ffn, e2, s), "gemm2");
     } else {
-      TE_HIP(te::launch_gemm_bf16(w.xn, kernel1, rows, nb1, hidden, e1, s), "gemm1");
-      TE_HIP(te::launch_gemm_bf16(w.act, kernel2, rows, hidden, ffn, e2, s), "gemm2");
+      TE_HIP(te::launch_gemm_bf16(w.xn, kernel1, rows, nb1, hidden, e1, s, w.t1), "gemm1");
+      TE_HIP(te::launch_gemm_bf16(w.act, kernel2, rows, hidden, ffn, e2, s, w.t2), "gemm2");
     }
     return ok();
   }
@@ -852,11 +873,13 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
   Meta ma = pick_meta(saved ? &saved->act_meta : nullptr, w.metas + 6);
   Meta m2 = pick_meta(saved ? &saved->w2_meta : nullptr, w.metas + 9);
   void* h1 = h1_user != nullptr ? h1_user : w.h1;
+  // a caller's code buffer replaces the workspace one and is written row-major
+  bool tx = w.t1, tw1 = w.t1, tw2 = w.t2, ta = w.t2;
   if (saved != nullptr) {
-    if (saved->xq != nullptr) w.xn = saved->xq;
-    if (saved->w1q_t != nullptr) w.w1t = saved->w1q_t;
-    if (saved->w2q_t != nullptr) w.w2t = saved->w2q_t;
-    if (saved->actq != nullptr) w.act = saved->actq;
+    if (saved->xq != nullptr) { w.xn = saved->xq; tx = false; }
+    if (saved->w1q_t != nullptr) { w.w1t = saved->w1q_t; tw1 = false; }
+    if (saved->w2q_t != nullptr) { w.w2t = saved->w2q_t; tw2 = false; }
+    if (saved->actq != nullptr) { w.act = saved->actq; ta = false; }
   }
   TE_HIP(te::launch_fill_zero(w.metas, 12, s), "fill");
   for (const Meta* m : {&m1, &ma, &m2})   // (x's amax is written, not accumulated)
@@ -865,18 +888,22 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
                          rsigma, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
   TE_HIP(te::launch_amax2(kernel1, hidden * nb1, m1.amax, kernel2, ffn * hidden, m2.amax, dtype, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
-                         nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, w.npart, s), "norm quantise");
+                         nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, w.npart, s, tx), "norm quantise");
   TE_HIP(te::launch_quantize_transpose2(kernel1, hidden, nb1, w.w1t, m1.amax, m1.scale, m1.scale_inv, kernel2, ffn,
-                                        hidden, w.w2t, m2.amax, m2.scale, m2.scale_inv, dtype, s),
+                                        hidden, w.w2t, m2.amax, m2.scale, m2.scale_inv, dtype, s, tw1, tw2,
+                                        gated && tw1 ? ffn : 0),
          "kernel quantise");
   te::Epilogue e1{bias1, nullptr, h1, ma.amax, k, gated};
-  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.w1t, rows, nb1, hidden, mx.amax, m1.amax, e1, s),
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.xn), w.w1t, rows, nb1, hidden, mx.amax, m1.amax, e1, s,
+                             tx, tw1),
          "fp8 gemm1");
-  TE_HIP(te::launch_act(h1, rows, ffn, TE_BF16, k, gated, 2, w.act, TE_E4M3, ma.amax, ma.scale, ma.scale_inv, s),
+  TE_HIP(te::launch_act(h1, rows, ffn, TE_BF16, k, gated, 2, w.act, TE_E4M3, ma.amax, ma.scale, ma.scale_inv, s,
+                        ta),
          "act quantise");
   te::Epilogue e2{bias2, y, nullptr, nullptr, te::kLinear, false};
   e2.out_f32 = y_dtype == TE_F32;
-  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.act), w.w2t, rows, hidden, ffn, ma.amax, m2.amax, e2, s),
+  TE_HIP(te::launch_gemm_fp8(static_cast<const uint8_t*>(w.act), w.w2t, rows, hidden, ffn, ma.amax, m2.amax, e2, s,
+                             ta, tw2),
          "fp8 gemm2");
   return ok();
 }

@@ -43,6 +43,36 @@ inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint3
   hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<KArgs>(args)...);
 }
 
+// ---------------------------------------------------------------- GEMM operand tiles
+// The MFMA GEMMs stream a K-contiguous operand [rows, K] in k stages of 64
+// bytes per row and 256 rows per workgroup tile. An operand that the library
+// writes itself for one of its own GEMMs (the normalised input, the
+// activation, the quantised kernels; never a caller's tensor) is stored
+// "tiled": as the sequence of those stages, each exactly the image the GEMM
+// keeps in LDS, so that every load instruction of the GEMM reads one
+// contiguous KiB instead of sixteen 64-byte pieces a row pitch apart.
+//   block (t, s): rows [256 t, 256 t + 256) x bytes [64 s, 64 s + 64) of each
+//   row, 16 KiB at (t * S + s) * 16 KiB, S = tiled_stages(row bytes); inside
+//   it row r sits at 64 r with its 16-byte chunk c at slot c ^ ((r / 4) % 4)
+//   (the GEMMs' LDS chunk swizzle).
+// Split layout (the gated GEMM1's transposed kernel, whose 256-row tile is
+// rows [128 t, 128 t + 128) of the first half and the same rows of the second
+// half [split, 2 split)): block rows 0..127 and 128..255 hold those two runs.
+// Bytes of a block past the operand's rows or K are never written or read
+// (the GEMMs' range checks return zeros there). tiled_offset() in
+// gemm_lds.hpp maps (row, byte) to the layout.
+constexpr int kTiledBlockShift = 14;   // 16 KiB blocks
+// Longest tiled row: keeps every stage's block offset (the GEMMs' scalar
+// buffer offset, up to three stages past the end) far below 2^31.
+constexpr int64_t kTiledMaxRowBytes = (int64_t)1 << 20;
+inline int64_t tiled_stages(int64_t row_bytes) { return (row_bytes + 63) / 64; }
+inline int64_t tiled_row_tiles(int64_t rows, int64_t split) {
+  return split > 0 ? (split + 127) / 128 : (rows + 255) / 256;
+}
+inline size_t tiled_bytes(int64_t rows, int64_t row_bytes, int64_t split) {
+  return (size_t)(tiled_row_tiles(rows, split) * tiled_stages(row_bytes)) << kTiledBlockShift;
+}
+
 // ---------------------------------------------------------------- norm
 enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
 // kNormStore: y (F32/BF16) and optional mu/rsigma.
@@ -51,10 +81,12 @@ enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
 // kNormQuant: y = E4M3 codes with the scale from the maximum of those
 //             partials; writes *amax, *scale_out and *scale_inv_out.
 // part is required by the two fp8 modes (norm_amax_parts(rows) floats).
+// y_tiled: y (BF16 or E4M3) in the tiled GEMM operand layout.
 hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                        int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
                        int y_dtype, void* y, float* mu, float* rsigma, float* amax,
-                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s);
+                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s,
+                       bool y_tiled = false);
 int64_t norm_amax_parts(int64_t rows);
 
 // ---------------------------------------------------------------- elementwise
@@ -76,27 +108,31 @@ hipError_t launch_quantize(const void* x, int64_t n, int x_dtype, uint8_t* codes
                            hipStream_t s);
 
 // Quantise a [rows, cols] matrix and store it transposed as [cols, rows]
-// codes (K-contiguous operand layout for the fp8 GEMM).
+// codes (K-contiguous operand layout for the fp8 GEMM); tiled: in the tiled
+// GEMM operand layout, split as described there (0: plain).
 hipError_t launch_quantize_transpose(const void* x, int64_t rows, int64_t cols, int x_dtype,
                                      uint8_t* codes_t, const float* amax, float* scale_out,
-                                     float* scale_inv_out, hipStream_t s);
-// The same for two matrices of one dtype in one launch (rows1 = 0: only the first).
-// y [cols, rows] = x [rows, cols]^T, bf16; rows and cols multiples of 16.
-hipError_t launch_transpose_bf16(const void* x, int64_t rows, int64_t cols, void* y, hipStream_t s);
+                                     float* scale_inv_out, hipStream_t s, bool tiled = false);
+// The same for two matrices of one dtype in one launch (rows1 = 0: only the
+// first), each tiled or not; split0 applies to the first.
 hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t cols0, uint8_t* codes_t0,
                                       const float* amax0, float* scale0, float* scale_inv0, const void* x1,
                                       int64_t rows1, int64_t cols1, uint8_t* codes_t1, const float* amax1,
-                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s);
+                                      float* scale1, float* scale_inv1, int x_dtype, hipStream_t s,
+                                      bool tiled0 = false, bool tiled1 = false, int64_t split0 = 0);
+// y [cols, rows] = x [rows, cols]^T, bf16; rows and cols multiples of 16.
+hipError_t launch_transpose_bf16(const void* x, int64_t rows, int64_t cols, void* y, hipStream_t s);
 
 hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale_inv, void* y,
                              int y_dtype, hipStream_t s);
 
 // Activation forward: x [rows, G*cols] -> y [rows, cols].
 // mode 0: store y (F32/BF16); 1: amax only, one partial maximum per workgroup
-// into amax[0 .. act_amax_blocks()); 2: E4M3 codes using *amax.
+// into amax[0 .. act_amax_blocks()); 2: E4M3 codes using *amax, in the tiled
+// GEMM operand layout when y_tiled.
 hipError_t launch_act(const void* x, int64_t rows, int64_t cols, int x_dtype, int act,
                       bool gated, int mode, void* y, int y_dtype, float* amax,
-                      float* scale_out, float* scale_inv_out, hipStream_t s);
+                      float* scale_out, float* scale_inv_out, hipStream_t s, bool y_tiled = false);
 int64_t act_amax_blocks(int64_t rows, int64_t cols, bool gated);
 // Max of n partial maxima -> amax; scale = 448 / amax (1 if 0), scale_inv.
 hipError_t launch_amax_finalize(const float* part, int64_t n, float* amax, float* scale, float* scale_inv,
@@ -147,22 +183,25 @@ struct Epilogue {
   bool gated;
   const char* name = nullptr;   // timing-scope name (default: from act / gated)
   bool out_f32 = false;   // out is fp32 (plain ungated epilogue without h_out / amax only)
+  bool out_tiled = false; // out (bf16) in the tiled GEMM operand layout (the next GEMM's A)
 };
 
-// bf16: C[M, n_out] from A [M, K] (row-major) and B [K, n_b] (row-major).
+// bf16: C[M, n_out] from A [M, K] (row-major, or tiled when a_tiled) and
+// B [K, n_b] (row-major).
 hipError_t launch_gemm_bf16(const void* A, const void* B, int64_t M, int64_t n_b, int64_t K,
-                            const Epilogue& ep, hipStream_t s);
+                            const Epilogue& ep, hipStream_t s, bool a_tiled = false);
 
 // bf16 with A^T [K, M] and B [K, n_b] (both row-major with K the row index),
 // linear epilogue: the weight-gradient GEMMs of the backward.
 hipError_t launch_gemm_bf16_at(const void* At, const void* B, int64_t M, int64_t n_b, int64_t K,
                                const Epilogue& ep, hipStream_t s);
 
-// fp8: A codes [M, K] and B^T codes [n_b, K] (both K-contiguous); the
+// fp8: A codes [M, K] and B^T codes [n_b, K] (both K-contiguous, each
+// row-major or tiled; a gated B^T is tiled with split n_b / 2); the
 // accumulator is multiplied by scale_inv(amax_a) * scale_inv(amax_b).
 hipError_t launch_gemm_fp8(const uint8_t* A, const uint8_t* Bt, int64_t M, int64_t n_b,
                            int64_t K, const float* amax_a, const float* amax_b,
-                           const Epilogue& ep, hipStream_t s);
+                           const Epilogue& ep, hipStream_t s, bool a_tiled = false, bool b_tiled = false);
 
 // fp32: all operands fp32.
 hipError_t launch_gemm_f32(const float* A, const float* B, int64_t M, int64_t n_b, int64_t K,

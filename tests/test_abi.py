@@ -249,6 +249,29 @@ def test_workspace_sizes_cover_the_buffers():
         < lib.te_layernorm_mlp_fwd_workspace_size(200, 64, 128, B.TE_F32, B.TE_ACT_RELU, B.TE_QUANT_NONE)
 
 
+def test_workspace_sizes_hold_the_tiled_operands():
+    """The GEMM operands kept in the workspace are stored as 16 KiB blocks of
+    256 rows x 64 bytes, a partial row tile or k stage taking a whole block
+    (the gated GEMM1's transposed kernel: tiles of 128 rows of each half), so
+    the sizes cover the padded blocks."""
+    lib = B._lib
+    blk = 16384
+
+    def tiled(rows, row_bytes, tile_rows=256):
+        return -(-rows // tile_rows) * -(-row_bytes // 64) * blk
+
+    r, h, f = 300, 80, 144
+    bf16 = lib.te_layernorm_mlp_fwd_workspace_size(r, h, f, B.TE_BF16, B.TE_ACT_GELU, B.TE_QUANT_NONE)
+    assert bf16 >= tiled(r, 2 * h) + tiled(r, 2 * f) == (6 + 10) * blk
+    fp8 = lib.te_layernorm_mlp_fwd_workspace_size(r, h, f, B.TE_BF16, B.TE_ACT_SWIGLU, B.TE_QUANT_FP8_E4M3_CURRENT)
+    assert fp8 >= tiled(r, h) + tiled(f, h, 128) + tiled(h, f) + r * 2 * f * 2 + tiled(r, f)
+    d = lib.te_layernorm_dense_fwd_workspace_size(r, h, 528, B.TE_BF16, B.TE_QUANT_FP8_E4M3_CURRENT)
+    assert d >= tiled(r, h) + tiled(528, h)
+    # fp32 operands stay row-major
+    assert lib.te_layernorm_mlp_fwd_workspace_size(r, h, f, B.TE_F32, B.TE_ACT_GELU, B.TE_QUANT_NONE) \
+        < tiled(r, 4 * h) + tiled(r, 4 * f)
+
+
 def test_timing_api_without_launches():
     te.te_timing_reset()
     te.te_timing_enable(True)

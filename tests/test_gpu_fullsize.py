@@ -80,18 +80,24 @@ def fp8_run():
                                 activation_type=w.activation_type, quantizer_set=q, return_saved=True,
                                 save_codes=True)
     dx, db = te.dact_dbias(g["grad"], saved["h1"], w.activation_type, dbias_dtype=torch.bfloat16)
+    # as bench.py runs it: no saved context, the codes in the workspace's tiled layout
+    y_bench = te.layernorm_mlp(g["x"], g["gamma"], g["beta"], [g["kernel1"], g["kernel2"]],
+                               [g["bias1"], g["bias2"]], w.norm_type, epsilon=w.epsilon,
+                               activation_type=w.activation_type, quantizer_set=te.QuantizerSet())
     torch.cuda.synchronize()
     f = {k: f64(v) for k, v in t.items()}
     o = O.layernorm_mlp_fwd(f["x"], f["gamma"], f["beta"], f["kernel1"], f["kernel2"], f["bias1"], f["bias2"],
                             epsilon=w.epsilon, activation_type=w.activation_type, quant="fp8_e4m3_current")
     rdx, rdb = O.dact_dbias(f["grad"], o["h1"], w.activation_type)
-    return dict(w=w, q=q, y=y, saved=saved, dx=dx, db=db, o=o, rdx=rdx, rdb=rdb, grad=f["grad"])
+    return dict(w=w, q=q, y=y, saved=saved, dx=dx, db=db, o=o, rdx=rdx, rdb=rdb, grad=f["grad"], y_bench=y_bench)
 
 
 def test_full_mlp_fp8_forward(fp8_run):
     r = fp8_run
     print("full fp8 forward: every code, h1 and y element", flush=True)
     check_fp8_forward(r["q"], r["saved"], r["y"], r["o"], r["w"].activation_type, label="ln_mlp_gelu_fp8")
+    # the benchmarked call (workspace codes, tiled) computes the same values in the same order
+    assert torch.equal(r["y_bench"], r["y"]), "y of the call without saved codes"
 
 
 def test_full_dact_dbias_on_fp8_saved_h1(fp8_run):

@@ -154,7 +154,12 @@ def test_mlp_fp8(name, rows, hidden, ffn, gated):
     g = to_dev(t)
     q = te.QuantizerSet()
     y, saved = _mlp_gpu(w, g, quantizer_set=q, return_saved=True, save_codes=True)
+    # without caller code buffers the codes stay in the workspace in the tiled
+    # GEMM operand layout: the same values in the same summation order, so y
+    # and h1 are bit-identical to the run above, whose codes are checked
+    y_t, saved_t = _mlp_gpu(w, g, quantizer_set=te.QuantizerSet(), return_saved=True)
     torch.cuda.synchronize()
+    assert torch.equal(y_t, y) and torch.equal(saved_t["h1"], saved["h1"]), "tiled workspace codes"
     o = _mlp_oracle(w, t, quant="fp8_e4m3_current")
     check_fp8_forward(q, saved, y, o, w.activation_type, w.name)
 
