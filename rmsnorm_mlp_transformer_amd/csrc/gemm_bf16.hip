@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   if constexpr (PP) {
     // ---- ping-pong pipeline. Waves 0-3 and 4-7 form two groups with one
     // wave of each on every SIMD. Each wave alternates a memory phase M(t)
-    // (its share of the DMA of stage t+3, all fragment reads of stage t, then
+    // (all fragment reads of stage t, its share of the DMA of stage t+3, then
     // waits) and a compute phase C(t) (the stage's 16 MFMAs), with a barrier
     // after each. Group 1 starts one phase late, so on every SIMD one wave
     // issues MFMAs while the other feeds LDS and registers.
@@ -257,9 +257,13 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     block_barrier();
     if (late) block_barrier();
     auto pp_step = [&](int kt, int s) {
-      issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+      // the fragment reads go out before the DMA: issuing the LDS-DMA first
+      // held the reads back (and the phase's MFMAs with them) by ~100 clocks
+      // per stage
       read_frags(s, 0, fa);
       read_frags(s, 1, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_stage(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
       wait_vmcnt_lgkm0<(STAGES - 2) * (LA + LB)>();
       block_barrier();
       __builtin_amdgcn_sched_barrier(0);

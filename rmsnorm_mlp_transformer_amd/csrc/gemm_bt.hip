@@ -23,9 +23,9 @@
 //
 // 256 x 256 output tile per workgroup, 8 waves of 128 x 64, 4 LDS stages
 // (128 KiB). Ping-pong schedule: waves 0-3 and 4-7 hold one wave per SIMD
-// each and alternate, one phase apart, between a memory phase (their share
-// of the DMA three stages ahead, all fragment reads of the current stage)
-// and a compute phase (the stage's MFMAs), so each SIMD's matrix core is fed
+// each and alternate, one phase apart, between a memory phase (all fragment
+// reads of the current stage, then their share of the DMA three stages
+// ahead) and a compute phase (the stage's MFMAs), so each SIMD's matrix core is fed
 // by one wave while the other loads.
 #include "gemm_common.hpp"
 #include "gemm_lds.hpp"
@@ -196,9 +196,9 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   // ---- ping-pong pipeline.
   //   phase 2t:   group 0 memory M(t),  group 1 compute C(t-1)
   //   phase 2t+1: group 0 compute C(t), group 1 memory M(t)
-  // M(t): DMA of the wave's share of stage t+3 into the buffer of stage t-1,
-  // fragment reads of stage t, then wait for those reads and for the wave's
-  // share of stage t+1 (two newer stages stay in flight); barrier.
+  // M(t): fragment reads of stage t, DMA of the wave's share of stage t+3
+  // into the buffer of stage t-1, then wait for those reads and for the
+  // wave's share of stage t+1 (two newer stages stay in flight); barrier.
   // C(t): the stage's MFMAs; barrier.
   // The buffer of stage t-1 was last read by group 1 in phase 2t-1 and those
   // reads completed before that phase's barrier; both groups' shares of stage
@@ -213,8 +213,11 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   block_barrier();
   if (late) block_barrier();
   auto step = [&](int kt, int s) {
-    issue_stage(kt + kStages - 1, (s + kStages - 1) % kStages);
+    // the fragment reads go out before the DMA (issuing the LDS-DMA first
+    // held the reads and the phase's MFMAs back)
     read_frags(s);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_stage(kt + kStages - 1, (s + kStages - 1) % kStages);
     wait_vmcnt_lgkm0<(kStages - 2) * kLoads>();
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);

@@ -184,41 +184,43 @@ __device__ __forceinline__ void stage_copy_out(St st, int tid, int rows_valid, D
   }
 }
 
-// Copies the staged tile (C bf16 columns) to a tiled operand whose block 0
-// for this tile starts at dst: tile columns [32 s, 32 s + 32) of the 256 rows
-// form block s (16 KiB, dst + s * 16 KiB), row r at 64 r with its chunks at
-// the swizzled slots. Each wave store covers four runs of four rows (256
-// contiguous bytes each); the 16 lanes of each quarter-wave read rows that
-// differ in bits 3-4, which the staging swizzle maps to four disjoint bank
-// quarters. Rows past rows_valid and columns past cols_valid are not written.
+// Tiled staging (an output in the tiled GEMM operand layout): the tile is
+// staged as its own tiled image, block s (tile columns [32 s, 32 s + 32))
+// of rows [64 a, 64 a + 64) at st(a) + 4 KiB s, row r at 64 (r % 64), its
+// 16-byte chunk c at slot c ^ chunk_swizzle<4>(r) as in global memory, and
+// the two 8-byte halves of the slot exchanged in rows with bit 4 set. A
+// staging write (8 bytes: four columns of one row, 32 consecutive rows per
+// half-wave) then touches 32 distinct 8-byte bank pairs, and the copy-out
+// moves each wave's 16 rows x 64 bytes of a block as one contiguous KiB,
+// from LDS and to memory alike.
+template <typename St>
+__device__ __forceinline__ uint8_t* stage_tiled(St st, int r, int tc) {
+  const int s = tc >> 5, c = (tc >> 3) & 3, h = ((tc >> 2) & 1) ^ ((r >> 4) & 1);
+  return st(r >> 6) + s * 4096 + (r & 63) * 64 + ((c ^ chunk_swizzle<4>(r)) << 4) + h * 8;
+}
+
+// Copies a tile staged by stage_tiled() (C bf16 columns) to the tiled
+// operand whose block 0 for this tile starts at dst (block s at dst + s * 16
+// KiB). Rows past rows_valid and columns past cols_valid are not written.
 template <int C, int NT, int BATCH, typename St>
 __device__ __forceinline__ void stage_copy_out_tiled(St st, int tid, int rows_valid, int cols_valid, uint8_t* dst) {
   constexpr int N = kTileM * (C / 8) / NT;   // 16-byte chunks per thread
   static_assert(kTileM * (C / 8) % NT == 0 && C % 32 == 0, "whole blocks");
   static_assert(N % BATCH == 0, "whole batches");
-  // chunk u: slot p of row r of block s; the staged chunk q holds its 8 columns
-  auto place = [&](int u, int& r, int& p, int& q, int& s) {
-    p = u & 3;
-    const int i = (u >> 2) & 15, g = (u >> 6) & 15;
-    s = u >> 10;
-    r = (g >> 1) * 32 + (g & 1) * 4 + (i & 3) * 8 + (i >> 2);
-    q = s * 4 + (p ^ chunk_swizzle<4>(r));
-  };
 #pragma unroll
   for (int k0 = 0; k0 < N; k0 += BATCH) {
     uint4 v[BATCH];
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      int r, p, q, s;
-      place(tid + (k0 + k) * NT, r, p, q, s);
-      v[k] = *reinterpret_cast<const uint4*>(st(r >> 6) + (r & 63) * (C * 2) + 16 * (q ^ ((r & 31) >> 1)));
+      const int u = tid + (k0 + k) * NT, p = u & 3, r = (u >> 2) & 255, s = u >> 10;   // slot p of row r, block s
+      v[k] = *reinterpret_cast<const uint4*>(st(r >> 6) + s * 4096 + (r & 63) * 64 + p * 16);
     }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
-      int r, p, q, s;
-      place(tid + (k0 + k) * NT, r, p, q, s);
-      if (r < rows_valid && 8 * q < cols_valid) {
-        const uint4 w = (r & 1) ? make_uint4(v[k].z, v[k].w, v[k].x, v[k].y) : v[k];  // odd rows swap 8-byte units
+      const int u = tid + (k0 + k) * NT, p = u & 3, r = (u >> 2) & 255, s = u >> 10;
+      const int col = 32 * s + 8 * (p ^ chunk_swizzle<4>(r));   // first of the slot's 8 columns
+      if (r < rows_valid && col < cols_valid) {
+        const uint4 w = (r & 16) ? make_uint4(v[k].z, v[k].w, v[k].x, v[k].y) : v[k];
         *reinterpret_cast<uint4*>(dst + ((int64_t)s << kTiledBlockShift) + r * 64 + p * 16) = w;
       }
     }
@@ -371,7 +373,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
             unpack_bias4(bv[j][g], b);
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + b[q]);
-            *reinterpret_cast<uint2*>(stage_unit<C>(st, r, tc >> 2)) =
+            *reinterpret_cast<uint2*>(ep.out_nks > 0 ? stage_tiled(st, r, tc) : stage_unit<C>(st, r, tc >> 2)) =
                 make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
         }
@@ -387,7 +389,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
-            *reinterpret_cast<uint2*>(stage_unit<C>(st, r, tc >> 2)) =
+            *reinterpret_cast<uint2*>(ep.out_nks > 0 ? stage_tiled(st, r, tc) : stage_unit<C>(st, r, tc >> 2)) =
                 make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           }
         }
