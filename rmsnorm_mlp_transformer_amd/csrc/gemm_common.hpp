@@ -134,6 +134,13 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, const float* v) {
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
+// x, as a value the compiler cannot see through (it stops the reuse of
+// values computed from x earlier in the epilogue).
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void round_bf16x4(float* v) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) v[r] = bf16_to_f32(f32_to_bf16(v[r]));
@@ -286,7 +293,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     return;
   }
   float lmax = 0.0f;
-  float hmax = -INFINITY, hmin = INFINITY;   // range of the lane's rounded h (plain amax)
+  // range of the lane's h (plain amax), rounded to bf16 at the end: rounding
+  // to nearest is monotonic, so the rounded maximum is the maximum of the
+  // rounded values (and likewise the minimum)
+  float hmax = -INFINITY, hmin = INFINITY;
   // every wave's LDS reads of the main loop are done before the staging writes
   __syncthreads();
 
@@ -312,9 +322,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
             bool in_range;
             tile_col<GATED>(ep, n0, tc, in_range);
             if (in_range && m0 + r < ep.M) {
-              round_bf16x4(h);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) { hmax = fmaxf(hmax, h[q]); hmin = fminf(hmin, h[q]); }
+              hmax = fmaxf(fmaxf(hmax, h[0]), fmaxf(h[1], fmaxf(h[2], h[3])));
+              hmin = fminf(fminf(hmin, h[0]), fminf(h[1], fminf(h[2], h[3])));
             }
           }
         }
@@ -413,9 +422,13 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
     // max |act(h)| from the range of h: exact whenever it reaches the
     // activation's threshold; otherwise (a lane whose values are all small)
     // every value is evaluated.
-    lmax = amax_from_range<ACT>(hmax, hmin);
+    lmax = amax_from_range<ACT>(bf16_to_f32(f32_to_bf16(hmax)), bf16_to_f32(f32_to_bf16(hmin)));
     if (lmax < amax_exact_from<ACT>()) {
       lmax = 0.0f;
+      // an opaque copy of the scale: recomputing h here from the
+      // accumulators keeps the compiler from holding the first pass's h
+      // values (128 registers) live until this rarely taken branch
+      const float scale_a = opaque(scale);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = wm * 128 + i * 32 + lm;
@@ -430,7 +443,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
               float h[4], b[4];
               unpack_bias4(bv[j][g], b);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale + b[q];
+              for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale_a + b[q];
               round_bf16x4(h);
 #pragma unroll
               for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(h[q])));
