@@ -92,6 +92,30 @@ __device__ __forceinline__ void store_chunk(void* y, int64_t row, int64_t hidden
   }
 }
 
+// Tiled output staged through LDS: the workgroup's four rows r0 .. r0 + 3
+// (one per wave, r0 a multiple of 4, so all in one 256-row tile) are written
+// to LDS as the four 64-byte pieces of every k stage, stage s at 256 s with
+// row w's piece in slot w ^ (s % 4) (the XOR keeps a wave's chunk writes on
+// distinct banks), each piece already in the operand's chunk swizzle; the
+// workgroup then stores each stage's 256 bytes as one contiguous run.
+template <int OUT, int VEC>
+__device__ __forceinline__ void stage_chunk(uint8_t* stg, int w, int64_t row, int64_t c, const float* v,
+                                            float qscale) {
+  constexpr int OB = OUT == kBF16 ? 2 : 1;
+  static_assert(OUT != kF32 && VEC == 8, "bf16 or E4M3 output of 8-value chunks");
+  const int kb = (int)c * VEC * OB;                   // byte of the chunk in its row
+  const int s = kb >> 6;
+  const int slot = ((kb >> 4) & 3) ^ (int)((row >> 2) & 3);
+  uint8_t* p = stg + s * 256 + ((w ^ (s & 3)) << 6) + (slot << 4) + (kb & 15);
+  if constexpr (OUT == kBF16) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+  } else {
+    *reinterpret_cast<uint2*>(p) = make_uint2(e4m3_pack4(v[0] * qscale, v[1] * qscale, v[2] * qscale, v[3] * qscale),
+                                              e4m3_pack4(v[4] * qscale, v[5] * qscale, v[6] * qscale, v[7] * qscale));
+  }
+}
+
 struct NormArgs {
   const void* x; const void* gamma; const void* beta;
   int64_t rows, hidden; float eps; int zcg;
@@ -116,10 +140,13 @@ __device__ __forceinline__ float block_max_of_parts(const float* part, int n, fl
 }
 
 // NCH > 0: NCH 16-byte chunks per lane kept in registers. NCH == 0: loop.
-template <bool BF16, int NCH, bool RMS, int MODE, int OUT>
+// STAGED (NCH > 0, bf16 or E4M3 output in the tiled GEMM operand layout): the
+// output goes through LDS (stage_chunk()) and leaves in 256-byte runs.
+template <bool BF16, int NCH, bool RMS, int MODE, int OUT, bool STAGED = false>
 __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   using I = Io<BF16>;
   constexpr int VEC = I::VEC;
+  static_assert(!STAGED || (NCH > 0 && MODE != kNormAmax && OUT != kF32), "staged: tiled bf16 / E4M3 rows");
   const int lane = threadIdx.x & 63;
   const int64_t nch = a.hidden / VEC;
   const uint4* gr = reinterpret_cast<const uint4*>(a.gamma);
@@ -155,6 +182,8 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   // gamma and beta, read once per workgroup into LDS (rows of up to NCH * 64
   // chunks use the register path below)
   __shared__ uint4 sg[NCH > 0 ? NCH * 64 : 1], sb[NCH > 0 && !RMS ? NCH * 64 : 1];
+  // STAGED: four rows of output (NCH * 64 chunks of 8 values each)
+  __shared__ __attribute__((aligned(16))) uint8_t stg[STAGED ? 4 * NCH * 64 * 8 * (OUT == kBF16 ? 2 : 1) : 16];
   if constexpr (NCH > 0) {
     for (int64_t c = threadIdx.x; c < nch; c += blockDim.x) {
       sg[c] = load16(rgam, c, Cached{});
@@ -212,11 +241,74 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
           y[i] = norm_value(v[j][i], mean, rs, gi, RMS ? 0.0f : b[i]);
           lmax = fmaxf(lmax, fabsf(y[i]));
         }
-        if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale, a.y_nks);
+        if constexpr (STAGED) stage_chunk<OUT, VEC>(stg, wave, row, c, y, qscale);
+        else if constexpr (MODE != kNormAmax) store_chunk<OUT, VEC>(a.y, row, a.hidden, c, y, qscale, a.y_nks);
       }
     }
   };
-  if (row < a.rows) {
+  if constexpr (STAGED) {
+    // every wave of the workgroup walks the same row groups (rows 4 g .. 4 g
+    // + 3 of groups g = blockIdx.x, + gridDim.x, ...), so all reach the
+    // barriers; a row past the end is neither loaded nor staged
+    auto load_row = [&](int64_t r, uint4* xw) {
+      const bool ok = r < a.rows;
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint4*>(reinterpret_cast<const uint4*>(a.x) + (ok ? r : 0) * nch), (short)0,
+          ok ? (int)row_bytes : 0, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) xw[j] = load16(rx, lane + 64 * j, Stream{});
+    };
+    constexpr int OB = OUT == kBF16 ? 2 : 1;
+    const int64_t groups = (a.rows + 3) / 4;
+    const int64_t nks = a.y_nks;
+    const int64_t rb = a.hidden * OB;   // output bytes per row
+    uint8_t* ybase = reinterpret_cast<uint8_t*>(a.y);
+    // the staged group leaves as 256-byte runs: 16-byte unit u = 16 s + q of
+    // stage s is slot q % 4 of the piece in LDS slot q / 4
+    auto store_group = [&](int64_t g) {
+      const int64_t r0 = 4 * g;
+      for (int64_t u = threadIdx.x; u < nks * 16; u += blockDim.x) {
+        const int64_t st = u >> 4;
+        const int q = (int)(u & 15), p = q & 3;
+        const int64_t r = r0 + ((q >> 2) ^ (int)(st & 3));
+        const int cs = p ^ (int)((r >> 2) & 3);   // the chunk the slot holds
+        if (r < a.rows && st * 64 + cs * 16 < rb) {
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + st * 256 + q * 16);
+          *reinterpret_cast<uint4*>(ybase + (((r0 >> 8) * nks + st) << kTiledBlockShift) + ((r & 255) << 6) + p * 16) = v;
+        }
+      }
+    };
+    // LDS-only barrier: the prefetched rows' loads stay in flight across it
+    auto lds_barrier = [&]() {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's LDS accesses are done (lgkmcnt 0)
+      block_barrier();
+    };
+    int64_t g = blockIdx.x;
+    if (g < groups) {
+      uint4 xa[NCH], xb[NCH];
+      load_row(row, xa);
+      while (true) {
+        load_row(row + step, xb);
+        __builtin_amdgcn_sched_barrier(0);
+        if (row < a.rows) finish_row(row, xa);
+        lds_barrier();
+        store_group(g);
+        lds_barrier();
+        row += step;
+        g += gridDim.x;
+        if (g >= groups) break;
+        load_row(row + step, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (row < a.rows) finish_row(row, xb);
+        lds_barrier();
+        store_group(g);
+        lds_barrier();
+        row += step;
+        g += gridDim.x;
+        if (g >= groups) break;
+      }
+    }
+  } else if (row < a.rows) {
     if constexpr (NCH > 0) {
       // the next row's x is in flight while the current one is reduced and
       // written (two register sets used
@@ -305,12 +397,18 @@ hipError_t dispatch_mode(const NormArgs& a, int mode, int y_dtype, hipStream_t s
   const int64_t blocks = (a.rows + 3) / 4;
   const int64_t cap = mode == kNormAmax ? (int64_t)kNormAmaxBlocks : (int64_t)kNormBlocks;
   const dim3 grid((unsigned)(blocks > cap ? cap : blocks)), block(256);
+  // tiled output of the register path goes through LDS
+  constexpr bool kStage = NCH > 0 && BF16;
+  const bool staged = kStage && a.y_nks > 0;
   if (mode == kNormAmax) {
     launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormAmax, kF32>, grid, block, 0, s, a);
   } else if (mode == kNormQuant) {
-    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3>, grid, block, 0, s, a);
+    if (staged) launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3, kStage>, grid, block, 0, s, a);
+    else launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormQuant, kE4M3>, grid, block, 0, s, a);
   } else if (y_dtype == kF32) {
     launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kF32>, grid, block, 0, s, a);
+  } else if (staged) {
+    launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kBF16, kStage>, grid, block, 0, s, a);
   } else {
     launch_kernel(norm_fwd_kernel<BF16, NCH, RMS, kNormStore, kBF16>, grid, block, 0, s, a);
   }
