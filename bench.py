@@ -49,31 +49,31 @@ import workloads as W  # noqa: E402
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
 CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
-_GEMM_HDR = ["gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp"]
+_GEMM_HDR = ["gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp", "te_kernels.hpp"]
 _GEMM_NC = ["gemm_bf16.hip"] + _GEMM_HDR     # N-contiguous bf16 kernel
 _GEMM_KC = ["gemm_bt.hip"] + _GEMM_HDR       # K-contiguous fp8 kernel
+_ELEM = ["elementwise.hip", "te_common.hpp", "gemm_lds.hpp", "te_kernels.hpp"]
 KERNEL_SOURCES = {
     "gemm_bf16_act": _GEMM_NC, "gemm_bf16": _GEMM_NC, "gemm_bf16_gated": _GEMM_NC, "gemm_bf16_wgrad": _GEMM_NC,
     "gemm_bf16_dgrad": _GEMM_NC, "gemm_fp8_h_amax": _GEMM_KC, "gemm_fp8": _GEMM_KC,
-    "dact_dbias": ["elementwise.hip", "te_common.hpp"],
-    "dact_quant": ["elementwise.hip", "te_common.hpp"], "dact_dbias_amax": ["elementwise.hip", "te_common.hpp"],
-    "norm_bwd": ["norm_bwd.hip", "te_common.hpp", "gemm_lds.hpp"],
+    "dact_dbias": _ELEM, "dact_quant": _ELEM, "dact_dbias_amax": _ELEM,
+    "norm_bwd": ["norm_bwd.hip", "te_common.hpp", "gemm_lds.hpp", "te_kernels.hpp"],
 }
 # Counter-measured HBM bytes per launch: {(workload, kernel): (bytes, source hash)}.
 # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 (the plain-copy scales); the summary is
 # profiles/counters_all_kernels_bench.md. The backward's entry is the mean of
 # its two data-gradient GEMMs (dY.kernel2^T and dh1.kernel1^T), one launch each per step.
 TRAFFIC = {
-    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879551110, "c28be1a4f8e854ea"),
-    ("ln_dense_bf16", "gemm_bf16"): (704864112, "c28be1a4f8e854ea"),
-    ("rms_swiglu_bf16", "gemm_bf16_gated"): (3121984168, "c28be1a4f8e854ea"),
-    ("ln_mlp_gelu_fp8", "gemm_fp8_h_amax"): (1477747120, "ec0c46db7023bc00"),
-    ("dact_dbias_gelu_bf16", "dact_dbias"): (822159747, "d3b023cb0d88a07d"),
-    ("dact_dbias_swiglu_bf16", "dact_dbias"): (1208135150, "d3b023cb0d88a07d"),
-    ("ln_mlp_gelu_bf16_backward", "gemm_bf16_dgrad"): (1761546502, "c28be1a4f8e854ea"),
-    ("norm_bwd_ln_bf16", "norm_bwd"): (210005248, "25ef1d48eb7af58f"),
-    ("dact_dbias_quantize_gelu_bf16", "dact_quant"): (671158940, "d3b023cb0d88a07d"),
-    ("dact_dbias_quantize_gelu_bf16", "dact_dbias_amax"): (553992571, "d3b023cb0d88a07d"),
+    ("ln_mlp_gelu_bf16", "gemm_bf16_act"): (1879599218, "b73a58c3c59c305b"),
+    ("ln_dense_bf16", "gemm_bf16"): (704901326, "b73a58c3c59c305b"),
+    ("rms_swiglu_bf16", "gemm_bf16_gated"): (3107404177, "b73a58c3c59c305b"),
+    ("ln_mlp_gelu_fp8", "gemm_fp8_h_amax"): (1515434769, "163908ca43513e37"),
+    ("dact_dbias_gelu_bf16", "dact_dbias"): (822159612, "f1dc48a578ebbb1e"),
+    ("dact_dbias_swiglu_bf16", "dact_dbias"): (1208090081, "f1dc48a578ebbb1e"),
+    ("ln_mlp_gelu_bf16_backward", "gemm_bf16_dgrad"): (1749555131, "b73a58c3c59c305b"),
+    ("norm_bwd_ln_bf16", "norm_bwd"): (210005208, "04d1fb31abfda56a"),
+    ("dact_dbias_quantize_gelu_bf16", "dact_quant"): (671166046, "f1dc48a578ebbb1e"),
+    ("dact_dbias_quantize_gelu_bf16", "dact_dbias_amax"): (553981292, "f1dc48a578ebbb1e"),
 }
 
 
