@@ -671,7 +671,10 @@ __global__ void __launch_bounds__(64 * kActWaves) act_kernel(const void* x, int6
   const uint32_t vy = (uint32_t)((w * cols + col) * OS);
   float m = 0.0f;
   if (col < cols) {
-    for (int64_t ch = blockIdx.y; ch < nchunks; ch += gridDim.y) {
+    for (int64_t ch0 = blockIdx.y; ch0 < nchunks; ch0 += gridDim.y) {
+      // the quantise mode takes the last rows first: the ones its producer,
+      // GEMM1's epilogue, wrote last (0.0714 -> 0.0697 ms at 8192 x 16384)
+      const int64_t ch = MODE == 2 ? nchunks - 1 - ch0 : ch0;
       const int64_t r_begin = ch * rows_per_chunk;
       const int64_t nr = min(rows_per_chunk, rows - r_begin);
       const Rsrc rx = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + r_begin * xcols * ES, nr * xcols * ES);

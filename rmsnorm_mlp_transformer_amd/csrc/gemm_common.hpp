@@ -17,6 +17,8 @@
 // j + NJ / 2, so the gate product f(a) * b happens in registers.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_lds.hpp"
 #include "te_common.hpp"
 
@@ -305,6 +307,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wm * 128 + i * 32 + lm;
+      float hmax_i = -INFINITY, hmin_i = INFINITY;   // this row's part of the range
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -319,13 +322,20 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
                 make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
           }
           if constexpr (AMAX && !GATED) {
-            bool in_range;
-            tile_col<GATED>(ep, n0, tc, in_range);
-            if (in_range && m0 + r < ep.M) {
-              hmax = fmaxf(fmaxf(hmax, h[0]), fmaxf(h[1], fmaxf(h[2], h[3])));
-              hmin = fminf(fminf(hmin, h[0]), fminf(h[1], fminf(h[2], h[3])));
-            }
+            // no column check: a column past the matrix holds h = 0 exactly
+            // (its B values and its bias read as zero), and a 0 added to the
+            // range changes no result of amax_from_range() (nor the exact
+            // evaluation it falls back to)
+            hmax_i = fmaxf(fmaxf(hmax_i, h[0]), fmaxf(h[1], fmaxf(h[2], h[3])));
+            hmin_i = fminf(fminf(hmin_i, h[0]), fminf(h[1], fminf(h[2], h[3])));
           }
+        }
+      }
+      if constexpr (AMAX && !GATED) {
+        // rows past the matrix hold h = bias: left out, one check per row
+        if (m0 + r < ep.M) {
+          hmax = fmaxf(hmax, hmax_i);
+          hmin = fminf(hmin, hmin_i);
         }
       }
       if constexpr (AMAX && GATED) {
@@ -369,41 +379,50 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
   // ---- activation output
   if constexpr (STORE_OUT) {
     constexpr int C = GATED ? 128 : 256;
+    // the staging layout is chosen once, outside the loops (a per-store
+    // choice costs a branch and both address computations per store); with
+    // the h store before it, the per-store choice keeps fewer registers live
+    auto stage_act = [&](auto tiled) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + lm;
-      if constexpr (!GATED) {
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + lm;
+        auto dst = [&](int tc) -> uint2* {
+          return reinterpret_cast<uint2*>(static_cast<bool>(tiled) ? stage_tiled(st, r, tc) : stage_unit<C>(st, r, tc >> 2));
+        };
+        if constexpr (!GATED) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
+          for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;
-            float b[4], o[4];
-            unpack_bias4(bv[j][g], b);
+            for (int g = 0; g < 4; ++g) {
+              const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;
+              float b[4], o[4];
+              unpack_bias4(bv[j][g], b);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + b[q]);
-            *reinterpret_cast<uint2*>(ep.out_nks > 0 ? stage_tiled(st, r, tc) : stage_unit<C>(st, r, tc >> 2)) =
-                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+              for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + b[q]);
+              *dst(tc) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            }
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
+          for (int j = 0; j < NJ / 2; ++j) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;   // first-half tile column
-            float ba[4], bb[4], o[4];
-            unpack_bias4(bv[j][g], ba);
-            unpack_bias4(bv[j + NJ / 2][g], bb);
+            for (int g = 0; g < 4; ++g) {
+              const int tc = b_block_row<GATED, NJ>(wn, j) + g * 8 + lh * 4;   // first-half tile column
+              float ba[4], bb[4], o[4];
+              unpack_bias4(bv[j][g], ba);
+              unpack_bias4(bv[j + NJ / 2][g], bb);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
-            *reinterpret_cast<uint2*>(ep.out_nks > 0 ? stage_tiled(st, r, tc) : stage_unit<C>(st, r, tc >> 2)) =
-                make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+              for (int q = 0; q < 4; ++q)
+                o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
+              *dst(tc) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+            }
           }
         }
       }
-    }
+    };
+    if constexpr (STORE_H) stage_act(ep.out_nks > 0);
+    else if (ep.out_nks > 0) stage_act(std::true_type{});
+    else stage_act(std::false_type{});
     __syncthreads();
     const int n_out = GATED ? ep.F : ep.n_b;
     if (ep.out_nks > 0) {
