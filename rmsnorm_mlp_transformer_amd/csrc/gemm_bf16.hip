@@ -180,16 +180,23 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     b_off[j] = St::A_BYTES + (8 * (g >> 1) + i4) * 512 + 16 * ((n_local >> 3) ^ swz_b(i4)) + 8 * (c4 & 1);
   }
 
-  uint2 bv[NJ][4];   // the epilogue's bias values, loaded while the main loop runs
+  // the bias starts the accumulation (h = bias + the products, in fp32), so
+  // no bias registers stay live through the main loop and the epilogue has
+  // no add per value
+  uint2 bv[NJ][4];
   load_bias_frag<GATED, NJ>(a.ep, n0, wn, lane, bv);
-
   f32x16_t acc[4][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int g = 0; g < 4; ++g) {
+      float b[4];
+      unpack_bias4(bv[j][g], b);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = b[q];
+    }
 
   // ---- one k-substep: fragment reads and the MFMAs that consume them
   constexpr int KS = BK / 16;                         // substeps per stage
@@ -321,8 +328,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
   wait_vmcnt<0>();   // no LDS-DMA may still be writing when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
 
-  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES, OUT_F32>(acc, bv, a.ep, m0, n0, wm, wn, lane, tid,
-                                                                             1.0f, stage_ptr);
+  gemm_epilogue<ACT, GATED, STORE_OUT, STORE_H, AMAX, NJ, 64 * WAVES, OUT_F32, true>(acc, bv, a.ep, m0, n0, wm, wn, lane,
+                                                                                   tid, 1.0f, stage_ptr);
 }
 
 constexpr int kWaves = TE_GEMM_WAVES;

@@ -128,6 +128,13 @@ __device__ __forceinline__ void load_bias_frag(const EpiArgs& ep, int n0, int wn
     }
 }
 
+// h from an accumulator: acc * scale + bias, or acc * scale when the bias
+// started the accumulation (the bf16 GEMMs, whose scale is 1)
+template <bool IN_ACC>
+__device__ __forceinline__ float hval(float acc, float scale, float b) {
+  return IN_ACC ? acc * scale : acc * scale + b;
+}
+
 __device__ __forceinline__ void unpack_bias4(const uint2& w, float* b) {
   b[0] = bf16_lo(w.x); b[1] = bf16_hi(w.x); b[2] = bf16_lo(w.y); b[3] = bf16_hi(w.y);
 }
@@ -254,7 +261,8 @@ constexpr float amax_exact_from() {
   return ACT == kGelu || ACT == kGeluErf ? 0.2f : ACT == kSilu ? 0.3f : 0.0f;
 }
 
-// h = acc * scale + bias; then the stores / amax selected by the flags. Both
+// h = acc * scale + bias (BIAS_IN_ACC: acc * scale, the accumulators having
+// started from the bias); then the stores / amax selected by the flags. Both
 // bf16 stores go through the LDS staging tile (the main loop's LDS is free
 // here). AMAX evaluates the activation from h rounded to bf16, exactly as a
 // later pass reading the stored h would. bv: load_bias_frag() of the same
@@ -262,7 +270,7 @@ constexpr float amax_exact_from() {
 // direct 16-byte stores: a lane's four consecutive columns of one row; the
 // four register groups of a block cover 128 contiguous bytes of each row.
 template <int ACT, bool GATED, bool STORE_OUT, bool STORE_H, bool AMAX, int NJ, int NT, bool OUT_F32 = false,
-          typename St>
+          bool BIAS_IN_ACC = false, typename St>
 __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], const uint2 (&bv)[NJ][4],
                                               const EpiArgs& ep, int m0, int n0, int wm, int wn, int lane,
                                               int tid, float scale, St st) {
@@ -282,10 +290,10 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
           float b[4];
           unpack_bias4(bv[j][g], b);
           float4 o;
-          o.x = act_fwd<ACT>(acc[i][j][4 * g + 0] * scale + b[0]);
-          o.y = act_fwd<ACT>(acc[i][j][4 * g + 1] * scale + b[1]);
-          o.z = act_fwd<ACT>(acc[i][j][4 * g + 2] * scale + b[2]);
-          o.w = act_fwd<ACT>(acc[i][j][4 * g + 3] * scale + b[3]);
+          o.x = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + 0], scale, b[0]));
+          o.y = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + 1], scale, b[1]));
+          o.z = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + 2], scale, b[2]));
+          o.w = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + 3], scale, b[3]));
           // n_b is a multiple of 16 and tc of 4: the four columns are all in or all out
           if (r < rows_valid && n0 + tc < ep.n_b)
             *reinterpret_cast<float4*>(out + (int64_t)(m0 + r) * ep.n_b + n0 + tc) = o;
@@ -316,7 +324,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
           float h[4], b[4];
           unpack_bias4(bv[j][g], b);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale + b[q];
+          for (int q = 0; q < 4; ++q) h[q] = hval<BIAS_IN_ACC>(acc[i][j][4 * g + q], scale, b[q]);
           if constexpr (STORE_H) {
             *reinterpret_cast<uint2*>(stage_unit<256>(st, r, tc >> 2)) =
                 make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
@@ -351,8 +359,8 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
               unpack_bias4(bv[j + NJ / 2][g], bb);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                ha[q] = acc[i][j][4 * g + q] * scale + ba[q];
-                hb[q] = acc[i][j + NJ / 2][4 * g + q] * scale + bb[q];
+                ha[q] = hval<BIAS_IN_ACC>(acc[i][j][4 * g + q], scale, ba[q]);
+                hb[q] = hval<BIAS_IN_ACC>(acc[i][j + NJ / 2][4 * g + q], scale, bb[q]);
               }
               round_bf16x4(ha);
               round_bf16x4(hb);
@@ -398,7 +406,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
               float b[4], o[4];
               unpack_bias4(bv[j][g], b);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + b[q]);
+              for (int q = 0; q < 4; ++q) o[q] = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + q], scale, b[q]));
               *dst(tc) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
           }
@@ -413,7 +421,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
               unpack_bias4(bv[j + NJ / 2][g], bb);
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                o[q] = act_fwd<ACT>(acc[i][j][4 * g + q] * scale + ba[q]) * (acc[i][j + NJ / 2][4 * g + q] * scale + bb[q]);
+                o[q] = act_fwd<ACT>(hval<BIAS_IN_ACC>(acc[i][j][4 * g + q], scale, ba[q])) * (hval<BIAS_IN_ACC>(acc[i][j + NJ / 2][4 * g + q], scale, bb[q]));
               *dst(tc) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
             }
           }
@@ -462,7 +470,7 @@ __device__ __forceinline__ void gemm_epilogue(const f32x16_t (&acc)[4][NJ], cons
               float h[4], b[4];
               unpack_bias4(bv[j][g], b);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) h[q] = acc[i][j][4 * g + q] * scale_a + b[q];
+              for (int q = 0; q < 4; ++q) h[q] = hval<BIAS_IN_ACC>(acc[i][j][4 * g + q], scale_a, b[q]);
               round_bf16x4(h);
 #pragma unroll
               for (int q = 0; q < 4; ++q) lmax = fmaxf(lmax, fabsf(act_fwd<ACT>(h[q])));
