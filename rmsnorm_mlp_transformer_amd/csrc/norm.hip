@@ -122,6 +122,7 @@ struct NormArgs {
   void* y; float* mu; float* rsigma; float* amax; float* scale_out; float* scale_inv_out;
   float* part; int nparts;   // the amax pass's per-workgroup maxima
   int64_t y_nks;             // > 0: y in the tiled GEMM operand layout with that many k stages
+  ClearList clear;           // amax pass: floats workgroup 0 sets to zero
 };
 
 // Maximum of the amax pass's partial maxima, returned to every thread of the
@@ -153,6 +154,14 @@ __global__ void __launch_bounds__(256) norm_fwd_kernel(NormArgs a) {
   const uint4* br = reinterpret_cast<const uint4*>(a.beta);
   const float inv_h = 1.0f / (float)a.hidden;
 
+  if constexpr (MODE == kNormAmax) {
+    // the call's amax slots that later passes raise with atomics start at zero
+    if (blockIdx.x == 0) {
+      const int t = threadIdx.x;
+      if (t < a.clear.n) a.clear.first[t] = 0.0f;
+      if (t < 3 && a.clear.one[t] != nullptr) *a.clear.one[t] = 0.0f;
+    }
+  }
   float qscale = 1.0f;
   if constexpr (MODE == kNormQuant) {
     // the tensor's amax from the amax pass's partials; workgroup 0 publishes
@@ -436,14 +445,18 @@ int64_t norm_amax_parts(int64_t rows) {
 hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                        int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
                        int y_dtype, void* y, float* mu, float* rsigma, float* amax,
-                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s, bool y_tiled) {
+                       float* scale_out, float* scale_inv_out, float* part, hipStream_t s, bool y_tiled,
+                       const ClearList* clear) {
   static const char* names[3] = {"norm_fwd", "norm_amax", "norm_quant"};
   LaunchScope scope(names[mode], s);
   if (mode != kNormStore && part == nullptr) return hipErrorInvalidValue;
   const int64_t out_bytes = mode == kNormQuant ? 1 : y_dtype == kBF16 ? 2 : 4;
   if (y_tiled && (out_bytes == 4 || hidden * out_bytes > kTiledMaxRowBytes)) return hipErrorInvalidValue;
   NormArgs a{x, gamma, beta, rows, hidden, eps, zcg ? 1 : 0, y, mu, rsigma, amax, scale_out,
-             scale_inv_out, part, (int)norm_amax_parts(rows), y_tiled ? tiled_stages(hidden * out_bytes) : 0};
+             scale_inv_out, part, (int)norm_amax_parts(rows), y_tiled ? tiled_stages(hidden * out_bytes) : 0,
+             clear != nullptr ? *clear : ClearList{}};
+  if (a.clear.n > 256 || (a.clear.n > 0 && a.clear.first == nullptr) || (clear != nullptr && mode != kNormAmax))
+    return hipErrorInvalidValue;
   if (x_dtype == kBF16) {
     return rms ? dispatch_nch<true, true>(a, mode, y_dtype, s)
                : dispatch_nch<true, false>(a, mode, y_dtype, s);

@@ -784,9 +784,11 @@ te_status te_layernorm_dense_fwd(const void* x, const void* kernel, const void* 
   }
   float* mx = w.metas;      // amax, scale, scale_inv of the normalised input
   float* mw = w.metas + 3;  // ... of the kernel
-  TE_HIP(te::launch_fill_zero(w.metas, 6, s), "fill");
+  te::ClearList clear;   // the kernel's amax, raised by atomics (x's is written)
+  clear.first = w.metas;
+  clear.n = 6;
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr,
-                         nullptr, nullptr, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
+                         nullptr, nullptr, nullptr, nullptr, nullptr, w.npart, s, false, &clear), "norm amax");
   TE_HIP(te::launch_amax(kernel, hidden * out_features, dtype, mw, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
                          nullptr, nullptr, mx, mx + 1, mx + 2, w.npart, s, w.tiled), "norm quantise");
@@ -881,11 +883,16 @@ te_status te_layernorm_mlp_fwd(const void* x, const void* gamma, const void* bet
     if (saved->w2q_t != nullptr) { w.w2t = saved->w2q_t; tw2 = false; }
     if (saved->actq != nullptr) { w.act = saved->actq; ta = false; }
   }
-  TE_HIP(te::launch_fill_zero(w.metas, 12, s), "fill");
-  for (const Meta* m : {&m1, &ma, &m2})   // (x's amax is written, not accumulated)
-    if (m->amax < w.metas || m->amax >= w.metas + 12) TE_HIP(te::launch_fill_zero(m->amax, 1, s), "fill");
+  // the amax slots raised by atomics (both kernels' and act's; x's is
+  // written) are zeroed by the first pass, with the workspace metas
+  te::ClearList clear;
+  clear.first = w.metas;
+  clear.n = 12;
+  int nclear = 0;
+  for (const Meta* m : {&m1, &ma, &m2})
+    if (m->amax < w.metas || m->amax >= w.metas + 12) clear.one[nclear++] = m->amax;
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormAmax, TE_E4M3, nullptr, mu,
-                         rsigma, nullptr, nullptr, nullptr, w.npart, s), "norm amax");
+                         rsigma, nullptr, nullptr, nullptr, w.npart, s, false, &clear), "norm amax");
   TE_HIP(te::launch_amax2(kernel1, hidden * nb1, m1.amax, kernel2, ffn * hidden, m2.amax, dtype, s), "kernel amax");
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zcg, epsilon, te::kNormQuant, TE_E4M3, w.xn,
                          nullptr, nullptr, mx.amax, mx.scale, mx.scale_inv, w.npart, s, tx), "norm quantise");

@@ -82,11 +82,21 @@ enum NormMode { kNormStore = 0, kNormAmax = 1, kNormQuant = 2 };
 //             partials; writes *amax, *scale_out and *scale_inv_out.
 // part is required by the two fp8 modes (norm_amax_parts(rows) floats).
 // y_tiled: y (BF16 or E4M3) in the tiled GEMM operand layout.
+// Floats that a call's first pass sets to zero for the passes after it to
+// raise with atomics (amax slots): n floats from `first`, and up to three
+// single floats elsewhere (nullptr: none).
+struct ClearList {
+  float* first = nullptr;
+  int n = 0;
+  float* one[3] = {nullptr, nullptr, nullptr};
+};
+// clear (amax mode only): workgroup 0 zeroes the listed floats, so that no
+// separate fill launch precedes the pass.
 hipError_t launch_norm(const void* x, const void* gamma, const void* beta, int64_t rows,
                        int64_t hidden, int x_dtype, bool rms, bool zcg, float eps, int mode,
                        int y_dtype, void* y, float* mu, float* rsigma, float* amax,
                        float* scale_out, float* scale_inv_out, float* part, hipStream_t s,
-                       bool y_tiled = false);
+                       bool y_tiled = false, const ClearList* clear = nullptr);
 int64_t norm_amax_parts(int64_t rows);
 
 // ---------------------------------------------------------------- elementwise
