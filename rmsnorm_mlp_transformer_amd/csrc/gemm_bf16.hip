@@ -182,21 +182,25 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
 
   // the bias starts the accumulation (h = bias + the products, in fp32), so
   // no bias registers stay live through the main loop and the epilogue has
-  // no add per value
+  // no add per value. Its loads go out right after the first stage's DMA
+  // (which they would otherwise hold back), and the wait for that stage
+  // covers them.
   uint2 bv[NJ][4];
-  load_bias_frag<GATED, NJ>(a.ep, n0, wn, lane, bv);
   f32x16_t acc[4][NJ];
+  auto start_from_bias = [&]() {
+    load_bias_frag<GATED, NJ>(a.ep, n0, wn, lane, bv);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float b[4];
-      unpack_bias4(bv[j][g], b);
+      for (int g = 0; g < 4; ++g) {
+        float b[4];
+        unpack_bias4(bv[j][g], b);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = b[q];
-    }
+          for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = b[q];
+      }
+  };
 
   // ---- one k-substep: fragment reads and the MFMAs that consume them
   constexpr int KS = BK / 16;                         // substeps per stage
@@ -258,8 +262,10 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
     // complete before phase 2t+2, where it is first read.
     const bool late = wave >= WAVES / 2;
     Frags fa, fb;
+    issue_stage(0, 0);
+    start_from_bias();
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+    for (int s = 1; s < STAGES - 1; ++s) issue_stage(s, s);
     wait_vmcnt<(STAGES - 2) * (LA + LB)>();
     block_barrier();
     if (late) block_barrier();
@@ -311,8 +317,10 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_bf16_kernel(GemmArgs a) {
       mfmas(f1);
       interleave();
     };
+    issue_stage(0, 0);
+    start_from_bias();
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s) issue_stage(s, s);
+    for (int s = 1; s < STAGES - 1; ++s) issue_stage(s, s);
     wait_vmcnt<(STAGES - 2) * (LA + LB)>();
     block_barrier();
     read_frags(0, 0, f0);

@@ -157,7 +157,6 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   }
 
   uint2 bv[kNJ][4];   // the epilogue's bias values, loaded while the main loop runs
-  load_bias_frag<GATED, kNJ>(a.ep, n0, wn, lane, bv);
 
   f32x16_t acc[4][kNJ];
 #pragma unroll
@@ -207,8 +206,12 @@ __global__ void __launch_bounds__(64 * kWaves, 1) gemm_bt_kernel(FpArgs a) {
   // the same in every step, and both groups pass the same number of barriers.
   const bool late = wave >= kWaves / 2;
   const int nk = (K + KE - 1) / KE;
+  // the bias loads go out right after the first stage's DMA, which they
+  // would otherwise hold back
+  issue_stage(0, 0);
+  load_bias_frag<GATED, kNJ>(a.ep, n0, wn, lane, bv);
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_stage(s, s);
+  for (int s = 1; s < kStages - 1; ++s) issue_stage(s, s);
   wait_vmcnt<(kStages - 2) * kLoads>();
   block_barrier();
   if (late) block_barrier();
