@@ -30,6 +30,7 @@ kernel's source files and reported as null once those sources change.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                        [--no-parts] [--no-cpu-baseline] [--workload NAME]
        python bench.py --copy-probe MIB      (plain copy, for counter scaling)
+       python bench.py --mfma-probe ITERS    (the library's MFMA issue-rate probe, bf16 and fp8)
 """
 import argparse
 import hashlib
@@ -47,6 +48,7 @@ import torch  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}   # dense TFLOP/s, MI355X spec
+MFMA_PROBE_BLOCKS = 512   # the MFMA probe: two 4-wave workgroups per compute unit, the GEMMs' 8 waves
 CSRC = os.path.join(ROOT, "rmsnorm_mlp_transformer_amd", "csrc")
 # Source files that define each kernel (for the staleness check of TRAFFIC).
 _GEMM_HDR = ["gemm_common.hpp", "gemm_lds.hpp", "te_common.hpp", "te_kernels.hpp"]
@@ -466,7 +468,23 @@ def main():
                     help="run steps for this long before the warmup steps of each measurement (clock ramp)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times)")
+    ap.add_argument("--mfma-probe", type=int, default=0,
+                    help="only run the library's MFMA issue-rate probe with this many iterations per chain")
     args = ap.parse_args()
+    if args.mfma_probe:
+        import rmsnorm_mlp_transformer_amd as te
+        out = {"blocks": MFMA_PROBE_BLOCKS, "iters": args.mfma_probe}
+        for name, fp8, peak in (("bf16", False, PEAK["bf16"]), ("fp8", True, PEAK["fp8"])):
+            t_end = time.perf_counter() + SETTLE_MS / 1e3   # clock settle, as for the workloads
+            while time.perf_counter() < t_end:
+                te.probe_mfma(fp8, args.mfma_probe, MFMA_PROBE_BLOCKS)
+            runs = [te.probe_mfma(fp8, args.mfma_probe, MFMA_PROBE_BLOCKS) for _ in range(3)]
+            ms, flops, sticks, rticks = sorted(runs)[1]
+            tflops = flops / (ms * 1e-3) / 1e12
+            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tflops, 1), "frac_of_peak": round(tflops / peak, 4),
+                         "clock_GHz": round(sticks / rticks * 0.1, 3)}
+        print(json.dumps({"mfma_probe": out}), flush=True)
+        return
     if args.copy_probe:
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")

@@ -329,6 +329,20 @@ te_status te_quantize(const void* x, int64_t n, te_dtype x_dtype, uint8_t* codes
 te_status te_dequantize(const uint8_t* codes, int64_t n, const te_fp8_meta* meta,
                         void* y, te_dtype y_dtype, void* stream);
 
+/* te_probe_mfma - a measurement aid, not an operation of the method: the
+ * matrix instructions of the GEMMs' main loops with nothing around them, to
+ * measure the rate and shader clock the chip sustains on them. Each of
+ * `blocks` workgroups (256 threads) runs, per wave, four independent chains
+ * of `iters` MFMAs on fixed pseudo-random operands: v_mfma_f32_32x32x16_bf16
+ * (bf16 values of magnitude 0.5 to 2), or with fp8 != 0
+ * v_mfma_f32_32x32x64_f8f6f4 on E4M3 codes. Work: blocks * 4 waves * iters
+ * * 4 * 32768 flops (bf16) or * 131072 (fp8). sink: device, blocks * 256
+ * floats, written (one sum per thread, so the loop stays). ticks: device, 2
+ * uint64 or NULL: the shader-clock ticks (s_memtime) and 100 MHz
+ * reference-clock ticks (s_memrealtime) workgroup 0 spent in its loop.
+ * TE_ERR_INVALID_ARGUMENT for blocks or iters < 1 or a NULL sink. */
+te_status te_probe_mfma(int fp8, int64_t iters, int blocks, float* sink, uint64_t* ticks, void* stream);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* te_last_error(void);
 

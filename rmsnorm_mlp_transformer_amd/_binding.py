@@ -98,6 +98,7 @@ _SIGS = {
     "te_layernorm_mlp_bwd_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "te_quantize": (_int, [_vp, _i64, _int, _vp, _meta_p, _vp]),
     "te_dequantize": (_int, [_vp, _i64, _meta_p, _vp, _int, _vp]),
+    "te_probe_mfma": (_int, [_int, _i64, _int, _vp, _vp, _vp]),
     "te_last_error": (ctypes.c_char_p, []),
     "te_version": (ctypes.c_char_p, []),
     "te_timing_enable": (_int, [_int]),
@@ -310,6 +311,22 @@ def te_quantize(x, n, x_dtype, codes, meta: Fp8Meta, stream=None):
 
 def te_dequantize(codes, n, meta: Fp8Meta, y, y_dtype, stream=None):
     _check(_lib.te_dequantize(_ptr(codes), n, ctypes.byref(meta.c()), _ptr(y), y_dtype, _stream(stream)))
+
+
+def probe_mfma(fp8: bool, iters: int, blocks: int, device="cuda:0"):
+    """Runs the MFMA issue-rate probe (te_probe_mfma) once on the current
+    stream; returns (milliseconds, flops, shader-clock ticks, 100 MHz
+    reference ticks) of the launch."""
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    ticks = torch.zeros(2, dtype=torch.int64, device=device)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    _check(_lib.te_probe_mfma(1 if fp8 else 0, iters, blocks, sink.data_ptr(), ticks.data_ptr(), _stream()))
+    stop.record()
+    torch.cuda.synchronize()
+    flops = blocks * 4 * iters * 4 * (131072 if fp8 else 32768)
+    t = ticks.cpu().tolist()
+    return start.elapsed_time(stop), flops, t[0], t[1]
 
 
 def te_version() -> str:

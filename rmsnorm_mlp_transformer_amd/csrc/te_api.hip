@@ -276,6 +276,13 @@ void scope_launch_events(hipEvent_t* start, hipEvent_t* stop) {
 extern "C" {
 
 const char* te_last_error(void) { return g_error.c_str(); }
+te_status te_probe_mfma(int fp8, int64_t iters, int blocks, float* sink, uint64_t* ticks, void* stream) {
+  TE_ARG(blocks >= 1 && iters >= 1, "blocks and iters must be at least 1");
+  TE_ARG(sink != nullptr, "sink is required");
+  TE_HIP(te::launch_mfma_probe(fp8 != 0, iters, blocks, sink, ticks, as_stream(stream)), "mfma probe");
+  return ok();
+}
+
 const char* te_version(void) { return "temi355x 0.1.0 (gfx950)"; }
 
 // ---------------------------------------------------------------- timing

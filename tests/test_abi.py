@@ -288,3 +288,11 @@ def test_act_type_names():
     assert te.act_type_of("gelu") == B.TE_ACT_GELU
     with pytest.raises(ValueError):
         te.act_type_of(("tanh",))
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    """The probe's argument checks run before any GPU work."""
+    lib = B._lib
+    assert lib.te_probe_mfma(0, 0, 4, 1, None, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_probe_mfma(0, 10, 0, 1, None, None) == B.TE_ERR_INVALID_ARGUMENT
+    assert lib.te_probe_mfma(1, 10, 4, None, None, None) == B.TE_ERR_INVALID_ARGUMENT

@@ -274,3 +274,15 @@ def test_norm_bwd_zero_rows():
     dx, dg, db = te.layernorm_bwd(x, x, mu, mu, gamma, "layernorm")
     torch.cuda.synchronize()
     assert dx.shape == (0, 64) and not dg.any() and not db.any()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mfma_probe_runs_and_reports_its_clock(fp8):
+    """The MFMA issue-rate probe (a measurement aid): every thread's sum is
+    finite and the loop's shader-clock and reference-clock ticks are positive
+    (their ratio, the shader clock, is a plausible frequency)."""
+    print(f"mfma probe fp8={fp8}", flush=True)
+    ms, flops, sticks, rticks = te.probe_mfma(fp8, 200, 8)
+    assert flops == 8 * 4 * 200 * 4 * (131072 if fp8 else 32768)
+    assert ms > 0 and sticks > 0 and rticks > 0
+    assert 0.3 < sticks / rticks * 0.1 < 3.5, (sticks, rticks)
