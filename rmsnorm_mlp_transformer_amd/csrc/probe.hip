@@ -4,6 +4,7 @@
 // aid, not an operation of the method.
 #include <hip/hip_runtime.h>
 
+#include "probe.hpp"
 #include "te_common.hpp"
 #include "te_kernels.hpp"
 

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "probe.hpp"
 #include "te_kernels.hpp"
 #include "../../include/te_mi355x.h"
 

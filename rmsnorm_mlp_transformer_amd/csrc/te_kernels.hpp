@@ -132,8 +132,6 @@ hipError_t launch_quantize_transpose2(const void* x0, int64_t rows0, int64_t col
                                       bool tiled0 = false, bool tiled1 = false, int64_t split0 = 0);
 // y [cols, rows] = x [rows, cols]^T, bf16; rows and cols multiples of 16.
 hipError_t launch_transpose_bf16(const void* x, int64_t rows, int64_t cols, void* y, hipStream_t s);
-// The MFMA issue-rate probe (te_probe_mfma): blocks workgroups of 256 threads.
-hipError_t launch_mfma_probe(bool fp8, int64_t iters, int blocks, float* sink, uint64_t* ticks, hipStream_t s);
 
 hipError_t launch_dequantize(const uint8_t* codes, int64_t n, const float* scale_inv, void* y,
                              int y_dtype, hipStream_t s);
