@@ -86,6 +86,12 @@ def _mlp(**kw):
     (dict(y_dtype=7), B.TE_ERR_INVALID_ARGUMENT),
     (dict(y_dtype=B.TE_E4M3), B.TE_ERR_UNSUPPORTED),
     (dict(dtype=B.TE_F32, y_dtype=B.TE_BF16), B.TE_ERR_UNSUPPORTED),
+    # one size past the largest accepted: a 2 GiB kernel (plain, then gated),
+    # and features beyond 2^22
+    (dict(hidden=256, ffn=1 << 22), B.TE_ERR_UNSUPPORTED),
+    (dict(hidden=4096, ffn=1 << 17, act=B.TE_ACT_SWIGLU), B.TE_ERR_UNSUPPORTED),
+    (dict(hidden=16, ffn=(1 << 22) + 16), B.TE_ERR_INVALID_ARGUMENT),
+    (dict(hidden=(1 << 22) + 16), B.TE_ERR_INVALID_ARGUMENT),
 ])
 def test_mlp_validation(kw, status):
     assert _mlp(**kw) == status

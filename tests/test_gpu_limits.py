@@ -1,0 +1,123 @@
+"""GPU parity at the largest sizes the C ABI accepts, against the fp64 oracle:
+rows of 2^22 features (the widest the norm, activation and activation-gradient
+entry points take) and GEMM kernels just under 2 GiB, where the 32-bit byte
+offsets of the GEMM's operand buffers reach the end of their range. The calls
+one size further are rejected on the host (test_abi)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import rmsnorm_mlp_transformer_amd as te
+import workloads as W
+from gpu_util import TOL, assert_rel, check_codes, check_elementwise, codes_np, dev, f64, to_dev
+from tolerances import rounding_bound
+
+pytestmark = pytest.mark.gpu
+
+WIDEST = 1 << 22          # the largest hidden / feature count the entry points accept
+LIMIT = 1 << 31           # kernels must be smaller than this many bytes
+ACTS = [("gelu",), ("silu", "linear")]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("norm", ["layernorm", "rmsnorm"])
+def test_norm_widest_rows(dtype, norm):
+    rows = 3
+    print(f"norm {norm} {dtype} {rows}x{WIDEST}", flush=True)
+    g = torch.Generator().manual_seed(41)
+    dt = W.TORCH_DTYPE[dtype]
+    x = (torch.randn(rows, WIDEST, generator=g) * 1.7 + 0.3).to(dt)
+    gamma = (torch.randn(WIDEST, generator=g) * 0.1 + 1.0).to(dt)
+    beta = (torch.randn(WIDEST, generator=g) * 0.1).to(dt)
+    xd, gd, bd = x.to(dev()), gamma.to(dev()), beta.to(dev())
+    y, mu, rs = te.layernorm(xd, gd, bd if norm == "layernorm" else None, norm, False, 1e-5,
+                             out_dtype=torch.float32, return_stats=True)
+    q = te.Fp8Meta()
+    codes = te.layernorm(xd, gd, bd if norm == "layernorm" else None, norm, False, 1e-5, quantizer=q) \
+        if dtype == "bf16" else None
+    torch.cuda.synchronize()
+    ry, rmu, rrs = O.normalize(f64(x), f64(gamma), f64(beta), norm, 1e-5, False)
+    assert_rel(f64(y), ry, TOL["fp32"], "y fp32")
+    assert_rel(f64(rs), rrs, 1e-5, "rsigma")
+    if norm == "layernorm":
+        assert np.max(np.abs(f64(mu) - rmu)) <= 1e-5 * np.abs(f64(x)).mean()
+    if codes is not None:
+        rq, rm = O.quantize(ry)
+        assert abs(q.values()["amax"] - rm["amax"]) <= 1e-5 * rm["amax"]
+        check_codes(codes_np(codes), rq, "xq")
+
+
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_act_lu_widest_rows(act, dtype):
+    rows = 3
+    print(f"act_lu {act} {dtype} {rows}x{WIDEST}", flush=True)
+    a = W.make_act_inputs(rows, WIDEST, len(act) == 2, dtype, seed=43)
+    x = a["x"].to(dev())
+    y = te.activation(x, act)
+    q = te.Fp8Meta()
+    codes = te.activation_codes(x, act, q) if dtype == "bf16" else None
+    torch.cuda.synchronize()
+    ref = O.activation(f64(a["x"]), act)
+    assert_rel(f64(y), ref, TOL[dtype], "act")
+    if codes is not None:
+        rq, rm = O.quantize(ref)
+        assert abs(q.values()["amax"] - rm["amax"]) <= 1e-5 * rm["amax"]
+        check_codes(codes_np(codes), rq, "act codes")
+
+
+@pytest.mark.parametrize("act", ACTS, ids=["-".join(a) for a in ACTS])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dact_dbias_widest_rows(act, dtype):
+    rows = 3
+    print(f"dact_dbias {act} {dtype} {rows}x{WIDEST}", flush=True)
+    a = W.make_act_inputs(rows, WIDEST, len(act) == 2, dtype, seed=47)
+    g, x = a["grad"].to(dev()), a["x"].to(dev())
+    dx, db = te.dact_dbias(g, x, act)
+    q = te.Fp8Meta()
+    codes, dbq = te.dact_dbias_quantize(g, x, act, q)
+    torch.cuda.synchronize()
+    rdx, rdb = O.dact_dbias(f64(a["grad"]), f64(a["x"]), act)
+    assert_rel(f64(dx), rdx, TOL[dtype], "dx")
+    assert_rel(f64(db), rdb, 1e-5, "dbias")
+    assert torch.equal(dbq, db), "dbias of the quantising variant"
+    rq, rm = O.quantize(rdx)
+    m = q.values()
+    assert abs(m["amax"] - rm["amax"]) <= 1e-5 * rm["amax"], (m, rm)
+    assert m["scale"] == float(np.float32(448.0) / np.float32(m["amax"]))
+    check_codes(codes_np(codes), rq, "dx codes")
+
+
+@pytest.mark.parametrize("name,rows,hidden,ffn", [
+    # both kernels 8 KiB under 2 GiB, ffn at the widest; the activation is
+    # stored row-major (rows of 8 MiB are past the tiled layout's limit)
+    ("ln_mlp_gelu_bf16", 40, 256, WIDEST - 16),
+    # gated: kernel1 256 KiB under 2 GiB, both GEMMs on the tiled operands
+    ("rms_swiglu_bf16", 40, 4096, (1 << 17) - 16),
+])
+def test_mlp_kernels_just_under_2gib(name, rows, hidden, ffn):
+    w = W.WORKLOADS[name].scaled(rows, hidden, ffn)
+    k1_bytes = hidden * (2 if w.gated else 1) * ffn * 2
+    assert LIMIT - (1 << 20) < k1_bytes < LIMIT
+    print(f"layernorm_mlp {w.name} (kernel1 {k1_bytes} bytes)", flush=True)
+    t = W.make_inputs(w)
+    g = to_dev(t)
+    y, saved = te.layernorm_mlp(g["x"], g["gamma"], g.get("beta"), [g["kernel1"], g["kernel2"]],
+                                [g.get("bias1"), g.get("bias2")], w.norm_type,
+                                zero_centered_gamma=w.zero_centered_gamma, epsilon=w.epsilon,
+                                activation_type=w.activation_type, return_saved=True)
+    torch.cuda.synchronize()
+    got, got_h1 = f64(y), f64(saved["h1"])
+    del y, saved, g
+    torch.cuda.empty_cache()
+    f = {k: f64(v) for k, v in t.items()}
+    del t
+    o = O.layernorm_mlp_fwd(f["x"], f["gamma"], f.get("beta"), f["kernel1"], f["kernel2"], f.get("bias1"),
+                            f.get("bias2"), norm_type=w.norm_type, zero_centered_gamma=w.zero_centered_gamma,
+                            epsilon=w.epsilon, activation_type=w.activation_type)
+    e = assert_rel(got, o["y"], TOL["bf16"], "y")
+    m = check_elementwise(got, o["y"], rounding_bound(2), "y")
+    check_elementwise(got_h1, o["h"], rounding_bound(1), "h1")
+    print(f"  rel_l2 {e:.3e}, max |err| / rms {m:.3e}", flush=True)
