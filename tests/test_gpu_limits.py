@@ -121,3 +121,76 @@ def test_mlp_kernels_just_under_2gib(name, rows, hidden, ffn):
     m = check_elementwise(got, o["y"], rounding_bound(2), "y")
     check_elementwise(got_h1, o["h"], rounding_bound(1), "h1")
     print(f"  rel_l2 {e:.3e}, max |err| / rms {m:.3e}", flush=True)
+
+
+# rows of a 256 -> 16384 -> 256 MLP whose [rows, ffn] activation (bf16 h1 and
+# act, E4M3 codes) passes 2 GiB and, in bf16, 4 GiB
+MANY_ROWS = (1 << 17) + 40
+# y of the fp8 forward against the exact one: E4M3 keeps 3 mantissa bits, so a
+# value's rounding error is uniform within half a step, a relative rms of at
+# most 2^-4 / sqrt(3) = 3.6% (at the bottom of a binade). x-hat, kernel1, the
+# activation and kernel2 are rounded independently, the first two through
+# GELU's slope (at most 1.13): 3.6% * sqrt(2 * 1.13^2 + 2) = 7.7% at most.
+FP8_VS_EXACT = 0.08
+
+
+def _rows_at_offset_limits(rows, row_bytes):
+    """The first and last rows, and the rows on either side of the 2 GiB and
+    4 GiB byte offsets of a [rows, row_bytes] buffer."""
+    idx = set(range(8)) | set(range(rows - 8, rows))
+    for lim in (1 << 31, 1 << 32):
+        r = lim // row_bytes
+        idx |= set(range(max(r - 8, 0), min(r + 8, rows)))
+    return np.array(sorted(idx))
+
+
+@pytest.mark.parametrize("quant", ["none", "fp8_e4m3_current"])
+def test_mlp_activation_past_4gib(quant):
+    name = "ln_mlp_gelu_bf16" if quant == "none" else "ln_mlp_gelu_fp8"
+    w = W.WORKLOADS[name].scaled(MANY_ROWS, 256, 16384)
+    print(f"layernorm_mlp {w.name} {quant}", flush=True)
+    t = W.make_inputs(w)
+    g = to_dev(t)
+    idx = _rows_at_offset_limits(w.rows, w.ffn * 2)
+    assert idx.max() >= (1 << 32) // (w.ffn * 2)
+    it = torch.from_numpy(idx).to(dev())
+    kw = dict(return_saved=True)
+    if quant != "none":
+        q = te.QuantizerSet()
+        kw.update(quantizer_set=q, save_codes=True)
+    y, saved = te.layernorm_mlp(g["x"], g["gamma"], g["beta"], [g["kernel1"], g["kernel2"]],
+                                [g["bias1"], g["bias2"]], w.norm_type, epsilon=w.epsilon,
+                                activation_type=w.activation_type, **kw)
+    got_y, got_h1 = f64(y[it]), f64(saved["h1"][it])
+    codes = {k: codes_np(saved[k]) for k in ("w1q_t", "w2q_t")} if quant != "none" else {}
+    if quant != "none":
+        codes["xq"] = codes_np(saved["xq"][it])
+    torch.cuda.synchronize()
+    del y, saved, g
+    torch.cuda.empty_cache()
+    f = {k: f64(v) for k, v in t.items()}
+    # the sampled rows' exact forward (rows are independent)
+    o = O.layernorm_mlp_fwd(f["x"][idx], f["gamma"], f["beta"], f["kernel1"], f["kernel2"], f["bias1"],
+                            f["bias2"], norm_type=w.norm_type, epsilon=w.epsilon,
+                            activation_type=w.activation_type)
+    if quant == "none":
+        assert_rel(got_y, o["y"], TOL["bf16"], "y")
+        check_elementwise(got_y, o["y"], rounding_bound(2), "y")
+        check_elementwise(got_h1, o["h"], rounding_bound(1), "h1")
+        return
+    # current scaling over the whole tensors: the normalised input of every
+    # row sets x's scale, which the sampled rows' codes must use
+    xn, _, _ = O.normalize(f["x"], f["gamma"], f["beta"], w.norm_type, w.epsilon, False)
+    mx = O.current_scaling(xn)
+    assert abs(q.x.values()["amax"] - mx["amax"]) <= 1e-5 * mx["amax"]
+    w1q, m1 = O.quantize(f["kernel1"])
+    w2q, m2 = O.quantize(f["kernel2"])
+    assert np.array_equal(codes["w1q_t"].T, w1q), "w1 codes"
+    assert np.array_equal(codes["w2q_t"].T, w2q), "w2 codes"
+    xq, _ = O.quantize(xn[idx], mx)
+    check_codes(codes["xq"], xq, "xq")
+    h1 = O.fp8_dense(xq, mx, w1q, m1, f["bias1"])
+    assert_rel(got_h1, h1, TOL["bf16"], "h1")
+    # the activation's scale needs every row's h1, so y is held to the exact
+    # forward within the quantisation noise of its four E4M3 operands
+    assert_rel(got_y, o["y"], FP8_VS_EXACT, "y")
