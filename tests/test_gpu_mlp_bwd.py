@@ -125,3 +125,38 @@ def test_full_mlp_bwd_ln_gelu_bf16():
         e = assert_rel(out[k], ref_x[k], bound, f"{k} (fp64)")
         m = check_elementwise(out[k], ref_x[k], bound, k)
         print(f"  {k}: rel_l2 vs fp64 {e:.3e} (k = {n}), max |err| / rms {m:.3e}", flush=True)
+
+
+def test_mlp_bwd_activation_just_under_2gib():
+    """65528 x 256 -> 16384: the [rows, ffn] activation and its gradient are
+    256 KiB under 2 GiB, the backward's limit, where both weight-gradient
+    GEMMs read them through one buffer descriptor. Every element of every
+    gradient against fp64, the oracle run in row blocks (dx per block, the
+    parameter gradients summed over the blocks). The activation is linear:
+    the GEMMs under test are the same for every activation, and the oracle's
+    GELU over 2^30 elements would take minutes."""
+    import dataclasses
+    w = dataclasses.replace(W.WORKLOADS["ln_mlp_gelu_bf16"].scaled(65528, 256, 16384), activation_type=("linear",))
+    assert (1 << 31) - (1 << 20) < w.rows * w.ffn * 2 < 1 << 31
+    print(f"layernorm_mlp_bwd {w.name}", flush=True)
+    t = W.make_inputs(w)
+    gy = _grad(w)
+    out = {k: (f64(v) if v is not None else None) for k, v in _run(w, t, gy).items()}
+    torch.cuda.empty_cache()
+    f = {k: f64(v) for k, v in t.items()}
+    g64 = f64(gy)
+    ref = {k: None for k in NAMES}
+    ref["dx"] = np.empty_like(out["dx"])
+    for r0 in range(0, w.rows, 8192):
+        b = O.layernorm_mlp_bwd(g64[r0:r0 + 8192], f["x"][r0:r0 + 8192], f["gamma"], f["beta"], f["kernel1"],
+                                f["kernel2"], f["bias1"], f["bias2"], norm_type=w.norm_type, epsilon=w.epsilon,
+                                activation_type=w.activation_type)
+        ref["dx"][r0:r0 + 8192] = b["dx"]
+        for k in NAMES[1:]:
+            ref[k] = b[k] if ref[k] is None else ref[k] + b[k]
+    for k in NAMES:
+        n = bwd_roundings(k, w.gated, output_rounded=True)
+        bound = rounding_bound(n) if n else 1e-5
+        e = assert_rel(out[k], ref[k], bound, f"{k} (fp64)")
+        m = check_elementwise(out[k], ref[k], bound, k)
+        print(f"  {k}: rel_l2 vs fp64 {e:.3e} (k = {n}), max |err| / rms {m:.3e}", flush=True)
