@@ -194,3 +194,48 @@ def test_mlp_activation_past_4gib(quant):
     # the activation's scale needs every row's h1, so y is held to the exact
     # forward within the quantisation noise of its four E4M3 operands
     assert_rel(got_y, o["y"], FP8_VS_EXACT, "y")
+
+
+def test_mlp_fp8_kernels_just_under_2gib():
+    """The fp8 forward with both kernels 8 KiB under 2 GiB (bf16; their codes
+    are 1 GiB): the weights' amax and quantise-transpose over the whole range.
+    The kernels' scales come from their full amax; their codes are checked
+    bit-exact on the first, middle and last columns of kernel1 and rows of
+    kernel2, h1 on those columns, and y against the exact forward within the
+    E4M3 noise (the activation's full-width codes are not emulated)."""
+    w = W.WORKLOADS["ln_mlp_gelu_fp8"].scaled(40, 256, WIDEST - 16)
+    assert LIMIT - (1 << 20) < w.hidden * w.ffn * 2 < LIMIT
+    print(f"layernorm_mlp fp8 {w.name}", flush=True)
+    t = W.make_inputs(w)
+    g = to_dev(t)
+    q = te.QuantizerSet()
+    y, saved = te.layernorm_mlp(g["x"], g["gamma"], g["beta"], [g["kernel1"], g["kernel2"]],
+                                [g["bias1"], g["bias2"]], w.norm_type, epsilon=w.epsilon,
+                                activation_type=w.activation_type, quantizer_set=q, return_saved=True,
+                                save_codes=True)
+    cols = np.concatenate([np.arange(16), np.arange(w.ffn // 2 - 8, w.ffn // 2 + 8), np.arange(w.ffn - 16, w.ffn)])
+    ct = torch.from_numpy(cols).to(dev())
+    got_y, got_h1 = f64(y), f64(saved["h1"][:, ct])
+    w1q_got, w2q_got = codes_np(saved["w1q_t"][ct]).T, codes_np(saved["w2q_t"][:, ct])
+    xq_got = codes_np(saved["xq"])
+    metas = {k: getattr(q, k).values() for k in ("x", "w1", "w2")}
+    torch.cuda.synchronize()
+    del y, saved, g
+    torch.cuda.empty_cache()
+    f = {k: f64(v) for k, v in t.items()}
+    del t
+    m1, m2 = O.current_scaling(f["kernel1"]), O.current_scaling(f["kernel2"])
+    for key, m in (("w1", m1), ("w2", m2)):
+        assert abs(metas[key]["amax"] - m["amax"]) <= 1e-5 * m["amax"], key
+    w1q, _ = O.quantize(f["kernel1"][:, cols], m1)
+    w2q, _ = O.quantize(f["kernel2"][cols, :], m2)
+    assert np.array_equal(w1q_got, w1q), "w1 codes"
+    assert np.array_equal(w2q_got, w2q.T), "w2 codes"
+    xn, _, _ = O.normalize(f["x"], f["gamma"], f["beta"], w.norm_type, w.epsilon, False)
+    xq, mx = O.quantize(xn)
+    assert abs(metas["x"]["amax"] - mx["amax"]) <= 1e-5 * mx["amax"]
+    check_codes(xq_got, xq, "xq")
+    assert_rel(got_h1, O.fp8_dense(xq, mx, w1q, m1, f["bias1"][cols]), TOL["bf16"], "h1")
+    o = O.layernorm_mlp_fwd(f["x"], f["gamma"], f["beta"], f["kernel1"], f["kernel2"], f["bias1"], f["bias2"],
+                            norm_type=w.norm_type, epsilon=w.epsilon, activation_type=w.activation_type)
+    assert_rel(got_y, o["y"], FP8_VS_EXACT, "y")
