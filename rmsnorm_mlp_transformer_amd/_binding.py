@@ -125,6 +125,11 @@ def _ptr(t: Optional[torch.Tensor]):
         return None
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
+    # the kernels run on the current device and dereference every pointer there
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must be GPU tensors")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return t.data_ptr()
 
 

@@ -302,3 +302,12 @@ def test_mfma_probe_rejects_bad_arguments():
     assert lib.te_probe_mfma(0, 0, 4, 1, None, None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_probe_mfma(0, 10, 0, 1, None, None) == B.TE_ERR_INVALID_ARGUMENT
     assert lib.te_probe_mfma(1, 10, 4, None, None, None) == B.TE_ERR_INVALID_ARGUMENT
+
+
+def test_host_tensors_are_rejected_before_any_launch():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        te.layernorm(x, g, torch.zeros_like(g))
+    with pytest.raises(ValueError, match="GPU tensors"):
+        te.activation(x, ("gelu",))
