@@ -392,7 +392,10 @@ __global__ void __launch_bounds__(kThreads) dequantize_kernel(const uint8_t* cod
 // (fp32, before any rounding) to amax_part[block]; kDactQuant writes the E4M3
 // codes of dx * scale, the scale coming from the finished amax; kDactSum
 // writes nothing but the column partials (with the linear activation this is
-// the bias gradient sum over rows of grad).
+// the bias gradient sum over rows of grad); kDactStoreAct writes dx and, from
+// the same read of x, the activation output act(x) (gated: act(a) * b) in the
+// input dtype, the value the forward's activation pass stores, so that a
+// backward that needs both reads x once.
 // 8 waves per block: a sweep of 4 / 8 / 16 waves (with 2 or 4 rows per
 // iteration and 4096 / 8192 / 16384 blocks) at 8192 x 16384 (GELU) and
 // 8192 x 2 x 14336 (SwiGLU) found 8 waves, 4 rows, 8192 blocks fastest:
@@ -425,13 +428,13 @@ constexpr int kDactUnroll = TE_DACT_UNROLL;
 #endif
 constexpr int kActWaves = TE_ACT_WAVES;
 constexpr int kActUnroll = TE_ACT_UNROLL;
-enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2, kDactSum = 3 };
+enum DactMode { kDactStore = 0, kDactAmax = 1, kDactQuant = 2, kDactSum = 3, kDactStoreAct = 4 };
 
 template <bool BF16, int ACT, bool GATED, int MODE>
 __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad, const void* x, int64_t rows,
                                                                int64_t cols, int64_t rows_per_chunk,
                                                                void* dx, float* partials, float* amax_part,
-                                                               const float* amax) {
+                                                               const float* amax, void* act_out) {
   constexpr int G = GATED ? 2 : 1;
   constexpr int W = kDactWaves, U = kDactUnroll;
   constexpr int64_t ES = BF16 ? 2 : 4;                    // bytes per input / dx element
@@ -442,7 +445,8 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
   const int64_t col = (int64_t)blockIdx.x * kDactStrip + lane * 8;
   const int64_t xcols = G * cols;
   const int64_t nchunks = (rows + rows_per_chunk - 1) / rows_per_chunk;
-  const bool writes = MODE == kDactStore || MODE == kDactQuant;
+  const bool writes = MODE == kDactStore || MODE == kDactQuant || MODE == kDactStoreAct;
+  constexpr bool kAct = MODE == kDactStoreAct;
   // the lane's offsets in row w of a chunk; row w + k is k row pitches further (soffset)
   const uint32_t vg = (uint32_t)((w * cols + col) * ES);
   const uint32_t vx = (uint32_t)((w * xcols + col) * ES);
@@ -462,9 +466,12 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
       const Rsrc rx = buf_rsrc(reinterpret_cast<const uint8_t*>(x) + r_begin * xcols * ES, nr * xcols * ES);
       const Rsrc rd = buf_rsrc(writes ? reinterpret_cast<const uint8_t*>(dx) + r_begin * xcols * OS : nullptr,
                                writes ? nr * xcols * OS : 0);
+      // act(x): [rows, cols] like grad, so it takes grad's offsets
+      const Rsrc ra = buf_rsrc(kAct ? reinterpret_cast<const uint8_t*>(act_out) + r_begin * cols * ES : nullptr,
+                               kAct ? nr * cols * ES : 0);
       // one output chunk of 8 values at byte offset voff (+ soff) of the chunk's dx
       auto emit = [&](uint32_t voff, uint32_t soff, const float* d) {
-        if constexpr (MODE == kDactStore) {
+        if constexpr (MODE == kDactStore || MODE == kDactStoreAct) {
           // the gated dx (two outputs per grad element) is written with the nt
           // hint: 0.2014 -> 0.1918 ms at 8192 x 2 x 14336, while the same hint
           // made the one-output kernel slower (0.124 -> 0.1285 ms at 8192 x 16384)
@@ -499,6 +506,7 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
           unpack8_raw<BF16>(aw[u], a[0]);
           if constexpr (GATED) unpack8_raw<BF16>(bw[u], b[0]);
           float d[8];
+          float y[8];   // act(x), kept by kDactStoreAct only
           if constexpr (GATED) {
             float db[8];
 #pragma unroll
@@ -507,6 +515,7 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
               act_fwd_bwd<ACT>(a[0][i], f, df);
               d[i] = mul_rn(mul_rn(g[0][i], b[0][i]), df);
               db[i] = mul_rn(g[0][i], f);
+              y[i] = mul_rn(f, b[0][i]);
               sa[i] = add_rn(sa[i], d[i]);
               sb[i] = add_rn(sb[i], db[i]);
             }
@@ -515,11 +524,16 @@ __global__ void __launch_bounds__(64 * kDactWaves) dact_kernel(const void* grad,
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              d[i] = mul_rn(g[0][i], act_bwd<ACT>(a[0][i]));
+              // act_fwd_bwd's pair equals act_fwd and act_bwd bit for bit
+              float df;
+              if constexpr (kAct) act_fwd_bwd<ACT>(a[0][i], y[i], df);
+              else df = act_bwd<ACT>(a[0][i]);
+              d[i] = mul_rn(g[0][i], df);
               sa[i] = add_rn(sa[i], d[i]);
             }
             emit(vd, so, d);
           }
+          if constexpr (kAct) store8_buf<BF16>(ra, vg, (uint32_t)(rr * cols * ES), y);
         }
       }
     }
@@ -906,11 +920,12 @@ int64_t dact_blocks(int64_t rows, int64_t cols, bool gated) {
 namespace {
 template <int MODE>
 hipError_t dact_dispatch(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype, int act, bool gated,
-                         void* dx, float* partials, float* amax_part, const float* amax, hipStream_t s) {
+                         void* dx, float* partials, float* amax_part, const float* amax, hipStream_t s,
+                         void* act_out = nullptr) {
   const int64_t chunks = dact_row_chunks(rows, cols, gated);
   const int64_t rpc = dact_rows_per_chunk(rows, cols, gated);
   const dim3 grid((unsigned)((cols + kDactStrip - 1) / kDactStrip), (unsigned)chunks);
-#define TE_DACT(B, A, G) launch_kernel(dact_kernel<B, A, G, MODE>, grid, 64 * kDactWaves, 0, s, grad, x, rows, cols, rpc, dx, partials, amax_part, amax)
+#define TE_DACT(B, A, G) launch_kernel(dact_kernel<B, A, G, MODE>, grid, 64 * kDactWaves, 0, s, grad, x, rows, cols, rpc, dx, partials, amax_part, amax, act_out)
 #define TE_DACT_G(B, A) if (gated) TE_DACT(B, A, true); else TE_DACT(B, A, false);
 #define TE_DACT_A(B)                                   \
   switch (act) {                                       \
@@ -946,6 +961,20 @@ hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int6
     LaunchScope scope("dact_dbias", s);
     const hipError_t e = dact_dispatch<kDactStore>(grad, x, rows, cols, dtype, act, gated, dx,
                                                    dbias != nullptr ? partials : nullptr, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  if (dbias != nullptr) return dbias_finalize(partials, rows, cols, gated, dbias, dbias_dtype, s);
+  return hipSuccess;
+}
+
+hipError_t launch_dact_dbias_act(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                                 int act, bool gated, void* dx, void* act_out, void* dbias, int dbias_dtype,
+                                 float* partials, hipStream_t s) {
+  {
+    LaunchScope scope("dact_dbias_act", s);
+    const hipError_t e = dact_dispatch<kDactStoreAct>(grad, x, rows, cols, dtype, act, gated, dx,
+                                                      dbias != nullptr ? partials : nullptr, nullptr, nullptr, s,
+                                                      act_out);
     if (e != hipSuccess) return e;
   }
   if (dbias != nullptr) return dbias_finalize(partials, rows, cols, gated, dbias, dbias_dtype, s);

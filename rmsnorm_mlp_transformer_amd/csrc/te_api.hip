@@ -628,26 +628,27 @@ te_status te_layernorm_mlp_bwd(const void* grad, const void* x, const void* gamm
   MlpBwdWs w = mlp_bwd_ws(c, rows, hidden, ffn, act_type);
   const int k = act_kind(act_type);
   const te::Epilogue lin{nullptr, nullptr, nullptr, nullptr, te::kLinear, false};
-  // the normalised input (GEMM1's A operand) and the activation output, recomputed
+  // the normalised input (GEMM1's A operand), recomputed
   TE_HIP(te::launch_norm(x, gamma, beta, rows, hidden, dtype, rms, zero_centered_gamma != 0, epsilon, te::kNormStore,
                          dtype, w.xn, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s), "norm");
-  TE_HIP(te::launch_act(h1, rows, ffn, dtype, k, gated, 0, w.act, dtype, nullptr, nullptr, nullptr, s), "act");
-  // GEMM2: dact = grad @ kernel2^T, dkernel2 = act^T @ grad, dbias2 = sum of grad.
-  // The data-gradient GEMMs run on the N-contiguous kernel with a transposed
-  // copy of the weight (one streaming pass), faster than the K-contiguous
-  // kernel on the weight as stored.
+  // GEMM2's data gradient: dact = grad @ kernel2^T. The data-gradient GEMMs run
+  // on the N-contiguous kernel with a transposed copy of the weight (one
+  // streaming pass), faster than the K-contiguous kernel on the weight as stored.
   te::Epilogue e = lin;
   e.out = w.dact;
   e.name = "gemm_bf16_dgrad";
   TE_HIP(te::launch_transpose_bf16(kernel2, ffn, hidden, w.wt, s), "transpose kernel2");
   TE_HIP(te::launch_gemm_bf16(grad, w.wt, rows, ffn, hidden, e, s), "dgrad2");
+  // activation backward with dbias1; the same pass recomputes the activation
+  // output from its read of h1 for GEMM2's weight gradient (one read of h1)
+  TE_HIP(te::launch_dact_dbias_act(w.dact, h1, rows, ffn, dtype, k, gated, w.dh1, w.act, dbias1, dparam_dtype,
+                                   w.part_dact, s),
+         "dact");
+  // GEMM2's weight gradient dkernel2 = act^T @ grad, dbias2 = sum of grad
   e.name = nullptr;
   e.out = dkernel2;
   TE_HIP(te::launch_gemm_bf16_at(w.act, grad, ffn, hidden, rows, e, s), "wgrad2");
   if (dbias2 != nullptr) TE_HIP(te::launch_colsum(grad, rows, hidden, dtype, dbias2, dparam_dtype, w.part_b2, s), "dbias2");
-  // activation backward with dbias1
-  TE_HIP(te::launch_dact_dbias(w.dact, h1, rows, ffn, dtype, k, gated, w.dh1, dbias1, dparam_dtype, w.part_dact, s),
-         "dact");
   // GEMM1: dxn = dh1 @ kernel1^T, dkernel1 = xn^T @ dh1
   e.out = w.dxn;
   e.name = "gemm_bf16_dgrad";

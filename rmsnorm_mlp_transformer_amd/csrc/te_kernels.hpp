@@ -166,6 +166,11 @@ int64_t dact_blocks(int64_t rows, int64_t cols, bool gated);
 hipError_t launch_dact_dbias(const void* grad, const void* x, int64_t rows, int64_t cols,
                              int dtype, int act, bool gated, void* dx, void* dbias,
                              int dbias_dtype, float* partials, hipStream_t s);
+// The same, also writing act_out [rows, cols] = act(x) (gated: act(a) * b) in
+// dtype, the values launch_act's store mode writes, from the same read of x.
+hipError_t launch_dact_dbias_act(const void* grad, const void* x, int64_t rows, int64_t cols, int dtype,
+                                 int act, bool gated, void* dx, void* act_out, void* dbias, int dbias_dtype,
+                                 float* partials, hipStream_t s);
 // Column sums of x [rows, cols] (fp32, fixed order) into sum [cols];
 // partials: dact_row_chunks(rows, cols, false) * cols floats.
 hipError_t launch_colsum(const void* x, int64_t rows, int64_t cols, int dtype, void* sum, int sum_dtype,
